@@ -1,0 +1,198 @@
+"""CPU oracle for the DSA hot path: indexer -> top-k -> sparse MLA.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
+baseline may import this module; the HIP path never does, and this module
+imports nothing from it.  It is plain numpy in float64, deliberately slow and
+unblocked, so that it can be checked against the pages by eye.
+
+Sources (the pages have no code; every step below is restated from prose):
+  [CFG] page "2026大模型架构概览（二）：GLM 5 DSV3.2 的 DSA 与 MoE 配置拆解"
+        §2.1 (parameter table: index_n_heads 32, index_head_dim 128,
+        index_topk 2048, 64 heads, qk_nope 192, qk_rope 64, v_head 256,
+        kv_lora_rank 512) and §2.2 (the indexer scores every query against all
+        history and only ranks; the selector keeps the index_topk best keys,
+        which alone take part in attention; DSA filters on top of MLA).
+  [N2]  page "（五）一万亿次点积砍到两千次：DSA 怎么破 N²", sections on the indexer
+        (low-dimensional 32x128 dot products over every token), the full DSA
+        flow (indexer top-2048, then full Q.K.V, softmax, weighted V over those
+        only) and the cache division of labour (skipped K/V stay cached).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * score(t,s) = sum_h w[t,h] * ReLU(q_idx[t,h] . k_idx[s]); one 128-d key per
+    cached token shared by the 32 indexer heads; no scale, no bias.
+  * causal: s <= t (a token sees itself); sequence-local positions.
+  * scores are rounded once to fp32; selection compares fp32 values (so -0.0
+    equals +0.0), ties go to the lower position; the kept positions are
+    returned ascending and padded with -1 to length k; with n <= k all n are kept.
+  * MLA over the kept rows with explicit per-head up-projection
+    K_nope = c @ W_UK[h], V = c @ W_UV[h]; logits (q_nope.K_nope + q_rope.r)
+    times softmax_scale (1/sqrt(192+64) = 1/16 by default); softmax in full.
+
+Parity pins: the functions here are pinned by tests/test_oracle_pins.py
+(dense-attention equivalence, planted index sets, absorbed == explicit, brute
+force, softmax special cases).  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+
+# [CFG] §2.1 parameter table.
+INDEX_N_HEADS = 32
+INDEX_HEAD_DIM = 128
+INDEX_TOPK = 2048
+NUM_HEADS = 64
+QK_NOPE_HEAD_DIM = 192
+QK_ROPE_HEAD_DIM = 64
+QK_HEAD_DIM = QK_NOPE_HEAD_DIM + QK_ROPE_HEAD_DIM
+V_HEAD_DIM = 256
+KV_LORA_RANK = 512
+DEFAULT_SCALE = 1.0 / np.sqrt(QK_HEAD_DIM)  # = 1/16
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact conversion of bf16 bit patterns (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- O1 indexer
+def indexer_scores(q_idx_t, w_t, k_idx_seq, pos: int) -> np.ndarray:
+    """Lightning-indexer scores of one query against its history, fp32.
+
+    [CFG] §2.2 and [N2] (indexer section): one cheap relevance score per
+    (query, earlier token) from 32 heads of 128-d dot products; the score only
+    ranks keys.  Reading: score = sum over heads of w_h * ReLU(q_h . k_s) for
+    s = 0..pos, evaluated in float64 and rounded once to fp32.
+
+    q_idx_t [32,128] bf16, w_t [32] bf16, k_idx_seq [>=pos+1,128] bf16.
+    Returns float32 [pos+1].
+    """
+    q = bf16_bits_to_f64(q_idx_t)                    # [32,128]
+    w = bf16_bits_to_f64(w_t)                        # [32]
+    k = bf16_bits_to_f64(k_idx_seq[: pos + 1])       # [n,128]
+    per_head = k @ q.T                               # [n,32]  q_h . k_s
+    relu = np.maximum(per_head, 0.0)                 # ReLU per head, before weighting
+    score = relu @ w                                 # sum_h w_h * ReLU(.)
+    return score.astype(np.float32)                  # one RNE rounding to fp32
+
+
+# ---------------------------------------------------------------- O2 top-k
+def topk_select(scores_f32, k: int = INDEX_TOPK) -> np.ndarray:
+    """Top-k selector by a full stable sort.
+
+    [CFG] §2.2 / [N2] (the 2048 best-scoring history positions are kept).
+    Order: fp32 score descending, then position ascending.  Returns int32 [k]:
+    the kept positions ascending, then -1 padding.  If n <= k all n are kept.
+    """
+    s = np.asarray(scores_f32, dtype=np.float32)
+    n = int(s.shape[0])
+    out = np.full(k, -1, dtype=np.int32)
+    if n <= k:
+        out[:n] = np.arange(n, dtype=np.int32)
+        return out
+    key = s.astype(np.float64) + 0.0                 # -0.0 -> +0.0
+    order = np.argsort(-key, kind="stable")          # equal scores keep position order
+    kept = np.sort(order[:k])
+    out[:] = kept.astype(np.int32)
+    return out
+
+
+# ---------------------------------------------------------------- O3 MLA
+def mla_explicit(q_nope_t, q_rope_t, kv_rows, w_uk, w_uv,
+                 scale: float = DEFAULT_SCALE) -> np.ndarray:
+    """Full MLA attention of one query over the given latent-cache rows.
+
+    [N2] (DSA flow: full Q.K.V over the kept tokens, softmax, weighted sum of
+    V) with the MLA shapes of [CFG] §2.1.  Explicit form: every head
+    up-projects the kept latent rows to its own keys and values.
+
+    q_nope_t [64,192], q_rope_t [64,64], kv_rows [n,576] (512 latent | 64 rope,
+    rope key shared by all heads), w_uk [64,512,192], w_uv [64,512,256]; all
+    bf16 bit patterns.  Returns float64 [64,256].
+    """
+    qn = bf16_bits_to_f64(q_nope_t)
+    qr = bf16_bits_to_f64(q_rope_t)
+    rows = bf16_bits_to_f64(kv_rows)
+    c = rows[:, :KV_LORA_RANK]
+    r = rows[:, KV_LORA_RANK:]
+    wuk = bf16_bits_to_f64(w_uk)
+    wuv = bf16_bits_to_f64(w_uv)
+    out = np.empty((NUM_HEADS, V_HEAD_DIM))
+    for h in range(NUM_HEADS):
+        k_nope = c @ wuk[h]                          # [n,192]
+        v = c @ wuv[h]                               # [n,256]
+        z = (k_nope @ qn[h] + r @ qr[h]) * scale     # [n]
+        e = np.exp(z - z.max())
+        p = e / e.sum()
+        out[h] = p @ v
+    return out
+
+
+def mla_absorbed(q_nope_t, q_rope_t, kv_rows, w_uk, w_uv,
+                 scale: float = DEFAULT_SCALE) -> np.ndarray:
+    """Same attention in weight-absorbed form (used only to cross-check O3).
+
+    q_lat = W_UK[h] q_nope scores directly against the 512-d latent; the
+    latent-weighted sum is up-projected by W_UV[h] afterwards.
+    """
+    qn = bf16_bits_to_f64(q_nope_t)
+    qr = bf16_bits_to_f64(q_rope_t)
+    rows = bf16_bits_to_f64(kv_rows)
+    c = rows[:, :KV_LORA_RANK]
+    r = rows[:, KV_LORA_RANK:]
+    wuk = bf16_bits_to_f64(w_uk)
+    wuv = bf16_bits_to_f64(w_uv)
+    out = np.empty((NUM_HEADS, V_HEAD_DIM))
+    for h in range(NUM_HEADS):
+        q_lat = wuk[h] @ qn[h]                       # [512]
+        z = (c @ q_lat + r @ qr[h]) * scale
+        e = np.exp(z - z.max())
+        p = e / e.sum()
+        out[h] = (p @ c) @ wuv[h]
+    return out
+
+
+def softmax_weights(q_nope_t, q_rope_t, kv_rows, w_uk, h: int,
+                    scale: float = DEFAULT_SCALE) -> np.ndarray:
+    """The attention weights of head h (explicit form); rows of P sum to 1."""
+    qn = bf16_bits_to_f64(q_nope_t)[h]
+    qr = bf16_bits_to_f64(q_rope_t)[h]
+    rows = bf16_bits_to_f64(kv_rows)
+    z = (rows[:, :KV_LORA_RANK] @ bf16_bits_to_f64(w_uk)[h] @ qn
+         + rows[:, KV_LORA_RANK:] @ qr) * scale
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+# ---------------------------------------------------------------- whole path
+def query_forward(inp, t: int, k: int = INDEX_TOPK, scale: float = DEFAULT_SCALE,
+                  with_output: bool = True) -> Tuple[np.ndarray, np.ndarray, Optional[np.ndarray]]:
+    """Indexer -> top-k -> sparse MLA for query t of an input batch.
+
+    ``inp`` carries q_seq, q_pos, seq_row0, k_idx, kv, q_idx, w, q_nope, q_rope,
+    w_uk, w_uv (numpy; bf16 as uint16).  Rows of sequence b start at
+    seq_row0[b]; positions are sequence-local.  Returns (scores fp32 [p+1],
+    idx int32 [k], out float64 [64,256] or None).
+    """
+    b = int(inp.q_seq[t])
+    p = int(inp.q_pos[t])
+    r0 = int(inp.seq_row0[b])
+    scores = indexer_scores(inp.q_idx[t], inp.w[t], inp.k_idx[r0: r0 + p + 1], p)
+    idx = topk_select(scores, k)
+    out = None
+    if with_output:
+        kept = idx[idx >= 0].astype(np.int64)
+        out = mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept],
+                           inp.w_uk, inp.w_uv, scale)
+    return scores, idx, out
+
+
+def forward(inp, queries: Optional[Iterable[int]] = None, k: int = INDEX_TOPK,
+            scale: float = DEFAULT_SCALE, with_output: bool = True):
+    """query_forward over a set of queries (all by default); lists in query order."""
+    qs = range(len(inp.q_seq)) if queries is None else list(queries)
+    res = [query_forward(inp, t, k, scale, with_output) for t in qs]
+    return [r[0] for r in res], [r[1] for r in res], [r[2] for r in res]

@@ -1,0 +1,285 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-worked
+fixtures (tests/golden), closed forms of planted inputs, a library attention
+routine in a special case, brute-force enumeration, algebraic identities and
+softmax special cases.  A plausible slip in the oracle (ReLU after the head
+sum, wrong tie-break, transposed operand, dropped rope term, wrong scale,
+non-causal window) fails at least one of them.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_index_amd import synth
+from oracle import dsa_oracle as O
+
+
+def _bits(x):
+    return synth.bf16_rne(np.asarray(x, dtype=np.float32))
+
+
+def _parse_scores(vals):
+    return np.asarray([float(v) for v in vals], dtype=np.float32)
+
+
+# ------------------------------------------------------------------ dims
+def test_dims_match_page_table(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "model_dims.json")))
+    assert O.KV_LORA_RANK == g["kv_lora_rank"]
+    assert O.QK_NOPE_HEAD_DIM == g["qk_nope_head_dim"]
+    assert O.QK_ROPE_HEAD_DIM == g["qk_rope_head_dim"]
+    assert O.QK_HEAD_DIM == g["qk_head_dim"]
+    assert O.NUM_HEADS == g["num_attention_heads"]
+    assert O.V_HEAD_DIM == g["v_head_dim"]
+    assert O.INDEX_TOPK == g["index_topk"]
+    assert O.INDEX_HEAD_DIM == g["index_head_dim"]
+    assert O.INDEX_N_HEADS == g["index_n_heads"]
+    assert O.DEFAULT_SCALE == 1.0 / 16.0
+
+
+# ------------------------------------------------------------------ top-k (O2)
+def test_topk_golden_cases(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "topk_cases.json")))
+    for case in g["cases"]:
+        s = _parse_scores(case["scores"])
+        got = O.topk_select(s, case["k"])
+        assert got.dtype == np.int32
+        assert got.tolist() == case["expected"], case["name"]
+
+
+def _topk_by_rank_definition(s, k):
+    """Selection from the definition: s is kept iff fewer than k candidates beat it."""
+    n = len(s)
+    v = s.astype(np.float64) + 0.0
+    kept = []
+    for i in range(n):
+        beats = sum(1 for j in range(n) if v[j] > v[i] or (v[j] == v[i] and j < i))
+        if beats < k:
+            kept.append(i)
+    return kept + [-1] * (k - len(kept))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_subsets(seed):
+    """P4: for tiny n, exactly one k-subset has every member beating every non-member."""
+    rng = np.random.default_rng(100 + seed)
+    for n in range(1, 11):
+        for k in range(1, 5):
+            s = (rng.integers(-2, 3, size=n) * 0.5).astype(np.float32)  # many ties
+            if rng.random() < 0.3:
+                s[rng.integers(0, n)] = np.float32(-0.0)
+            got = O.topk_select(s, k)
+            if n <= k:
+                assert got.tolist() == list(range(n)) + [-1] * (k - n)
+                continue
+            winners = []
+            for sub in itertools.combinations(range(n), k):
+                rest = [j for j in range(n) if j not in sub]
+                ok = all((s[i] > s[j]) or (s[i] == s[j] and i < j) for i in sub for j in rest)
+                if ok:
+                    winners.append(list(sub))
+            assert len(winners) == 1
+            assert got.tolist() == winners[0]
+
+
+@pytest.mark.parametrize("kind", ["normal", "few_values", "signed"])
+def test_topk_matches_rank_definition(kind):
+    rng = np.random.default_rng(7)
+    s = synth.random_scores(rng, 3, 300, kind)
+    for row in s:
+        for k in (1, 17, 64, 299, 300, 512):
+            assert O.topk_select(row, k).tolist() == _topk_by_rank_definition(row, k)
+
+
+# ------------------------------------------------------------------ indexer (O1)
+def test_indexer_planted_closed_form(golden_dir):
+    """P2: planted keys/queries along e_0 give exact, hand-worked scores and index sets."""
+    g = json.load(open(os.path.join(golden_dir, "planted_indexer.json")))
+    q = np.zeros((32, 128), np.float32)
+    q[:, 0] = g["alpha"]
+    beta = np.asarray(g["beta"], np.float32)
+    k = np.zeros((len(beta), 128), np.float32)
+    k[:, 0] = beta
+    w = np.asarray(g["w"], np.float32)
+    for pos, exp_s, exp_k in ((g["position"], g["expected_scores"], g["expected_topk"]),
+                              (g["position_full"], g["expected_scores_full"], g["expected_topk_full"])):
+        s = O.indexer_scores(_bits(q), _bits(w), _bits(k), pos)
+        assert s.dtype == np.float32 and s.shape == (pos + 1,)
+        assert s.tolist() == exp_s
+        assert O.topk_select(s, g["k"]).tolist() == exp_k
+
+
+def test_indexer_relu_inactive_reduces_to_matmul():
+    """With every q and k entry positive, the ReLU never fires and
+    score = k_s . (sum_h w_h q_h): one matrix-vector product (torch, fp64)."""
+    rng = np.random.default_rng(3)
+    q = np.abs(rng.standard_normal((32, 128))).astype(np.float32) / 11
+    k = np.abs(rng.standard_normal((50, 128))).astype(np.float32) / 11
+    w = rng.random(32).astype(np.float32)
+    qb, kb, wb = _bits(q), _bits(k), _bits(w)
+    s = O.indexer_scores(qb, wb, kb, 49)
+    tq = torch.from_numpy(synth.bf16_to_f32(qb).astype(np.float64))
+    tk = torch.from_numpy(synth.bf16_to_f32(kb).astype(np.float64))
+    tw = torch.from_numpy(synth.bf16_to_f32(wb).astype(np.float64))
+    ref = (tk @ (tw @ tq)).to(torch.float32).numpy()
+    np.testing.assert_allclose(s, ref, rtol=1e-6, atol=0)
+
+
+def test_indexer_head_weight_and_sign_structure():
+    """Negating every key flips which heads fire: score(-k) uses the heads with q.k < 0."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((32, 128)).astype(np.float32) / 11
+    k = rng.standard_normal((20, 128)).astype(np.float32) / 11
+    w = rng.random(32).astype(np.float32)
+    qb, kb, wb = _bits(q), _bits(k), _bits(w)
+    qf = synth.bf16_to_f32(qb).astype(np.float64)
+    kf = synth.bf16_to_f32(kb).astype(np.float64)
+    wf = synth.bf16_to_f32(wb).astype(np.float64)
+    s_pos = O.indexer_scores(qb, wb, kb, 19).astype(np.float64)
+    s_neg = O.indexer_scores(qb, wb, _bits(-synth.bf16_to_f32(kb)), 19).astype(np.float64)
+    # ReLU(x) - ReLU(-x) = x for every head, so the difference is linear in k.
+    lin = kf @ (wf @ qf)
+    np.testing.assert_allclose(s_pos - s_neg, lin, rtol=0, atol=2e-6)
+    # and ReLU(x) + ReLU(-x) = |x|
+    absum = np.abs(kf @ qf.T) @ wf
+    np.testing.assert_allclose(s_pos + s_neg, absum, rtol=0, atol=2e-6)
+
+
+def test_indexer_causal_window():
+    """Only positions 0..pos are scored; keys after pos never matter."""
+    inp = synth.custom([64], [(0, 10)], seed=5)
+    s1 = O.indexer_scores(inp.q_idx[0], inp.w[0], inp.k_idx, 10)
+    k2 = inp.k_idx.copy()
+    k2[11:] = 0
+    s2 = O.indexer_scores(inp.q_idx[0], inp.w[0], k2, 10)
+    assert s1.shape == (11,)
+    assert np.array_equal(s1, s2)
+
+
+# ------------------------------------------------------------------ MLA (O3)
+def _sdpa_reference(inp, t):
+    """Dense causal attention by torch's SDPA in fp64 with explicitly up-projected K/V."""
+    b, p = int(inp.q_seq[t]), int(inp.q_pos[t])
+    r0 = int(inp.seq_row0[b])
+    rows = torch.from_numpy(synth.bf16_to_f32(inp.kv[r0: r0 + p + 1]).astype(np.float64))
+    c, r = rows[:, :512], rows[:, 512:]
+    wuk = torch.from_numpy(synth.bf16_to_f32(inp.w_uk).astype(np.float64))
+    wuv = torch.from_numpy(synth.bf16_to_f32(inp.w_uv).astype(np.float64))
+    qn = torch.from_numpy(synth.bf16_to_f32(inp.q_nope[t]).astype(np.float64))
+    qr = torch.from_numpy(synth.bf16_to_f32(inp.q_rope[t]).astype(np.float64))
+    kn = torch.einsum("nc,hcd->hnd", c, wuk)                   # [64,n,192]
+    kk = torch.cat([kn, r.unsqueeze(0).expand(64, -1, -1)], -1)  # [64,n,256]
+    vv = torch.einsum("nc,hce->hne", c, wuv)                   # [64,n,256]
+    qq = torch.cat([qn, qr], -1).unsqueeze(1)                  # [64,1,256]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)  # scale 1/sqrt(256)
+    return o[:, 0, :].numpy()
+
+
+def test_dense_equivalence_when_context_below_k():
+    """P1: with context <= k every position is kept and DSA is dense causal MLA."""
+    inp = synth.custom([40, 23], [(0, 0), (0, 7), (1, 22), (0, 39)], seed=11)
+    for t in range(4):
+        _, idx, out = O.query_forward(inp, t, k=2048)
+        p = int(inp.q_pos[t])
+        assert idx[: p + 1].tolist() == list(range(p + 1))
+        assert (idx[p + 1:] == -1).all()
+        ref = _sdpa_reference(inp, t)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_absorbed_equals_explicit():
+    """P3: weight absorption is an exact re-association in exact arithmetic."""
+    inp = synth.custom([70], [(0, 69)], seed=12)
+    rows = inp.kv[np.array([3, 5, 8, 13, 21, 34, 55, 69])]
+    a = O.mla_explicit(inp.q_nope[0], inp.q_rope[0], rows, inp.w_uk, inp.w_uv)
+    b = O.mla_absorbed(inp.q_nope[0], inp.q_rope[0], rows, inp.w_uk, inp.w_uv)
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_softmax_single_row_returns_its_value():
+    """P5: one kept row => weight exactly 1 => output = V of that row."""
+    inp = synth.custom([5], [(0, 0)], seed=13)
+    _, idx, out = O.query_forward(inp, 0)
+    assert idx[0] == 0 and (idx[1:] == -1).all()
+    c = synth.bf16_to_f32(inp.kv[0, :512]).astype(np.float64)
+    wuv = synth.bf16_to_f32(inp.w_uv).astype(np.float64)
+    for h in range(64):
+        np.testing.assert_allclose(out[h], c @ wuv[h], rtol=1e-14, atol=1e-15)
+
+
+def test_softmax_zero_query_is_uniform_mean():
+    """P5: q = 0 => all logits 0 => output is the mean of the kept rows' values.
+    This pins the gathered set independently of QK."""
+    inp = synth.custom([30], [(0, 29)], seed=14)
+    sel = np.array([2, 3, 11, 17, 29])
+    zero_n = np.zeros_like(inp.q_nope[0])
+    zero_r = np.zeros_like(inp.q_rope[0])
+    out = O.mla_explicit(zero_n, zero_r, inp.kv[sel], inp.w_uk, inp.w_uv)
+    c = synth.bf16_to_f32(inp.kv[sel, :512]).astype(np.float64).mean(0)
+    wuv = synth.bf16_to_f32(inp.w_uv).astype(np.float64)
+    for h in range(64):
+        np.testing.assert_allclose(out[h], c @ wuv[h], rtol=1e-12, atol=1e-14)
+
+
+def test_softmax_weights_rows_sum_to_one_and_duplicates_tie():
+    inp = synth.custom([30], [(0, 29)], seed=15)
+    rows = inp.kv[np.array([4, 9, 9, 20])]  # row 9 twice
+    for h in (0, 31, 63):
+        p = O.softmax_weights(inp.q_nope[0], inp.q_rope[0], rows, inp.w_uk, h)
+        assert abs(p.sum() - 1.0) < 1e-14
+        assert p[1] == p[2]
+
+
+def test_rope_term_and_scale_enter_logits():
+    """Only the rope part differs between two rows => the weight ratio is
+    exp(scale * q_rope . (r_a - r_b)), with scale = 1/16."""
+    inp = synth.custom([4], [(0, 3)], seed=16)
+    rows = inp.kv[:2].copy()
+    rows[1, :512] = rows[0, :512]
+    h = 5
+    p = O.softmax_weights(inp.q_nope[0], inp.q_rope[0], rows, inp.w_uk, h)
+    qr = synth.bf16_to_f32(inp.q_rope[0, h]).astype(np.float64)
+    ra = synth.bf16_to_f32(rows[0, 512:]).astype(np.float64)
+    rb = synth.bf16_to_f32(rows[1, 512:]).astype(np.float64)
+    np.testing.assert_allclose(np.log(p[0] / p[1]), (qr @ (ra - rb)) / 16.0, rtol=1e-10)
+
+
+# ------------------------------------------------------------------ whole path
+def test_selection_only_coupling():
+    """P7: the indexer only ranks.  Scaling w by a power of two scales every score
+    exactly, keeps the selection and leaves the attention output bit-identical."""
+    inp = synth.custom([3000], [(0, 2999), (0, 2500)], seed=17)
+    s1, i1, o1 = O.forward(inp)
+    inp.w = _bits(synth.bf16_to_f32(inp.w) * 4)
+    s2, i2, o2 = O.forward(inp)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a * 4, b)
+    for a, b in zip(i1, i2):
+        assert np.array_equal(a, b)
+    for a, b in zip(o1, o2):
+        assert np.array_equal(a, b)
+
+
+def test_selection_matters_beyond_k():
+    """With more than k candidates the output is attention over the kept set only:
+    moving one kept row's latent changes the output, moving a skipped row does not."""
+    inp = synth.custom([300], [(0, 299)], seed=18)
+    k = 32
+    _, idx, out = O.query_forward(inp, 0, k=k)
+    kept = set(idx.tolist())
+    skipped = next(s for s in range(300) if s not in kept)
+    kv2 = inp.kv.copy()
+    kv2[skipped, :512] = _bits(np.full(512, 3.0))
+    inp2 = synth.Inputs(**{**inp.__dict__, "kv": kv2})
+    _, idx2, out2 = O.query_forward(inp2, 0, k=k)
+    assert np.array_equal(idx, idx2) and np.array_equal(out, out2)
+    kv3 = inp.kv.copy()
+    kv3[idx[0], :512] = _bits(np.full(512, 3.0))
+    inp3 = synth.Inputs(**{**inp.__dict__, "kv": kv3})
+    _, _, out3 = O.query_forward(inp3, 0, k=k)
+    assert not np.allclose(out, out3)
