@@ -1,0 +1,178 @@
+/*
+ * dsa.h -- C ABI of the DSA sparse-attention hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method: a lightweight indexer scores every cached token of a query's
+ * history, a top-k selector keeps index_topk (2048) positions, and multi-head
+ * latent attention (MLA) runs over the kept positions only.
+ *   - page "2026大模型架构概览（二）：GLM 5 DSV3.2 的 DSA 与 MoE 配置拆解", §2.1 (dimension
+ *     table) and §2.2 (the indexer scores every query against all history and
+ *     only ranks; the selector keeps the index_topk best; DSA is a filter in
+ *     front of MLA, not a replacement);
+ *   - page "（五）一万亿次点积砍到两千次：DSA 怎么破 N²", sections on the indexer
+ *     (32 heads x 128-d dot products over every token), the full DSA flow
+ *     (top-2048, then full attention over those only) and the cache (skipped
+ *     tokens stay cached; DSA saves compute, not storage).
+ *
+ * Fixed dimensions (compile-time): indexer 32 heads x 128; attention 64 heads;
+ * q/k 192 (nope) + 64 (rope); v 256; latent 512.  One cache row holds the
+ * 512-d latent followed by the 64-d rope key (576 bf16 = 1152 B), one indexer
+ * key per token (128 bf16 = 256 B).
+ *
+ * Conventions for every call below
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *     unless stated; all arrays are dense row-major, innermost index last.
+ *   - bf16 arrays are raw bit patterns (uint16_t).  bf16 arrays, the score
+ *     matrix and the workspace must be 16-byte aligned (DSA_ERR_ALIGN).
+ *   - Positions are sequence-local: query t belongs to sequence q_seq[t] and
+ *     sits at position q_pos[t]; token s of sequence b is cache row
+ *     seq_row0[b] + s.  A query sees positions 0..q_pos[t] (itself included).
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *     frees nothing and keeps no pointer after a call returns.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = default stream) and is not
+ *     waited for: buffers must stay valid until the stream has passed it.
+ *     Input caches and weights are never written.
+ *   - Errors: every host-checkable precondition is checked before anything is
+ *     enqueued, and a failing call enqueues nothing.  DSA_ERR_LAUNCH reports a
+ *     failed kernel launch (see dsa_last_hip_error).  Device-side
+ *     preconditions (q_seq[t] < num_seqs, 0 <= q_pos[t] < rows of that
+ *     sequence, every cache row inside its allocation, idx entries in
+ *     {-1} U [0, q_pos[t]]) are not checked: violating them is undefined.
+ *   - num_queries == 0 is a valid empty call: DSA_OK, nothing enqueued.
+ *   - Calls are re-entrant; the only library state is a per-device cache of
+ *     the device check and a thread-local last HIP error.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+#define DSA_INDEX_HEADS 32
+#define DSA_INDEX_DIM 128
+#define DSA_HEADS 64
+#define DSA_QK_NOPE_DIM 192
+#define DSA_QK_ROPE_DIM 64
+#define DSA_V_DIM 256
+#define DSA_LATENT_DIM 512
+#define DSA_KV_ROW 576           /* 512 latent | 64 rope */
+#define DSA_MAX_TOPK 2048        /* index_topk of the page-4 table */
+
+typedef uint16_t dsa_bf16;       /* raw bf16 bits */
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,         /* a required pointer is NULL */
+  DSA_ERR_SHAPE = 2,        /* a size is out of range (counts, k, ld_scores, max_ctx) */
+  DSA_ERR_ALIGN = 3,        /* a pointer or leading dimension is misaligned */
+  DSA_ERR_WORKSPACE = 4,    /* workspace too small (see dsa_workspace_bytes) */
+  DSA_ERR_UNSUPPORTED = 5,  /* an option value this build does not implement */
+  DSA_ERR_LAUNCH = 6,       /* a kernel launch failed (dsa_last_hip_error) */
+  DSA_ERR_DEVICE = 7        /* the current HIP device is missing or is not gfx950 */
+} dsa_status;
+
+/* Output element type of the attention output. */
+enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
+
+/* Operation ids for dsa_workspace_bytes. */
+enum { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
+
+/* Batch geometry.  The struct itself is HOST memory, read during the call. */
+typedef struct dsa_batch {
+  int32_t num_queries;       /* T >= 0 */
+  int32_t num_seqs;          /* B >= 1 */
+  int32_t max_ctx;           /* >= max_t(q_pos[t]) + 1, >= 1: bounds grids and score rows */
+  int32_t reserved;          /* must be 0 */
+  const int32_t* q_seq;      /* [T] device: sequence of each query */
+  const int32_t* q_pos;      /* [T] device: position of each query (inclusive causal limit) */
+  const int64_t* seq_row0;   /* [B] device: first cache row of each sequence */
+} dsa_batch;
+
+/*
+ * Indexer scores (page-4 §2.2 "Lightning Indexer"; page-5 indexer section).
+ * For each query t and s = 0..q_pos[t]:
+ *   scores[t*ld_scores + s] = sum_{h<32} w[t,h] * max(0, sum_{d<128} q_idx[t,h,d] * k_idx[row(s),d])
+ * in fp32 (bf16 products, fp32 accumulation).  Entries beyond q_pos[t] are
+ * not written.
+ *   q_idx [T,32,128] bf16, w [T,32] bf16, k_idx [rows,128] bf16,
+ *   scores [T, ld_scores] fp32 with ld_scores >= max_ctx and ld_scores % 4 == 0.
+ * Batches averaging >= 8 queries per sequence run as a tiled MFMA GEMM over
+ * blocks of consecutive queries, others as a per-query key scan; both give
+ * the same values.
+ */
+dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                            const dsa_bf16* k_idx, float* scores, int64_t ld_scores,
+                            void* stream);
+
+/*
+ * Top-k selector (page-4 §2.2 "Top-k Selector"; page-5: index_topk = 2048).
+ * For each query t over scores[t, 0..q_pos[t]]: keeps the min(q_pos[t]+1, k)
+ * largest under the total order (fp32 value descending, -0.0 == +0.0, then
+ * position ascending) and writes them to idx[t*k .. t*k+k) in ascending
+ * position order, padded with -1.  Bit-exact: equal inputs give equal outputs.
+ * NaN scores are unsupported (unspecified result).
+ *   scores [T, ld_scores] fp32 (as above), 1 <= k <= DSA_MAX_TOPK, idx [T,k] int32.
+ *   ws: workspace of dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes (may be NULL if 0).
+ */
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse MLA attention over the kept positions (page-5 DSA flow: full
+ * Q.K.V over the kept tokens, softmax, weighted sum; page-4 §2.1 dims).
+ * For query t and head h, over the entries j of idx[t, 0..k) that are >= 0:
+ *   z_j  = softmax_scale * (q_nope[t,h] . (c_j W_UK[h]) + q_rope[t,h] . r_j)
+ *   out[t,h] = sum_j softmax(z)_j * (c_j W_UV[h])
+ * where c_j / r_j are the latent and rope parts of cache row seq_row0[b] + idx.
+ * Computed in weight-absorbed form: q_lat = W_UK[h] q_nope (rounded to bf16),
+ * logits against the latent, online softmax in fp32, the latent-weighted sum
+ * (rounded to bf16) up-projected by W_UV[h]; fp32 accumulation throughout.
+ *   q_nope [T,64,192], q_rope [T,64,64], kv [rows,576], w_uk [64,512,192],
+ *   w_uv [64,512,256]: bf16.  idx [T,k] int32 (-1 = absent; any order).
+ *   out [T,64,256]: bf16 (out_dtype DSA_OUT_BF16) or fp32 (DSA_OUT_F32).
+ *   A query with no valid entry gets a zero output.
+ *   ws: dsa_workspace_bytes(DSA_OP_SPARSE_MLA, T, max_ctx, k) bytes.
+ */
+dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
+                               const dsa_bf16* q_rope, const dsa_bf16* kv,
+                               const dsa_bf16* w_uk, const dsa_bf16* w_uv, const int32_t* idx,
+                               int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole path (page-5 DSA flow): dsa_index_scores -> dsa_topk ->
+ * dsa_sparse_mla_attn on one stream, in query chunks sized to the workspace.
+ * Same inputs and outputs as the three calls.  idx_out [T,k] receives the
+ * selection when not NULL (e.g. for reuse by later layers).
+ *   ws: at least dsa_workspace_bytes(DSA_OP_FORWARD, 1, max_ctx, k) bytes;
+ *   dsa_workspace_bytes(DSA_OP_FORWARD, T, max_ctx, k) runs T queries per chunk.
+ */
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                       const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                       const dsa_bf16* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                       int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an op needs for num_queries queries (host only; 0 = none).
+ * Returns 0 as well for invalid arguments (then the op itself reports them). */
+size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int32_t k);
+
+/* Static description of a status code (never NULL). */
+const char* dsa_status_string(int32_t status);
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+
+/* hipError_t of the last DSA_ERR_LAUNCH / DSA_ERR_DEVICE on this thread (0 = none). */
+int32_t dsa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,258 @@
+// C ABI of the DSA hot path: argument checks, workspace planning, query
+// chunking and kernel launches on the caller's stream.  No allocation, no
+// host synchronisation, nothing enqueued when a check fails.
+#include <atomic>
+#include <cstring>
+
+#include "dsa.h"
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+// Upper bounds that keep every grid dimension and 32-bit index in range.
+constexpr int32_t kMaxQueries = 1 << 21;
+constexpr int32_t kMaxCtx = 1 << 24;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dsa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorNoDevice);
+    return DSA_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return DSA_OK;
+    if (s == 2) return DSA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return DSA_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+dsa_status check_batch(const dsa_batch* b) {
+  if (!b) return DSA_ERR_NULL;
+  if (b->num_queries < 0 || b->num_queries > kMaxQueries) return DSA_ERR_SHAPE;
+  if (b->num_seqs < 1 || b->max_ctx < 1 || b->max_ctx > kMaxCtx || b->reserved != 0)
+    return DSA_ERR_SHAPE;
+  if (b->num_queries > 0 && (!b->q_seq || !b->q_pos || !b->seq_row0)) return DSA_ERR_NULL;
+  return DSA_OK;
+}
+
+dsa_status check_scores(const dsa_batch* b, const void* scores, int64_t ld) {
+  if (!scores) return DSA_ERR_NULL;
+  if (ld < b->max_ctx) return DSA_ERR_SHAPE;
+  if ((ld & 3) != 0 || !aligned16(scores)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+dsa_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return DSA_OK;
+  g_last_hip_error = (int32_t)e;
+  return DSA_ERR_LAUNCH;
+}
+
+dsa::LaunchBatch to_launch(const dsa_batch* b, int t0, int T) {
+  dsa::LaunchBatch lb;
+  lb.T = T;
+  lb.max_ctx = b->max_ctx;
+  lb.q_seq = b->q_seq + t0;
+  lb.q_pos = b->q_pos + t0;
+  lb.seq_row0 = b->seq_row0;
+  return lb;
+}
+
+int64_t score_ld(int32_t max_ctx) { return ((int64_t)max_ctx + 3) / 4 * 4; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool use_gemm(const dsa_batch* b) {
+  return b->num_queries >= 8 && (int64_t)b->num_queries >= 8 * (int64_t)b->num_seqs;
+}
+
+// Workspace of dsa_forward for a chunk of T queries.
+struct FwdPlan {
+  size_t scores_off, idx_off, mla_off, total;
+  dsa::MlaPlan mla;
+};
+FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
+  FwdPlan f{};
+  f.scores_off = 0;
+  size_t end = align256((size_t)T * score_ld(max_ctx) * sizeof(float));
+  f.idx_off = end;
+  if (need_idx) end += align256((size_t)T * k * sizeof(int32_t));
+  f.mla_off = end;
+  f.mla = dsa::plan_mla(T, k);
+  f.total = end + f.mla.total;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+int32_t dsa_last_hip_error(void) { return g_last_hip_error; }
+
+const char* dsa_status_string(int32_t s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "a size argument is out of range";
+    case DSA_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_UNSUPPORTED: return "unsupported option";
+    case DSA_ERR_LAUNCH: return "kernel launch failed";
+    case DSA_ERR_DEVICE: return "no gfx950 HIP device is current";
+    default: return "unknown status";
+  }
+}
+
+size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int32_t k) {
+  if (num_queries < 0 || num_queries > kMaxQueries || max_ctx < 1 || max_ctx > kMaxCtx) return 0;
+  switch (op) {
+    case DSA_OP_INDEX_SCORES: return 0;
+    case DSA_OP_TOPK: return 0;
+    case DSA_OP_SPARSE_MLA:
+      if (k < 1 || k > DSA_MAX_TOPK) return 0;
+      return dsa::plan_mla(num_queries, k).total;
+    case DSA_OP_FORWARD:
+      if (k < 1 || k > DSA_MAX_TOPK) return 0;
+      return plan_forward(num_queries, max_ctx, k, true).total;
+    default: return 0;
+  }
+}
+
+dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                            const dsa_bf16* k_idx, float* scores, int64_t ld_scores,
+                            void* stream) {
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (batch->num_queries == 0) return DSA_OK;
+  if (!q_idx || !w || !k_idx) return DSA_ERR_NULL;
+  if ((s = check_scores(batch, scores, ld_scores)) != DSA_OK) return s;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx)) return DSA_ERR_ALIGN;
+  if ((s = check_device()) != DSA_OK) return s;
+  (void)hipGetLastError();
+  return launch_status(dsa::launch_index_scores(to_launch(batch, 0, batch->num_queries), q_idx, w,
+                                                k_idx, scores, ld_scores, use_gemm(batch),
+                                                (hipStream_t)stream));
+}
+
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (batch->num_queries == 0) return DSA_OK;
+  if ((s = check_scores(batch, scores, ld_scores)) != DSA_OK) return s;
+  if (!idx) return DSA_ERR_NULL;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  if ((s = check_device()) != DSA_OK) return s;
+  (void)hipGetLastError();
+  return launch_status(dsa::launch_topk(to_launch(batch, 0, batch->num_queries), scores,
+                                        ld_scores, k, idx, (hipStream_t)stream));
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
+                               const dsa_bf16* q_rope, const dsa_bf16* kv,
+                               const dsa_bf16* w_uk, const dsa_bf16* w_uv, const int32_t* idx,
+                               int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                               void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (batch->num_queries == 0) return DSA_OK;
+  if (!q_nope || !q_rope || !kv || !w_uk || !w_uv || !idx || !out) return DSA_ERR_NULL;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  if (out_dtype != DSA_OUT_BF16 && out_dtype != DSA_OUT_F32) return DSA_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return DSA_ERR_SHAPE;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(out))
+    return DSA_ERR_ALIGN;
+  const dsa::MlaPlan plan = dsa::plan_mla(batch->num_queries, k);
+  if (!ws) return DSA_ERR_NULL;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  if (ws_bytes < plan.total) return DSA_ERR_WORKSPACE;
+  if ((s = check_device()) != DSA_OK) return s;
+  (void)hipGetLastError();
+  return launch_status(dsa::launch_sparse_mla(to_launch(batch, 0, batch->num_queries), plan,
+                                              q_nope, q_rope, kv, w_uk, w_uv, idx, softmax_scale,
+                                              out, out_dtype == DSA_OUT_F32, ws,
+                                              (hipStream_t)stream));
+}
+
+dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                       const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                       const dsa_bf16* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                       int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                       int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (batch->num_queries == 0) return DSA_OK;
+  if (!q_idx || !w || !k_idx || !q_nope || !q_rope || !kv || !w_uk || !w_uv || !out)
+    return DSA_ERR_NULL;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  if (out_dtype != DSA_OUT_BF16 && out_dtype != DSA_OUT_F32) return DSA_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || softmax_scale > 1e30f) return DSA_ERR_SHAPE;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(q_nope) ||
+      !aligned16(q_rope) || !aligned16(kv) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(out))
+    return DSA_ERR_ALIGN;
+  const int32_t T = batch->num_queries;
+  if (!ws) return DSA_ERR_NULL;
+  if (!aligned16(ws)) return DSA_ERR_ALIGN;
+  const bool need_idx = idx_out == nullptr;
+  // Largest chunk (by halving) for which both the full chunks and the last,
+  // shorter one fit (a short chunk may use more key splits per query).
+  auto fits = [&](int32_t c) {
+    if (plan_forward(c, batch->max_ctx, k, need_idx).total > ws_bytes) return false;
+    const int32_t rem = T % c;
+    return rem == 0 || plan_forward(rem, batch->max_ctx, k, need_idx).total <= ws_bytes;
+  };
+  int32_t tc = T;
+  while (tc > 1 && !fits(tc)) tc = (tc + 1) / 2;
+  if (!fits(tc)) return DSA_ERR_WORKSPACE;
+  if ((s = check_device()) != DSA_OK) return s;
+  (void)hipGetLastError();
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t ld = score_ld(batch->max_ctx);
+  const bool gemm = use_gemm(batch);
+  char* base = static_cast<char*>(ws);
+  const size_t out_elem = out_dtype == DSA_OUT_F32 ? sizeof(float) : sizeof(uint16_t);
+  for (int32_t t0 = 0; t0 < T; t0 += tc) {
+    const int32_t n = T - t0 < tc ? T - t0 : tc;
+    const FwdPlan p = plan_forward(n, batch->max_ctx, k, need_idx);
+    const dsa::LaunchBatch lb = to_launch(batch, t0, n);
+    float* scores = reinterpret_cast<float*>(base + p.scores_off);
+    int32_t* idx = need_idx ? reinterpret_cast<int32_t*>(base + p.idx_off) : idx_out + (int64_t)t0 * k;
+    hipError_t e = dsa::launch_index_scores(lb, q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
+                                            w + (int64_t)t0 * DSA_INDEX_HEADS, k_idx, scores, ld,
+                                            gemm, st);
+    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, st);
+    if (e == hipSuccess)
+      e = dsa::launch_sparse_mla(lb, p.mla, q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM,
+                                 q_rope + (int64_t)t0 * DSA_HEADS * DSA_QK_ROPE_DIM, kv, w_uk,
+                                 w_uv, idx, softmax_scale,
+                                 static_cast<char*>(out) + (size_t)t0 * DSA_HEADS * DSA_V_DIM * out_elem,
+                                 out_dtype == DSA_OUT_F32, base + p.mla_off, st);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

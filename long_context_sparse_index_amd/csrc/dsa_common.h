@@ -1,0 +1,90 @@
+// Device helpers shared by the DSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kIdxHeads = 32;
+constexpr int kIdxDim = 128;
+constexpr int kHeads = 64;
+constexpr int kNope = 192;
+constexpr int kRope = 64;
+constexpr int kQk = kNope + kRope;    // 256
+constexpr int kV = 256;
+constexpr int kLat = 512;
+constexpr int kRow = kLat + kRope;    // 576 bf16 per latent-cache row
+constexpr int kMaxTopk = 2048;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> packed bf16x2 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// D = A(32x16) * B(16x32) + C.  Lane l supplies A row l%32 and B column l%32,
+// each with 8 K-elements for K-group l/32.  Output element j of lane l is
+// C[8*(j/4) + 4*(l/32) + j%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// D = A(16x32) * B(32x16) + C.  Lane l supplies A row l%16 and B column l%16,
+// each with 8 K-elements for K-group l/16.  Output element j of lane l is
+// C[4*(l/16) + j][l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Lane exchange within a wave (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int xor_lane(int v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Monotone unsigned image of an fp32 score: larger float <-> larger key, and
+// -0.0 maps to the key of +0.0.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0) u = 0;  // +-0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace dsa

@@ -1,0 +1,38 @@
+// Internal launch interface between the C ABI (dsa_abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct LaunchBatch {
+  int T;                   // queries in this launch
+  int max_ctx;             // host bound of q_pos + 1
+  const int32_t* q_seq;    // [T] device
+  const int32_t* q_pos;    // [T] device
+  const int64_t* seq_row0; // [B] device
+};
+
+// Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries.
+hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                               const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
+                               hipStream_t st);
+
+// Top-k selection, one workgroup per query row.
+hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
+                       hipStream_t st);
+
+// Sparse MLA: workspace layout and launches.
+struct MlaPlan {
+  int T, k, splits, keys_per_split;
+  size_t q_lat_off, o_lat_off, part_off, ml_off, total;
+};
+MlaPlan plan_mla(int T, int k);
+hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
+                             const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
+                             const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
+                             int out_f32, void* ws, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,208 @@
+// Lightning-indexer scoring on gfx950.
+//
+// score(t,s) = sum_{h<32} w[t,h] * ReLU(q_idx[t,h,:] . k_idx[s,:]),  s <= q_pos[t]
+// (page "2026大模型架构概览（二）：GLM 5 DSV3.2 的 DSA 与 MoE 配置拆解", §2.2: one cheap score
+// per query and history token, used only for ranking; page "（五）一万亿次点积砍到两千次：
+// DSA 怎么破 N²", indexer section: 32 heads of 128-d dot products over every token).
+//
+// Both kernels put the 32 indexer heads of one query on the M side of a
+// 32x32x16 bf16 MFMA and 32 keys on the N side; K = 128 is 8 MFMA steps.  The
+// epilogue applies ReLU and the head weights in fp32 and folds the 32 head rows
+// of each key column (16 per lane, then one cross-half lane exchange).
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------- decode scan
+// One workgroup = one query x kScanChunk keys.  Each wave streams
+// kScanTiles tiles of 32 keys (8 KB contiguous each); all of its loads are in
+// flight before the first MFMA.  Keys are read non-temporally: in decode they
+// are touched once per step.
+constexpr int kScanWaves = 4;
+constexpr int kScanTiles = 4;
+constexpr int kScanChunk = kScanWaves * kScanTiles * 32;
+
+__global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    float* __restrict__ scores, int64_t ld) {
+  const int t = blockIdx.x;
+  const int pos = q_pos[t];
+  const int chunk0 = blockIdx.y * kScanChunk;
+  if (chunk0 > pos) return;
+  const int64_t row0 = seq_row0[q_seq[t]];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+
+  // A operand: head n of query t, K-group g (dims 16j + 8g .. +8 at step j).
+  bf16x8 qa[8];
+  const uint16_t* qp = q_idx + ((int64_t)t * kIdxHeads + n) * kIdxDim + 8 * g;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(ld16(qp + 16 * j));
+  // Head weights of the accumulator rows this lane holds.
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = bf16_to_f32(w[t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)]);
+
+  const int wbase = chunk0 + wave * kScanTiles * 32;
+  u32x4 kb[kScanTiles][8];
+#pragma unroll
+  for (int it = 0; it < kScanTiles; ++it) {
+    const int s = min(wbase + it * 32 + n, pos);  // clamp: rows past pos are never used
+    const uint16_t* kp = k_idx + (row0 + s) * kIdxDim + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kb[it][j] = ld16_nt(kp + 16 * j);
+  }
+  float* srow = scores + (int64_t)t * ld;
+#pragma unroll
+  for (int it = 0; it < kScanTiles; ++it) {
+    if (wbase + it * 32 > pos) break;
+    f32x16 acc = {};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = mfma32(qa[j], as_bf16x8(kb[it][j]), acc);
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part = fmaf(wr[r], fmaxf(acc[r], 0.f), part);
+    const float tot = part + xor_lane(part, 32);
+    const int s = wbase + it * 32 + n;
+    if (g == 0 && s <= pos) srow[s] = tot;
+  }
+}
+
+// ---------------------------------------------------------------- prefill GEMM
+// One workgroup = kGemmQB consecutive queries x kGemmSplit keys.  Each wave
+// keeps kGemmQPW queries (32 heads each) as resident A operands; key tiles of
+// kGemmKT keys are staged through LDS (double buffered) and shared by the four
+// waves.  Queries of one block normally share a sequence; a block that mixes
+// sequences is processed once per distinct sequence.
+constexpr int kGemmQPW = 2;
+constexpr int kGemmQB = 4 * kGemmQPW;
+constexpr int kGemmKT = 64;
+constexpr int kGemmSplit = 8192;
+constexpr int kKeyLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
+
+__global__ __launch_bounds__(256) void idx_gemm_kernel(
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
+    const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    float* __restrict__ scores, int64_t ld, int T) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kGemmKT * kKeyLds];
+  __shared__ int s_seq[kGemmQB], s_pos[kGemmQB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int t0 = blockIdx.x * kGemmQB;
+  if (tid < kGemmQB) {
+    const int t = t0 + tid;
+    s_seq[tid] = t < T ? q_seq[t] : -1;
+    s_pos[tid] = t < T ? q_pos[t] : -1;
+  }
+  __syncthreads();
+  const int split0 = blockIdx.y * kGemmSplit;
+  int maxpos = -1;
+#pragma unroll
+  for (int i = 0; i < kGemmQB; ++i) maxpos = max(maxpos, s_pos[i]);
+  if (split0 > maxpos) return;
+
+  bf16x8 qa[kGemmQPW][8];
+  float wr[kGemmQPW][16];
+#pragma unroll
+  for (int qi = 0; qi < kGemmQPW; ++qi) {
+    const int tt = min(t0 + wave * kGemmQPW + qi, T - 1);
+    const uint16_t* qp = q_idx + ((int64_t)tt * kIdxHeads + n) * kIdxDim + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qa[qi][j] = as_bf16x8(ld16(qp + 16 * j));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[qi][r] = bf16_to_f32(w[tt * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)]);
+  }
+
+  for (int i = 0; i < kGemmQB; ++i) {
+    const int sq = s_seq[i];
+    if (sq < 0) continue;
+    bool seen = false;
+    int hi = -1;
+    for (int j = 0; j < kGemmQB; ++j) {
+      if (j < i && s_seq[j] == sq) seen = true;
+      if (s_seq[j] == sq) hi = max(hi, s_pos[j]);
+    }
+    if (seen) continue;
+    const int kbeg = split0;
+    const int kend = min(split0 + kGemmSplit, hi + 1);
+    if (kbeg >= kend) continue;
+    const int64_t row0 = seq_row0[sq];
+    const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
+
+    // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 4 per thread.
+    u32x4 stage[4];
+    auto gload = [&](int tile) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int lin = tid + 256 * c;
+        const int key = min(kbeg + tile * kGemmKT + (lin >> 4), hi);
+        stage[c] = ld16(k_idx + (row0 + key) * kIdxDim + (lin & 15) * 8);
+      }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int lin = tid + 256 * c;
+        st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
+      }
+    };
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int buf = tile & 1;
+      if (tile + 1 < ntiles) gload(tile + 1);
+      const int sbase = kbeg + tile * kGemmKT;
+      bf16x8 bfr[2][8];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          bfr[nt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              &ks[buf][(nt * 32 + n) * kKeyLds + 16 * j + 8 * g]));
+#pragma unroll
+      for (int qi = 0; qi < kGemmQPW; ++qi) {
+        const int local = wave * kGemmQPW + qi;
+        const int pos = s_pos[local];
+        if (s_seq[local] != sq || sbase > pos) continue;
+        float* srow = scores + (int64_t)(t0 + local) * ld;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc = mfma32(qa[qi][j], bfr[nt][j], acc);
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], fmaxf(acc[r], 0.f), part);
+          const float tot = part + xor_lane(part, 32);
+          const int s = sbase + nt * 32 + n;
+          if (g == 0 && s <= pos) srow[s] = tot;
+        }
+      }
+      if (tile + 1 < ntiles) lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                               const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
+                               hipStream_t st) {
+  if (gemm) {
+    dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (b.max_ctx + kGemmSplit - 1) / kGemmSplit);
+    idx_gemm_kernel<<<grid, 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx, scores,
+                                          ld, b.T);
+  } else {
+    dim3 grid(b.T, (b.max_ctx + kScanChunk - 1) / kScanChunk);
+    idx_scan_kernel<<<grid, kScanWaves * 64, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w,
+                                                      k_idx, scores, ld);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

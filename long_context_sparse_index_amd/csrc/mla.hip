@@ -1,0 +1,371 @@
+// Sparse MLA over the selected positions on gfx950 (weight-absorbed form).
+//
+// For query t, head h and kept cache rows (c_j | r_j):
+//   z_j = scale * (q_nope[t,h] . (c_j W_UK[h]) + q_rope[t,h] . r_j)
+//   out[t,h] = sum_j softmax(z)_j (c_j W_UV[h])
+// (page "（五）一万亿次点积砍到两千次：DSA 怎么破 N²", DSA flow: full Q.K.V over the kept
+// tokens, softmax, weighted V; page "2026大模型架构概览（二）：GLM 5 DSV3.2 的 DSA 与 MoE
+// 配置拆解", §2.1 dims and §2.2: DSA is a filter in front of MLA.)
+// Computed as
+//   absorb   q_lat[t,h] = W_UK[h] q_nope[t,h]                (bf16 out)
+//   core     logits against the 512-d latent + 64-d rope key, online softmax,
+//            o_lat[t,h] = sum_j p_j c_j                       (split over keys)
+//   merge    combine key splits (log-sum-exp)                 (bf16 out)
+//   upproj   out[t,h] = o_lat[t,h] W_UV[h]
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------- absorb
+// grid (64 heads, 4 blocks of 128 latent columns, ceil(T/32)); wave w owns 32
+// latent columns.  A = q_nope rows (queries), B[k=d][n=c] = W_UK[h][c][d]:
+// both operands are contiguous 16-byte loads.
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                     const uint16_t* __restrict__ w_uk,
+                                                     uint16_t* __restrict__ q_lat, int T) {
+  const int h = blockIdx.x, cb = blockIdx.y, tb = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int t = min(tb * 32 + n, T - 1);
+  const int c = cb * 128 + wave * 32 + n;
+  const uint16_t* ap = q_nope + ((int64_t)t * kHeads + h) * kNope + 8 * g;
+  const uint16_t* bp = w_uk + ((int64_t)h * kLat + c) * kNope + 8 * g;
+  f32x16 acc = {};
+#pragma unroll
+  for (int j = 0; j < kNope / 16; ++j)
+    acc = mfma32(as_bf16x8(ld16(ap + 16 * j)), as_bf16x8(ld16(bp + 16 * j)), acc);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tr = tb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    if (tr < T) q_lat[((int64_t)tr * kHeads + h) * kLat + c] = (uint16_t)f32_to_bf16_bits(acc[r]);
+  }
+}
+
+// ---------------------------------------------------------------- core
+// grid (T, splits); 4 waves, wave w owns heads 16w..16w+15 (16x16x32 MFMAs).
+// Tiles of 32 gathered rows are staged in LDS (double buffered).
+//   QK:  logits^T[key][head] = c_tile[key][576] . q[head][576]^T  (A from LDS, B resident)
+//   PV:  o^T[dim][head] += c_tile^T[dim][key] . P^T[key][head]
+// The PV K order (keys) follows the QK accumulator layout, so P feeds the MFMA
+// straight from registers; the transposed latent operand is read from LDS as
+// 4 consecutive dims x 8 keys and repacked with v_perm.
+constexpr int kKT = 32;
+constexpr int kKvLds = kRow + 8;  // 584 bf16 = 1168 B per LDS row
+constexpr int kGatherPerThread = kKT * (kRow / 8) / 256;  // 9 chunks of 16 B
+
+__global__ __launch_bounds__(256) void mla_core_kernel(
+    const int32_t* __restrict__ q_seq, const int64_t* __restrict__ seq_row0,
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int k, float scale_log2,
+    int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
+    float* __restrict__ ml_part) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKT * kKvLds];
+  __shared__ int s_valid[2][kKT];
+  const int t = blockIdx.x, sp = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int j0 = sp * kps;
+  const int j1 = min(k, j0 + kps);
+  const int64_t row0 = seq_row0[q_seq[t]];
+  const int32_t* irow = idx + (int64_t)t * k;
+  const int hq = wave * 16 + l16;
+
+  bf16x8 qb[18];
+  {
+    const uint16_t* ql = q_lat + ((int64_t)t * kHeads + hq) * kLat + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(ld16(ql + 32 * ks));
+    const uint16_t* qr = q_rope + ((int64_t)t * kHeads + hq) * kRope + 8 * g;
+    qb[16] = as_bf16x8(ld16(qr));
+    qb[17] = as_bf16x8(ld16(qr + 32));
+  }
+
+  f32x4 o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+
+  const int ntiles = j1 > j0 ? (j1 - j0 + kKT - 1) / kKT : 0;
+  u32x4 stage[kGatherPerThread];
+  auto gload = [&](int tt) {
+#pragma unroll
+    for (int c = 0; c < kGatherPerThread; ++c) {
+      const int lin = tid + 256 * c;
+      const int key = lin / (kRow / 8);
+      const int col = lin - key * (kRow / 8);
+      const int j = j0 + tt * kKT + key;
+      const int s = j < j1 ? irow[j] : -1;
+      stage[c] = s >= 0 ? ld16(kv + (row0 + s) * kRow + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&](int buf, int tt) {
+#pragma unroll
+    for (int c = 0; c < kGatherPerThread; ++c) {
+      const int lin = tid + 256 * c;
+      const int key = lin / (kRow / 8);
+      const int col = lin - key * (kRow / 8);
+      st16(&tile[buf][key * kKvLds + col * 8], stage[c]);
+    }
+    if (tid < kKT) {
+      const int j = j0 + tt * kKT + tid;
+      s_valid[buf][tid] = (j < j1) && irow[j] >= 0;
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0, 0);
+  }
+  __syncthreads();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int buf = tt & 1;
+    if (tt + 1 < ntiles) gload(tt + 1);
+    const uint16_t* tb = tile[buf];
+    // ---- QK for the two 16-key halves
+    f32x4 sc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* ap = tb + (hf * 16 + l16) * kKvLds + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks)
+        sc[hf] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 32 * ks)), qb[ks], sc[hf]);
+    }
+    // ---- online softmax (base 2); lane holds keys hf*16 + 4g + jj of head hq
+    float z[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float v = s_valid[buf][hf * 16 + 4 * g + jj] ? sc[hf][jj] * scale_log2 : -INFINITY;
+        z[hf * 4 + jj] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, xor_lane(tmax, 16));
+    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = exp2f(z[i] - m_new);
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) o[i] *= alpha;
+    const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+    // ---- PV: K element i of K-group g is key (i<4 ? 4g+i : 16+4g+i-4)
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      u32x2 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = (i < 4) ? 4 * g + i : 16 + 4 * g + (i - 4);
+        v[i] = *reinterpret_cast<const u32x2*>(tb + key * kKvLds + 64 * a + 4 * l16);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t x0 = (e < 2) ? v[2 * d].x : v[2 * d].y;
+          const uint32_t x1 = (e < 2) ? v[2 * d + 1].x : v[2 * d + 1].y;
+          f[d] = __builtin_amdgcn_perm(x1, x0, sel);
+        }
+        o[4 * a + e] = mfma16(as_bf16x8(f), pb, o[4 * a + e]);
+      }
+    }
+    if (tt + 1 < ntiles) lstore(buf ^ 1, tt + 1);
+    __syncthreads();
+  }
+
+  // ---- finish: the four K-groups of a head share m_run; sum their l.
+  float l_tot = l_run + xor_lane(l_run, 16);
+  l_tot += xor_lane(l_tot, 32);
+  // o[4a+e][jj] is dim 64a + 16g + 4jj + e of head hq.
+  if (S == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* dst = o_lat + ((int64_t)t * kHeads + hq) * kLat;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x2 v = {pack_bf16x2(o[4 * a][jj] * inv, o[4 * a + 1][jj] * inv),
+                         pack_bf16x2(o[4 * a + 2][jj] * inv, o[4 * a + 3][jj] * inv)};
+        *reinterpret_cast<u32x2*>(dst + 64 * a + 16 * g + 4 * jj) = v;
+      }
+  } else {
+    const int64_t base = ((int64_t)t * S + sp) * kHeads + hq;
+    float* dst = o_part + base * kLat;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 v = {o[4 * a][jj], o[4 * a + 1][jj], o[4 * a + 2][jj], o[4 * a + 3][jj]};
+        *reinterpret_cast<f32x4*>(dst + 64 * a + 16 * g + 4 * jj) = v;
+      }
+    if (g == 0) {
+      ml_part[base * 2] = m_run;
+      ml_part[base * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge
+// grid (T, 64 heads); thread i combines latent dims 2i, 2i+1 over the splits.
+__global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ o_part,
+                                                        const float* __restrict__ ml_part, int S,
+                                                        uint16_t* __restrict__ o_lat) {
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  float mstar = -1e30f;
+  for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml_part[(((int64_t)t * S + s) * kHeads + h) * 2]);
+  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const int64_t base = ((int64_t)t * S + s) * kHeads + h;
+    const float wgt = exp2f(ml_part[base * 2] - mstar);
+    L += wgt * ml_part[base * 2 + 1];
+    const float* src = o_part + base * kLat + 2 * tid;
+    a0 += wgt * src[0];
+    a1 += wgt * src[1];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<uint32_t*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 2 * tid) =
+      pack_bf16x2(a0 * inv, a1 * inv);
+}
+
+// ---------------------------------------------------------------- upproj
+// grid (64 heads, 4 blocks of 64 output dims, ceil(T / (32*kUpMT))).
+// W_UV[h][:, block] is staged in LDS transposed ([e][c]) so that the B operand
+// (8 consecutive c for one e) is one 16-byte LDS read.  Waves: (N-tile of 32
+// dims) x (half of the 512-long K); the two K halves are summed through LDS.
+constexpr int kUpEB = 64;
+constexpr int kUpMT = 4;
+constexpr int kWvLds = kLat + 8;
+
+__global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict__ o_lat,
+                                                     const uint16_t* __restrict__ w_uv,
+                                                     void* __restrict__ out, int out_f32, int T) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kUpEB * kWvLds];
+  __shared__ float red[2][64 * 16];
+  const int h = blockIdx.x, eb = blockIdx.y, mb = blockIdx.z;
+  const int tid = threadIdx.x;
+  for (int u = tid; u < (kLat / 4) * (kUpEB / 8); u += 256) {
+    const int q = u >> 3, r = u & 7;  // c = 4q..4q+3, e = 8r..8r+7
+    u32x4 rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rows[i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
+      const int dw = e8 >> 1;
+      const u32x2 v = {__builtin_amdgcn_perm(rows[1][dw], rows[0][dw], sel),
+                       __builtin_amdgcn_perm(rows[3][dw], rows[2][dw], sel)};
+      *reinterpret_cast<u32x2*>(&wt[(8 * r + e8) * kWvLds + 4 * q]) = v;
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int nt = wave & 1, kh = wave >> 1;
+  const uint16_t* bp = &wt[(nt * 32 + n) * kWvLds + kh * 256 + 8 * g];
+  for (int mt = 0; mt < kUpMT; ++mt) {
+    const int tbase = (mb * kUpMT + mt) * 32;
+    if (tbase >= T) break;
+    const int trow = min(tbase + n, T - 1);
+    const uint16_t* ap = o_lat + ((int64_t)trow * kHeads + h) * kLat + kh * 256 + 8 * g;
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      acc = mfma32(as_bf16x8(ld16(ap + 16 * ks)),
+                   as_bf16x8(*reinterpret_cast<const u32x4*>(bp + 16 * ks)), acc);
+    if (kh == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[nt][lane * 16 + r] = acc[r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const int e = eb * kUpEB + nt * 32 + n;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = tbase + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float v = acc[r] + red[nt][lane * 16 + r];
+        if (tr < T) {
+          const int64_t o = ((int64_t)tr * kHeads + h) * kV + e;
+          if (out_f32) reinterpret_cast<float*>(out)[o] = v;
+          else reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- plan + launch
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+MlaPlan plan_mla(int T, int k) {
+  MlaPlan p{};
+  p.T = T;
+  p.k = k;
+  int s = 1;
+  if (T > 0 && T < 256) s = (256 + T - 1) / T;
+  s = s < 16 ? s : 16;
+  const int max_s = (k + kKT - 1) / kKT;
+  s = s < max_s ? s : max_s;
+  if (s < 1) s = 1;
+  int kps = (k + s - 1) / s;
+  kps = (kps + kKT - 1) / kKT * kKT;
+  p.keys_per_split = kps;
+  p.splits = (k + kps - 1) / kps;
+  const size_t lat = (size_t)T * kHeads * kLat * sizeof(uint16_t);
+  p.q_lat_off = 0;
+  p.o_lat_off = align_up(lat, 256);
+  size_t end = p.o_lat_off + align_up(lat, 256);
+  if (p.splits > 1) {
+    p.part_off = end;
+    end += align_up((size_t)T * p.splits * kHeads * kLat * sizeof(float), 256);
+    p.ml_off = end;
+    end += align_up((size_t)T * p.splits * kHeads * 2 * sizeof(float), 256);
+  }
+  p.total = end;
+  return p;
+}
+
+hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
+                             const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
+                             const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
+                             int out_f32, void* ws, hipStream_t st) {
+  char* base = static_cast<char*>(ws);
+  uint16_t* q_lat = reinterpret_cast<uint16_t*>(base + p.q_lat_off);
+  uint16_t* o_lat = reinterpret_cast<uint16_t*>(base + p.o_lat_off);
+  float* o_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.part_off) : nullptr;
+  float* ml_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
+  const int T = b.T;
+  absorb_kernel<<<dim3(kHeads, kLat / 128, (T + 31) / 32), 256, 0, st>>>(q_nope, w_uk, q_lat, T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  mla_core_kernel<<<dim3(T, p.splits), 256, 0, st>>>(b.q_seq, b.seq_row0, q_lat, q_rope, kv, idx,
+                                                     p.k, scale_log2, p.keys_per_split, p.splits,
+                                                     o_lat, o_part, ml_part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.splits > 1) {
+    mla_merge_kernel<<<dim3(T, kHeads), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  upproj_kernel<<<dim3(kHeads, kV / kUpEB, (T + 32 * kUpMT - 1) / (32 * kUpMT)), 256, 0, st>>>(
+      o_lat, w_uv, out, out_f32, T);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,221 @@
+"""Thin Python binding of libdsa.so (the C ABI in include/dsa.h).
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, and their device pointers are handed to the library together with
+torch's current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+IDX_HEADS, IDX_DIM = 32, 128
+HEADS, D_NOPE, D_ROPE, D_V, D_LAT = 64, 192, 64, 256, 512
+D_KV = D_LAT + D_ROPE
+MAX_TOPK = 2048
+DEFAULT_SCALE = 1.0 / 16.0
+
+OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
+OUT_BF16, OUT_F32 = 0, 1
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip_error: int):
+        super().__init__(f"{fn}: status {status} ({msg}); last hip error {hip_error}")
+        self.status = status
+        self.hip_error = hip_error
+
+
+class _CBatch(ctypes.Structure):
+    _fields_ = [
+        ("num_queries", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("q_seq", ctypes.c_void_p),
+        ("q_pos", ctypes.c_void_p),
+        ("seq_row0", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "dsa_index_scores": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, ctypes.c_int64, _P], ctypes.c_int),
+    "dsa_topk": ([ctypes.POINTER(_CBatch), _P, ctypes.c_int64, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P],
+                 ctypes.c_int),
+    "dsa_sparse_mla_attn": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                             _P, ctypes.c_int32, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "dsa_forward": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                     _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "dsa_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], ctypes.c_size_t),
+    "dsa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
+    "dsa_abi_version": ([], ctypes.c_int32),
+    "dsa_last_hip_error": ([], ctypes.c_int32),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} not built: run `python -m long_context_sparse_index_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise DsaError(fn, status, L.dsa_status_string(status).decode(), L.dsa_last_hip_error())
+
+
+def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
+    return None if x is None else x.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _bf16(x: torch.Tensor, name: str, shape) -> torch.Tensor:
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bf16 bits, got {x.dtype}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(x.shape)} != {tuple(shape)}")
+    return x
+
+
+class Batch:
+    """Batch geometry: q_seq [T] int32, q_pos [T] int32, seq_row0 [B] int64 on the device."""
+
+    def __init__(self, q_seq: torch.Tensor, q_pos: torch.Tensor, seq_row0: torch.Tensor, max_ctx: int):
+        for name, x, dt in (("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
+                            ("seq_row0", seq_row0, torch.int64)):
+            if x.dtype != dt or not x.is_cuda or not x.is_contiguous() or x.dim() != 1:
+                raise ValueError(f"{name}: expected a contiguous 1-D {dt} device tensor")
+        if q_seq.shape != q_pos.shape:
+            raise ValueError("q_seq and q_pos differ in length")
+        self.q_seq, self.q_pos, self.seq_row0 = q_seq, q_pos, seq_row0
+        self.max_ctx = int(max_ctx)
+        self.T = int(q_seq.shape[0])
+        self.B = int(seq_row0.shape[0])
+
+    def c(self) -> _CBatch:
+        return _CBatch(self.T, self.B, self.max_ctx, 0, _ptr(self.q_seq), _ptr(self.q_pos), _ptr(self.seq_row0))
+
+    def slice(self, t0: int, t1: int) -> "Batch":
+        return Batch(self.q_seq[t0:t1], self.q_pos[t0:t1], self.seq_row0, self.max_ctx)
+
+
+def score_ld(max_ctx: int) -> int:
+    return (max_ctx + 3) // 4 * 4
+
+
+def dsa_workspace_bytes(op: int, num_queries: int, max_ctx: int, k: int) -> int:
+    return int(lib().dsa_workspace_bytes(op, num_queries, max_ctx, k))
+
+
+def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Indexer scores [T, ld] fp32 (only s <= q_pos[t] written)."""
+    T = batch.T
+    _bf16(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM))
+    _bf16(w, "w", (T, IDX_HEADS))
+    _bf16(k_idx, "k_idx", None)
+    if scores is None:
+        scores = torch.empty((T, score_ld(batch.max_ctx)), dtype=torch.float32, device=q_idx.device)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores: expected a row-major 2-D fp32 tensor")
+    cb = batch.c()
+    _check("dsa_index_scores", lib().dsa_index_scores(ctypes.byref(cb), _ptr(q_idx), _ptr(w), _ptr(k_idx),
+                                                      _ptr(scores), scores.stride(0), _stream()))
+    return scores
+
+
+def dsa_topk(batch: Batch, scores: torch.Tensor, k: int = MAX_TOPK,
+             idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k positions [T, k] int32, ascending, -1 padded."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores: expected a row-major 2-D fp32 tensor")
+    if idx is None:
+        idx = torch.empty((batch.T, k), dtype=torch.int32, device=scores.device)
+    cb = batch.c()
+    _check("dsa_topk", lib().dsa_topk(ctypes.byref(cb), _ptr(scores), scores.stride(0), k, _ptr(idx),
+                                      None, 0, _stream()))
+    return idx
+
+
+def dsa_sparse_mla_attn(batch: Batch, q_nope, q_rope, kv, w_uk, w_uv, idx: torch.Tensor,
+                        softmax_scale: float = DEFAULT_SCALE, out_dtype=torch.bfloat16,
+                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse MLA output [T, 64, 256] over the positions in idx (-1 = absent)."""
+    T = batch.T
+    _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
+    _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
+    _bf16(kv, "kv", None)
+    _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
+    _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != T or not idx.is_contiguous():
+        raise ValueError("idx: expected a contiguous [T, k] int32 tensor")
+    k = int(idx.shape[1])
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((T, HEADS, D_V), dtype=torch.float32 if od else torch.bfloat16, device=kv.device)
+    need = dsa_workspace_bytes(OP_SPARSE_MLA, T, batch.max_ctx, k)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=kv.device)
+    cb = batch.c()
+    _check("dsa_sparse_mla_attn",
+           lib().dsa_sparse_mla_attn(ctypes.byref(cb), _ptr(q_nope), _ptr(q_rope), _ptr(kv), _ptr(w_uk), _ptr(w_uv),
+                                     _ptr(idx), k, softmax_scale, _ptr(out), od, _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k: int = MAX_TOPK,
+                softmax_scale: float = DEFAULT_SCALE, out_dtype=torch.bfloat16, return_idx: bool = True,
+                ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                idx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Indexer -> top-k -> sparse MLA.  Returns (out [T,64,256], idx [T,k] or None)."""
+    T = batch.T
+    _bf16(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM))
+    _bf16(w, "w", (T, IDX_HEADS))
+    _bf16(k_idx, "k_idx", None)
+    _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
+    _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
+    _bf16(kv, "kv", None)
+    _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
+    _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if out is None:
+        out = torch.empty((T, HEADS, D_V), dtype=torch.float32 if od else torch.bfloat16, device=kv.device)
+    if return_idx and idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=kv.device)
+    if ws is None:
+        need = dsa_workspace_bytes(OP_FORWARD, T, batch.max_ctx, k)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=kv.device)
+    cb = batch.c()
+    _check("dsa_forward",
+           lib().dsa_forward(ctypes.byref(cb), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q_nope), _ptr(q_rope),
+                             _ptr(kv), _ptr(w_uk), _ptr(w_uv), k, softmax_scale, _ptr(out), od,
+                             _ptr(idx) if return_idx else None, _ptr(ws), ws.numel(), _stream()))
+    return out, (idx if return_idx else None)

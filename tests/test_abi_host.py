@@ -1,0 +1,121 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before touching the device (no kernels are launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_index_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced here
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.library_path()):
+        pytest.fail("libdsa.so not built (run python -m long_context_sparse_index_amd.build)")
+    return dsa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert set(names) == set(dsa.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.dsa_abi_version() == 1
+    for s in range(8):
+        assert L.dsa_status_string(s)
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+def _batch(T=4, B=1, max_ctx=100):
+    return dsa._CBatch(T, B, max_ctx, 0, FAKE, FAKE, FAKE)
+
+
+def test_index_scores_validation(L):
+    b = _batch()
+    f = L.dsa_index_scores
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 100, None) == 1
+    assert f(ctypes.byref(b), None, FAKE, FAKE, FAKE, 100, None) == 1
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 96, None) == 2      # ld < max_ctx
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 102, None) == 3     # ld % 4
+    assert f(ctypes.byref(b), FAKE + 2, FAKE, FAKE, FAKE, 100, None) == 3  # misaligned bf16
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE + 4, 100, None) == 3  # misaligned scores
+    bad = _batch(T=-1)
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
+    bad = _batch(B=0)
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
+    bad = dsa._CBatch(4, 1, 100, 7, FAKE, FAKE, FAKE)  # reserved != 0
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
+    bad = dsa._CBatch(4, 1, 100, 0, None, FAKE, FAKE)
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 1
+    empty = _batch(T=0)
+    assert f(ctypes.byref(empty), FAKE, FAKE, FAKE, FAKE, 100, None) == 0  # empty call: no-op
+
+
+def test_topk_validation(L):
+    b = _batch()
+    f = L.dsa_topk
+    assert f(ctypes.byref(b), FAKE, 100, 0, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(b), FAKE, 100, 2049, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(b), FAKE, 100, 16, None, None, 0, None) == 1
+    assert f(ctypes.byref(b), None, 100, 16, FAKE, None, 0, None) == 1
+    assert f(ctypes.byref(_batch(T=0)), FAKE, 100, 16, FAKE, None, 0, None) == 0
+
+
+def test_sparse_mla_validation(L):
+    b = _batch()
+    f = L.dsa_sparse_mla_attn
+    args = [FAKE] * 6
+    need = L.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, 4, 100, 2048)
+    assert need > 0
+    assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, FAKE, need - 1, None) == 4   # workspace
+    assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 5, FAKE, need, None) == 5       # out dtype
+    assert f(ctypes.byref(b), *args, 2048, -1.0, FAKE, 0, FAKE, need, None) == 2         # scale
+    assert f(ctypes.byref(b), *args, 4096, 0.0625, FAKE, 0, FAKE, need, None) == 2       # k
+    assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, None, need, None) == 1       # ws NULL
+    assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, FAKE + 8, need, None) == 3   # ws align
+
+
+def test_forward_validation(L):
+    b = _batch()
+    f = L.dsa_forward
+    args = [FAKE] * 8
+    one = L.dsa_workspace_bytes(dsa.OP_FORWARD, 1, 100, 2048)
+    assert 0 < one <= L.dsa_workspace_bytes(dsa.OP_FORWARD, 4, 100, 2048)
+    assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, None, FAKE, one - 1, None) == 4
+    assert f(ctypes.byref(b), *args, 0, 0.0625, FAKE, 0, None, FAKE, one, None) == 2
+    assert f(ctypes.byref(b), *args[:-1], None, 2048, 0.0625, FAKE, 0, None, FAKE, one, None) == 1
+
+
+def test_workspace_bytes(L):
+    assert L.dsa_workspace_bytes(dsa.OP_INDEX_SCORES, 8, 1000, 2048) == 0
+    assert L.dsa_workspace_bytes(dsa.OP_TOPK, 8, 1000, 2048) == 0
+    assert L.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, 8, 1000, 0) == 0        # invalid k
+    assert L.dsa_workspace_bytes(99, 8, 1000, 16) == 0
+    # decode (8 queries): q_lat + o_lat (64 KB each per query) + split partials
+    mla8 = L.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, 8, 204800, 2048)
+    assert mla8 >= 8 * 2 * 64 * 512 * 2
+    fwd = L.dsa_workspace_bytes(dsa.OP_FORWARD, 8, 204800, 2048)
+    assert fwd >= mla8 + 8 * 204800 * 4 + 8 * 2048 * 4
+
+
+def test_valid_call_without_gpu_reports_device_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path")
+    b = _batch()
+    assert L.dsa_index_scores(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None) == 7

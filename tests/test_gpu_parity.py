@@ -1,0 +1,287 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Scores: element-wise within SCORE_MAX_ABS; top-k on oracle scores: bit-exact;
+attention outputs: max-abs 2e-2 and relative L2 1e-2 against the oracle's
+explicit-up-projection MLA; end-to-end selections may differ from the oracle
+only at near-ties of the k-th score.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_index_amd import dsa, synth
+from oracle import dsa_oracle as O
+from tests.gpu_util import (OUT_MAX_ABS, OUT_REL_L2, SCORE_MAX_ABS, bf16_dev, check_selection,
+                            out_errors, run_forward, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _oracle_scores(inp, t):
+    b, p = int(inp.q_seq[t]), int(inp.q_pos[t])
+    r0 = int(inp.seq_row0[b])
+    return O.indexer_scores(inp.q_idx[t], inp.w[t], inp.k_idx[r0: r0 + p + 1], p)
+
+
+def _oracle_out(inp, t, idx_row):
+    b = int(inp.q_seq[t])
+    r0 = int(inp.seq_row0[b])
+    kept = idx_row[idx_row >= 0].astype(np.int64)
+    return O.mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept], inp.w_uk, inp.w_uv)
+
+
+# ------------------------------------------------------------------ indexer
+INDEXER_CASES = {
+    # per-query key scan (few queries per sequence), ragged lengths, position 0
+    "scan_multi_seq": ([1000, 777, 64, 3001, 1], [(0, 999), (1, 500), (2, 0), (3, 3000), (4, 0), (3, 1234)]),
+    # GEMM path: 40 queries of one sequence, unaligned positions, ragged last block
+    "gemm_ragged": ([5000], [(0, 4960 + i) for i in range(37)]),
+    # GEMM path crossing key-split boundaries (8192) with a causal tail
+    "gemm_split_boundary": ([20000], [(0, 16380 + 3 * i) for i in range(16)]),
+    # GEMM path where blocks mix two sequences (interleaved queries)
+    "gemm_mixed_blocks": ([3000, 2500], [(i % 2, 2000 + 7 * i) for i in range(16)]),
+}
+
+
+@pytest.mark.parametrize("case", list(INDEXER_CASES))
+def test_index_scores_match_oracle(case):
+    lens, qs = INDEXER_CASES[case]
+    _say(f"[index_scores] {case}")
+    inp = synth.custom(lens, qs, seed=21)
+    d = to_device(inp)
+    sc = dsa.dsa_index_scores(d.batch, d.q_idx, d.w, d.k_idx)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    worst = 0.0
+    for t in range(len(qs)):
+        ref = _oracle_scores(inp, t)
+        row = got[t, : len(ref)]
+        worst = max(worst, float(np.abs(row.astype(np.float64) - ref).max()))
+    _say(f"  max |score err| = {worst:.3e}")
+    assert worst <= SCORE_MAX_ABS
+
+
+def test_index_scores_write_only_the_causal_prefix():
+    inp = synth.custom([600], [(0, 100), (0, 599), (0, 0)], seed=22)
+    d = to_device(inp)
+    sc = torch.full((3, 604), 12345.0, device="cuda")
+    dsa.dsa_index_scores(d.batch, d.q_idx, d.w, d.k_idx, scores=sc)
+    got = sc.cpu().numpy()
+    assert np.all(got[0, 101:] == 12345.0) and np.all(got[0, :101] != 12345.0)
+    assert np.all(got[2, 1:] == 12345.0)
+
+
+# ------------------------------------------------------------------ top-k (bit-exact)
+def _topk_rows(kind, n_list, seed):
+    rng = np.random.default_rng(seed)
+    return [synth.random_scores(rng, 1, n, kind)[0] for n in n_list]
+
+
+TOPK_CASES = {
+    "normal_ragged": ("normal", [1, 33, 2047, 2048, 2049, 4097, 20000, 131071], 2048),
+    "signed": ("signed", [3000, 50000], 2048),
+    "heavy_ties": ("few_values", [2100, 100000], 2048),   # threshold bin overflows LDS -> global passes
+    "small_k": ("normal", [5000, 100], 7),
+    "k1": ("signed", [1000, 1], 1),
+}
+
+
+@pytest.mark.parametrize("case", list(TOPK_CASES))
+def test_topk_bit_exact_on_oracle_scores(case):
+    kind, ns, k = TOPK_CASES[case]
+    _say(f"[topk] {case} k={k} n={ns}")
+    rows = _topk_rows(kind, ns, 31)
+    T = len(rows)
+    ld = (max(ns) + 3) // 4 * 4
+    host = np.zeros((T, ld), np.float32)
+    for t, r in enumerate(rows):
+        host[t, : len(r)] = r
+    sc = torch.from_numpy(host).cuda()
+    b = dsa.Batch(torch.zeros(T, dtype=torch.int32, device="cuda"),
+                  torch.tensor([len(r) - 1 for r in rows], dtype=torch.int32, device="cuda"),
+                  torch.zeros(1, dtype=torch.int64, device="cuda"), max(ns))
+    idx = dsa.dsa_topk(b, sc, k).cpu().numpy()
+    for t, r in enumerate(rows):
+        assert np.array_equal(idx[t], O.topk_select(r, k)), f"row {t} (n={len(r)})"
+
+
+def test_topk_special_values():
+    """All-equal rows, signed zeros at the threshold, exact duplicates."""
+    n = 9000
+    rows = [np.zeros(n, np.float32),
+            np.where(np.arange(n) % 3 == 0, np.float32(-0.0), np.float32(0.0)).astype(np.float32),
+            np.repeat(np.arange(n // 9, dtype=np.float32), 9)[:n]]
+    r = np.random.default_rng(5).standard_normal(n).astype(np.float32)
+    r[4000:4100] = np.float32(-0.0)
+    r[r > 0] = -r[r > 0] - 1  # everything negative except the zeros
+    r[:3000] = 0.0
+    rows.append(r)
+    T = len(rows)
+    ld = (n + 3) // 4 * 4
+    host = np.zeros((T, ld), np.float32)
+    for t, x in enumerate(rows):
+        host[t, :n] = x
+    b = dsa.Batch(torch.zeros(T, dtype=torch.int32, device="cuda"),
+                  torch.full((T,), n - 1, dtype=torch.int32, device="cuda"),
+                  torch.zeros(1, dtype=torch.int64, device="cuda"), n)
+    for k in (1, 2048):
+        idx = dsa.dsa_topk(b, torch.from_numpy(host).cuda(), k).cpu().numpy()
+        for t, x in enumerate(rows):
+            assert np.array_equal(idx[t], O.topk_select(x, k)), f"row {t} k={k}"
+
+
+# ------------------------------------------------------------------ sparse MLA
+MLA_CASES = {
+    "tiny_ref_4k": None,
+    "decode_splits": ([3000, 2100, 5000], [(0, 2999), (1, 2099), (2, 100)]),   # T=3 -> key splits
+    "many_queries_no_split": ([2600], [(0, 2300 + i) for i in range(300)]),       # T=300 -> one split
+}
+
+
+@pytest.mark.parametrize("case", list(MLA_CASES))
+def test_sparse_mla_matches_oracle_given_oracle_indices(case):
+    _say(f"[sparse_mla] {case}")
+    if MLA_CASES[case] is None:
+        inp = synth.make_inputs(synth.workload(case))
+    else:
+        lens, qs = MLA_CASES[case]
+        inp = synth.custom(lens, qs, seed=41)
+    T = len(inp.q_pos)
+    sample = list(range(T)) if T <= 16 else [0, 1, T // 2, T - 1]
+    idx = np.full((T, 2048), -1, np.int32)
+    for t in range(T):
+        idx[t] = O.topk_select(_oracle_scores(inp, t), 2048)
+    d = to_device(inp)
+    out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv,
+                                  torch.from_numpy(idx).cuda(), out_dtype=torch.float32)
+    got = out.cpu().numpy()
+    for t in sample:
+        ref = _oracle_out(inp, t, idx[t])
+        mx, rel = out_errors(got[t], ref)
+        _say(f"  t={t} max-abs {mx:.2e} rel-L2 {rel:.2e}")
+        assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2
+
+
+def test_sparse_mla_absent_entries_and_order():
+    """-1 entries anywhere are skipped; the order of idx does not matter; a
+    query with no entry gets zeros; bf16 output equals rounded fp32 output."""
+    inp = synth.custom([700], [(0, 699), (0, 500), (0, 10)], seed=42)
+    rng = np.random.default_rng(0)
+    k = 96
+    idx = np.full((3, k), -1, np.int32)
+    sel0 = np.sort(rng.choice(700, 60, replace=False)).astype(np.int32)
+    idx[0, :60] = sel0
+    idx[1, :] = rng.permutation(np.concatenate([rng.choice(501, 50, replace=False),
+                                                np.full(k - 50, -1)])).astype(np.int32)
+    d = to_device(inp)
+    ti = torch.from_numpy(idx).cuda()
+    out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv, ti,
+                                  out_dtype=torch.float32).cpu().numpy()
+    for t in (0, 1):
+        mx, rel = out_errors(out[t], _oracle_out(inp, t, idx[t]))
+        assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2
+    assert np.all(out[2] == 0.0)
+    outb = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv, ti,
+                                   out_dtype=torch.bfloat16)
+    ref16 = torch.from_numpy(out).to(torch.bfloat16).float().numpy()
+    assert np.abs(outb.float().cpu().numpy() - ref16).max() <= 2 ** -7 * np.abs(out).max()
+
+
+# ------------------------------------------------------------------ end to end
+def _e2e(inp, sample, k=2048, ws=None, d=None):
+    d = d if d is not None else to_device(inp)
+    out, idx = run_forward(d, k=k, ws=ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    idx = idx.cpu().numpy()
+    worst_mx = worst_rel = 0.0
+    ndiff = 0
+    for t in sample:
+        s = _oracle_scores(inp, t)
+        oi = O.topk_select(s, k)
+        ndiff += check_selection(idx[t], s, oi, k)
+        ref = _oracle_out(inp, t, idx[t])
+        mx, rel = out_errors(out[t], ref)
+        worst_mx, worst_rel = max(worst_mx, mx), max(worst_rel, rel)
+    _say(f"  sampled {len(sample)}: near-tie selection diffs {ndiff}, out max-abs {worst_mx:.2e} rel-L2 {worst_rel:.2e}")
+    assert worst_mx <= OUT_MAX_ABS and worst_rel <= OUT_REL_L2
+    return out, idx
+
+
+def test_forward_tiny_ref_all_queries():
+    _say("[forward] tiny_ref_4k")
+    inp = synth.make_inputs(synth.workload("tiny_ref_4k"))
+    _e2e(inp, range(16))
+
+
+def test_forward_small_contexts_equal_dense_attention():
+    """Context <= k: every position is kept, so the path is dense causal MLA."""
+    inp = synth.custom([300, 40], [(0, 299), (1, 0), (1, 39), (0, 17)], seed=43)
+    out, idx = _e2e(inp, range(4))
+    for t, p in enumerate([299, 0, 39, 17]):
+        assert np.array_equal(idx[t, : p + 1], np.arange(p + 1)) and np.all(idx[t, p + 1:] == -1)
+
+
+def test_forward_chunking_is_invisible():
+    inp = synth.custom([4100], [(0, 4000 + 3 * i) for i in range(20)], seed=44)
+    d = to_device(inp)
+    out1, idx1 = run_forward(d)
+    small = torch.empty(dsa.dsa_workspace_bytes(dsa.OP_FORWARD, 3, d.batch.max_ctx, 2048),
+                        dtype=torch.uint8, device="cuda")
+    out2, idx2 = run_forward(d, ws=small)
+    # selections are identical; outputs may differ by the key-split count of the chunk size
+    assert torch.equal(idx1, idx2)
+    assert (out1 - out2).abs().max().item() <= 4e-3 * out1.abs().max().item()
+
+
+def test_forward_invariants():
+    """Deterministic; caches never written; scaling w by 4 changes nothing downstream."""
+    inp = synth.custom([6000, 3000], [(0, 5999), (1, 2999), (0, 4000)], seed=45)
+    d = to_device(inp)
+    ck = d.k_idx.clone()
+    ckv = d.kv.clone()
+    out1, idx1 = run_forward(d)
+    out2, idx2 = run_forward(d)
+    assert torch.equal(idx1, idx2) and torch.equal(out1, out2)
+    assert torch.equal(ck, d.k_idx) and torch.equal(ckv, d.kv)
+    w4 = synth.bf16_rne(synth.bf16_to_f32(inp.w) * 4)
+    d.w = bf16_dev(w4)
+    out3, idx3 = run_forward(d)
+    assert torch.equal(idx1, idx3) and torch.equal(out1, out3)
+
+
+def test_empty_batch_is_a_no_op():
+    z = torch.zeros(0, dtype=torch.int32, device="cuda")
+    b = dsa.Batch(z, z, torch.zeros(1, dtype=torch.int64, device="cuda"), 1)
+    e = torch.zeros((0, 32, 128), dtype=torch.bfloat16, device="cuda")
+    sc = dsa.dsa_index_scores(b, e, torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda"))
+    assert sc.shape[0] == 0
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+FULL = {
+    "decode_b32_ctx32k": [0, 31],
+    "decode_b8_ctx204k": [0, 5],
+    "prefill_chunk4096_ctx131k": [0, 2047, 4095],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_forward_full_size_sampled(name):
+    _say(f"[forward full] {name}: generating inputs")
+    inp = synth.make_inputs(synth.workload(name))
+    d = to_device(inp)
+    _say(f"  running; sampled queries {FULL[name]}")
+    _e2e(inp, FULL[name], d=d)
+    sc = dsa.dsa_index_scores(d.batch, d.q_idx, d.w, d.k_idx)
+    rows = sc[FULL[name]].cpu().numpy()
+    for i, t in enumerate(FULL[name]):
+        ref = _oracle_scores(inp, t)
+        err = float(np.abs(rows[i, : len(ref)].astype(np.float64) - ref).max())
+        _say(f"  t={t} max |score err| {err:.2e}")
+        assert err <= SCORE_MAX_ABS
