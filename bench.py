@@ -81,7 +81,7 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms
 
 
-def run_workload(name, steps, warmup):
+def run_workload(name, steps, warmup, with_ops=True):
     log(f"[bench] {name}: generating inputs")
     t0 = time.time()
     inp = synth.make_inputs(synth.workload(name))
@@ -100,6 +100,9 @@ def run_workload(name, steps, warmup):
     log(f"[bench] {name}: timing {steps} steps after {warmup} warmup")
     torch.cuda.synchronize()
     ms = time_calls(step, steps, warmup)
+    if not with_ops:
+        log(f"[bench] {name}: {ms:.3f} ms/step")
+        return inp, ms, {}
     # per-op breakdown: each ABI call below launches that op's kernels only
     scores = torch.empty((T, dsa.score_ld(batch.max_ctx)), dtype=torch.float32, device="cuda")
     mla_ws = torch.empty(max(dsa.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, T, batch.max_ctx, TOPK), 256),
@@ -142,6 +145,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="profiling aid: run only the prefill chunk (prints no result line)")
+    ap.add_argument("--no-ops", action="store_true", help="profiling aid: skip the per-op timing loops")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -152,6 +158,9 @@ def main():
         print("bench.py: no GPU", file=sys.stderr)
         sys.exit(2)
     dsa.lib()
+    if args.prefill_only:
+        run_workload(PREFILL, args.steps, args.warmup, not args.no_ops)
+        return
 
     inp, ms, ops = run_workload(DECODE, args.steps, args.warmup)
     alg = algorithmic(inp)

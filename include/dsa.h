@@ -117,7 +117,10 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const
  * position order, padded with -1.  Bit-exact: equal inputs give equal outputs.
  * NaN scores are unsupported (unspecified result).
  *   scores [T, ld_scores] fp32 (as above), 1 <= k <= DSA_MAX_TOPK, idx [T,k] int32.
- *   ws: workspace of dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes (may be NULL if 0).
+ *   ws: NULL, or at least dsa_workspace_bytes(DSA_OP_TOPK, T, max_ctx, k) bytes
+ *   (DSA_ERR_WORKSPACE otherwise).  Batches of few rows split each row over
+ *   many workgroups when a workspace is given; with NULL every row runs on one
+ *   workgroup.  Both give identical results.
  */
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);

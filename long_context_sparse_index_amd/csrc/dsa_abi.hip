@@ -85,7 +85,7 @@ bool use_gemm(const dsa_batch* b) {
 
 // Workspace of dsa_forward for a chunk of T queries.
 struct FwdPlan {
-  size_t scores_off, idx_off, mla_off, total;
+  size_t scores_off, idx_off, topk_off, mla_off, total;
   dsa::MlaPlan mla;
 };
 FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
@@ -94,6 +94,8 @@ FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
   size_t end = align256((size_t)T * score_ld(max_ctx) * sizeof(float));
   f.idx_off = end;
   if (need_idx) end += align256((size_t)T * k * sizeof(int32_t));
+  f.topk_off = end;
+  end += align256(dsa::topk_workspace_bytes(T, max_ctx));
   f.mla_off = end;
   f.mla = dsa::plan_mla(T, k);
   f.total = end + f.mla.total;
@@ -126,7 +128,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int
   if (num_queries < 0 || num_queries > kMaxQueries || max_ctx < 1 || max_ctx > kMaxCtx) return 0;
   switch (op) {
     case DSA_OP_INDEX_SCORES: return 0;
-    case DSA_OP_TOPK: return 0;
+    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(num_queries, max_ctx);
     case DSA_OP_SPARSE_MLA:
       if (k < 1 || k > DSA_MAX_TOPK) return 0;
       return dsa::plan_mla(num_queries, k).total;
@@ -155,18 +157,21 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   dsa_status s = check_batch(batch);
   if (s != DSA_OK) return s;
   if (batch->num_queries == 0) return DSA_OK;
   if ((s = check_scores(batch, scores, ld_scores)) != DSA_OK) return s;
   if (!idx) return DSA_ERR_NULL;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  if (ws != nullptr) {
+    if (!aligned16(ws)) return DSA_ERR_ALIGN;
+    if (ws_bytes < dsa::topk_workspace_bytes(batch->num_queries, batch->max_ctx))
+      return DSA_ERR_WORKSPACE;
+  }
   if ((s = check_device()) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_topk(to_launch(batch, 0, batch->num_queries), scores,
-                                        ld_scores, k, idx, (hipStream_t)stream));
+                                        ld_scores, k, idx, ws, (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
@@ -243,7 +248,7 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
     hipError_t e = dsa::launch_index_scores(lb, q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
                                             w + (int64_t)t0 * DSA_INDEX_HEADS, k_idx, scores, ld,
                                             gemm, st);
-    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, st);
+    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, base + p.topk_off, st);
     if (e == hipSuccess)
       e = dsa::launch_sparse_mla(lb, p.mla, q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM,
                                  q_rope + (int64_t)t0 * DSA_HEADS * DSA_QK_ROPE_DIM, kv, w_uk,

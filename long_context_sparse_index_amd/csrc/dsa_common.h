@@ -58,6 +58,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// max(x, 0) for fp32 in one integer instruction: negative values (and -0.0)
+// have negative int images, +0.0 is int 0.  (fmaxf costs a canonicalize plus
+// a max in IEEE mode.)  Inputs are finite.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Lane exchange within a wave (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int xor_lane(int v, int mask) { return __shfl_xor(v, mask, 64); }

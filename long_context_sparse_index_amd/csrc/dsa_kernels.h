@@ -20,9 +20,12 @@ hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, cons
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
                                hipStream_t st);
 
-// Top-k selection, one workgroup per query row.
+// Top-k selection.  Batches of few rows use a split path that needs
+// topk_workspace_bytes(T, max_ctx) of workspace; with ws == nullptr every row
+// runs on one workgroup (same result).
+size_t topk_workspace_bytes(int T, int max_ctx);
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       hipStream_t st);
+                       void* ws, hipStream_t st);
 
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {

@@ -15,25 +15,30 @@
 namespace dsa {
 
 // ---------------------------------------------------------------- decode scan
-// One workgroup = one query x kScanChunk keys.  Each wave streams
-// kScanTiles tiles of 32 keys (8 KB contiguous each); all of its loads are in
-// flight before the first MFMA.  Keys are read non-temporally: in decode they
-// are touched once per step.
-constexpr int kScanWaves = 4;
-constexpr int kScanTiles = 4;
-constexpr int kScanChunk = kScanWaves * kScanTiles * 32;
+// One workgroup = one query x kScanKeys keys, in tiles of 128 keys (32 KB).
+// A tile is read with fully coalesced 16-byte non-temporal loads (keys are
+// touched once per decode step) into LDS, double buffered; each of the 4 waves
+// then takes 32 keys of the tile as the MFMA B operand from LDS.  Reading the
+// MFMA layout straight from HBM (2 lanes per 256-byte key row per load) was
+// measured at about half the bandwidth of this coalesced form.
+constexpr int kScanKeys = 1024;
+constexpr int kScanTile = 128;
+constexpr int kScanLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 
-__global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(
+__global__ __launch_bounds__(256) void idx_scan_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
     float* __restrict__ scores, int64_t ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kScanTile * kScanLds];
   const int t = blockIdx.x;
   const int pos = q_pos[t];
-  const int chunk0 = blockIdx.y * kScanChunk;
-  if (chunk0 > pos) return;
+  const int k0 = blockIdx.y * kScanKeys;
+  if (k0 > pos) return;
+  const int kend = min(k0 + kScanKeys, pos + 1);
+  const int ntiles = (kend - k0 + kScanTile - 1) / kScanTile;
   const int64_t row0 = seq_row0[q_seq[t]];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
 
   // A operand: head n of query t, K-group g (dims 16j + 8g .. +8 at step j).
@@ -46,44 +51,60 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) wr[r] = bf16_to_f32(w[t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)]);
 
-  const int wbase = chunk0 + wave * kScanTiles * 32;
-  u32x4 kb[kScanTiles][8];
+  u32x4 st[8];
+  auto gload = [&](int tile) {
 #pragma unroll
-  for (int it = 0; it < kScanTiles; ++it) {
-    const int s = min(wbase + it * 32 + n, pos);  // clamp: rows past pos are never used
-    const uint16_t* kp = k_idx + (row0 + s) * kIdxDim + 8 * g;
+    for (int c = 0; c < 8; ++c) {
+      const int lin = tid + 256 * c;  // 16-byte chunk of the 32 KB tile
+      const int key = min(k0 + tile * kScanTile + (lin >> 4), pos);  // rows past pos: never used
+      st[c] = ld16_nt(k_idx + (row0 + key) * kIdxDim + (lin & 15) * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kb[it][j] = ld16_nt(kp + 16 * j);
-  }
+    for (int c = 0; c < 8; ++c) {
+      const int lin = tid + 256 * c;
+      st16(&ks[buf][(lin >> 4) * kScanLds + (lin & 15) * 8], st[c]);
+    }
+  };
   float* srow = scores + (int64_t)t * ld;
-#pragma unroll
-  for (int it = 0; it < kScanTiles; ++it) {
-    if (wbase + it * 32 > pos) break;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < ntiles) gload(tile + 1);
+    const uint16_t* bp = &ks[buf][(wave * 32 + n) * kScanLds + 8 * g];
     f32x16 acc = {};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = mfma32(qa[j], as_bf16x8(kb[it][j]), acc);
+    for (int j = 0; j < 8; ++j)
+      acc = mfma32(qa[j], as_bf16x8(*reinterpret_cast<const u32x4*>(bp + 16 * j)), acc);
     float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(wr[r], fmaxf(acc[r], 0.f), part);
+    for (int r = 0; r < 16; ++r) part = fmaf(wr[r], relu(acc[r]), part);
     const float tot = part + xor_lane(part, 32);
-    const int s = wbase + it * 32 + n;
+    const int s = k0 + tile * kScanTile + wave * 32 + n;
     if (g == 0 && s <= pos) srow[s] = tot;
+    if (tile + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- prefill GEMM
-// One workgroup = kGemmQB consecutive queries x kGemmSplit keys.  Each wave
-// keeps kGemmQPW queries (32 heads each) as resident A operands; key tiles of
-// kGemmKT keys are staged through LDS (double buffered) and shared by the four
-// waves.  Queries of one block normally share a sequence; a block that mixes
+// One workgroup = kGemmQB consecutive queries x kGemmSplit keys.  Each of the
+// 8 waves keeps kGemmQPW queries (32 heads each) as resident A operands; key
+// tiles of kGemmKT keys are staged through LDS (double buffered) and shared by
+// the eight waves.  Queries of one block normally share a sequence; a block that mixes
 // sequences is processed once per distinct sequence.
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kGemmQPW = 2;
-constexpr int kGemmQB = 4 * kGemmQPW;
+constexpr int kGemmQB = kGemmWaves * kGemmQPW;
 constexpr int kGemmKT = 64;
 constexpr int kGemmSplit = 8192;
 constexpr int kKeyLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 
-__global__ __launch_bounds__(256) void idx_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
@@ -133,20 +154,21 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(
     const int64_t row0 = seq_row0[sq];
     const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
 
-    // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 4 per thread.
-    u32x4 stage[4];
+    // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 2 per thread.
+    constexpr int kPer = kGemmKT * 16 / kGemmThreads;
+    u32x4 stage[kPer];
     auto gload = [&](int tile) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int lin = tid + 256 * c;
+      for (int c = 0; c < kPer; ++c) {
+        const int lin = tid + kGemmThreads * c;
         const int key = min(kbeg + tile * kGemmKT + (lin >> 4), hi);
         stage[c] = ld16(k_idx + (row0 + key) * kIdxDim + (lin & 15) * 8);
       }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int lin = tid + 256 * c;
+      for (int c = 0; c < kPer; ++c) {
+        const int lin = tid + kGemmThreads * c;
         st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
       }
     };
@@ -177,7 +199,7 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(
           for (int j = 0; j < 8; ++j) acc = mfma32(qa[qi][j], bfr[nt][j], acc);
           float part = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], fmaxf(acc[r], 0.f), part);
+          for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], relu(acc[r]), part);
           const float tot = part + xor_lane(part, 32);
           const int s = sbase + nt * 32 + n;
           if (g == 0 && s <= pos) srow[s] = tot;
@@ -195,12 +217,12 @@ hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, cons
                                hipStream_t st) {
   if (gemm) {
     dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (b.max_ctx + kGemmSplit - 1) / kGemmSplit);
-    idx_gemm_kernel<<<grid, 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx, scores,
-                                          ld, b.T);
+    idx_gemm_kernel<<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx,
+                                                   scores, ld, b.T);
   } else {
-    dim3 grid(b.T, (b.max_ctx + kScanChunk - 1) / kScanChunk);
-    idx_scan_kernel<<<grid, kScanWaves * 64, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w,
-                                                      k_idx, scores, ld);
+    dim3 grid(b.T, (b.max_ctx + kScanKeys - 1) / kScanKeys);
+    idx_scan_kernel<<<grid, 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx, scores,
+                                          ld);
   }
   return hipGetLastError();
 }

@@ -18,58 +18,85 @@
 namespace dsa {
 
 // ---------------------------------------------------------------- absorb
-// grid (64 heads, 4 blocks of 128 latent columns, ceil(T/32)); wave w owns 32
-// latent columns.  A = q_nope rows (queries), B[k=d][n=c] = W_UK[h][c][d]:
-// both operands are contiguous 16-byte loads.
+// grid (64 heads, 4 blocks of 128 latent columns, query groups); wave w owns
+// 32 latent columns and keeps their W_UK fragments resident (B[k=d][n=c] =
+// W_UK[h][c][d], contiguous 16-byte loads), then walks 32-query tiles (A =
+// q_nope rows).
+constexpr int kAbsorbTilesPerWg = 8;
+
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ w_uk,
                                                      uint16_t* __restrict__ q_lat, int T) {
-  const int h = blockIdx.x, cb = blockIdx.y, tb = blockIdx.z;
+  const int h = blockIdx.x, cb = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int t = min(tb * 32 + n, T - 1);
   const int c = cb * 128 + wave * 32 + n;
-  const uint16_t* ap = q_nope + ((int64_t)t * kHeads + h) * kNope + 8 * g;
+  bf16x8 bw[kNope / 16];
   const uint16_t* bp = w_uk + ((int64_t)h * kLat + c) * kNope + 8 * g;
-  f32x16 acc = {};
 #pragma unroll
-  for (int j = 0; j < kNope / 16; ++j)
-    acc = mfma32(as_bf16x8(ld16(ap + 16 * j)), as_bf16x8(ld16(bp + 16 * j)), acc);
+  for (int j = 0; j < kNope / 16; ++j) bw[j] = as_bf16x8(ld16(bp + 16 * j));
+  const int ntb = (T + 31) / 32;
+  for (int tb = blockIdx.z * kAbsorbTilesPerWg; tb < min(ntb, (int)(blockIdx.z + 1) * kAbsorbTilesPerWg);
+       ++tb) {
+    const int t = min(tb * 32 + n, T - 1);
+    const uint16_t* ap = q_nope + ((int64_t)t * kHeads + h) * kNope + 8 * g;
+    bf16x8 a[kNope / 16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tr = tb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (tr < T) q_lat[((int64_t)tr * kHeads + h) * kLat + c] = (uint16_t)f32_to_bf16_bits(acc[r]);
+    for (int j = 0; j < kNope / 16; ++j) a[j] = as_bf16x8(ld16(ap + 16 * j));
+    f32x16 acc = {};
+#pragma unroll
+    for (int j = 0; j < kNope / 16; ++j) acc = mfma32(a[j], bw[j], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = tb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tr < T) q_lat[((int64_t)tr * kHeads + h) * kLat + c] = (uint16_t)f32_to_bf16_bits(acc[r]);
+    }
   }
 }
 
 // ---------------------------------------------------------------- core
-// grid (T, splits); 4 waves, wave w owns heads 16w..16w+15 (16x16x32 MFMAs).
-// Tiles of 32 gathered rows are staged in LDS (double buffered).
-//   QK:  logits^T[key][head] = c_tile[key][576] . q[head][576]^T  (A from LDS, B resident)
-//   PV:  o^T[dim][head] += c_tile^T[dim][key] . P^T[key][head]
-// The PV K order (keys) follows the QK accumulator layout, so P feeds the MFMA
-// straight from registers; the transposed latent operand is read from LDS as
-// 4 consecutive dims x 8 keys and repacked with v_perm.
+// grid (T, key splits); 8 waves.  Tiles of 32 gathered rows are staged in LDS
+// (double buffered).  Per tile:
+//   QK   wave (hg, hf) computes logits^T[16 keys of half hf][16 heads of group
+//        hg] = c_tile . q^T with the group's q (576 = 512 latent + 64 rope)
+//        resident as the B operand of 16x16x32 MFMAs;
+//   softmax  both halves' maxima meet in LDS; the reference max of a head only
+//        moves when a tile exceeds it by 2^8 (so P <= 256 and the running
+//        output is rescaled rarely); P^T goes to LDS as bf16;
+//   PV   wave w accumulates o^T[64 latent dims of slice w][64 heads] =
+//        c_tile^T . P^T; the latent operand is read transposed from LDS as
+//        4 consecutive dims x 8 keys and repacked with v_perm.
 constexpr int kKT = 32;
 constexpr int kKvLds = kRow + 8;  // 584 bf16 = 1168 B per LDS row
-constexpr int kGatherPerThread = kKT * (kRow / 8) / 256;  // 9 chunks of 16 B
+constexpr int kCoreThreads = 512;
+constexpr int kGatherChunks = kKT * (kRow / 8);  // 16-byte chunks per tile
+constexpr int kGatherPerThread = (kGatherChunks + kCoreThreads - 1) / kCoreThreads;
+constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
 
-__global__ __launch_bounds__(256) void mla_core_kernel(
+__global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ seq_row0,
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int k, float scale_log2,
     int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
     float* __restrict__ ml_part) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKT * kKvLds];
+  __shared__ __attribute__((aligned(16))) uint16_t pT[kHeads * kPLds];
+  __shared__ float s_max[2][kHeads];
+  __shared__ float s_alpha[kHeads];
+  __shared__ float s_l[2][kHeads];
+  __shared__ float s_m[kHeads];
   __shared__ int s_valid[2][kKT];
+  __shared__ int s_idx[kMaxTopk];
   const int t = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int hg = wave & 3, hf = wave >> 2;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
   const int64_t row0 = seq_row0[q_seq[t]];
   const int32_t* irow = idx + (int64_t)t * k;
-  const int hq = wave * 16 + l16;
+  const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
 
   bf16x8 qb[18];
   {
@@ -81,35 +108,43 @@ __global__ __launch_bounds__(256) void mla_core_kernel(
     qb[17] = as_bf16x8(ld16(qr + 32));
   }
 
-  f32x4 o[32];
+  // o[e][j]: latent dim 64*wave + 16g + 4jj + e, head 16j + l16 (element jj)
+  f32x4 o[4][4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -1e30f, l_run = 0.f;
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[e][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -1e30f, l_part = 0.f;
 
   const int ntiles = j1 > j0 ? (j1 - j0 + kKT - 1) / kKT : 0;
+  // The split's positions go to LDS first, so that no row gather waits on a
+  // dependent global load of its index.
+  for (int j = j0 + tid; j < j1; j += kCoreThreads) s_idx[j - j0] = irow[j];
+  __syncthreads();
   u32x4 stage[kGatherPerThread];
   auto gload = [&](int tt) {
 #pragma unroll
     for (int c = 0; c < kGatherPerThread; ++c) {
-      const int lin = tid + 256 * c;
+      const int lin = tid + kCoreThreads * c;
       const int key = lin / (kRow / 8);
       const int col = lin - key * (kRow / 8);
-      const int j = j0 + tt * kKT + key;
-      const int s = j < j1 ? irow[j] : -1;
+      const int jl = tt * kKT + key;
+      const int s = (lin < kGatherChunks && j0 + jl < j1) ? s_idx[jl] : -1;
       stage[c] = s >= 0 ? ld16(kv + (row0 + s) * kRow + col * 8) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto lstore = [&](int buf, int tt) {
 #pragma unroll
     for (int c = 0; c < kGatherPerThread; ++c) {
-      const int lin = tid + 256 * c;
+      const int lin = tid + kCoreThreads * c;
+      if (lin >= kGatherChunks) break;
       const int key = lin / (kRow / 8);
       const int col = lin - key * (kRow / 8);
       st16(&tile[buf][key * kKvLds + col * 8], stage[c]);
     }
     if (tid < kKT) {
-      const int j = j0 + tt * kKT + tid;
-      s_valid[buf][tid] = (j < j1) && irow[j] >= 0;
+      const int jl = tt * kKT + tid;
+      s_valid[buf][tid] = (j0 + jl < j1) && s_idx[jl] >= 0;
     }
   };
 
@@ -122,53 +157,65 @@ __global__ __launch_bounds__(256) void mla_core_kernel(
     const int buf = tt & 1;
     if (tt + 1 < ntiles) gload(tt + 1);
     const uint16_t* tb = tile[buf];
-    // ---- QK for the two 16-key halves
-    f32x4 sc[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- QK: keys hf*16 + 4g + jj of head hq
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    {
       const uint16_t* ap = tb + (hf * 16 + l16) * kKvLds + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks)
-        sc[hf] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 32 * ks)), qb[ks], sc[hf]);
+        sc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 32 * ks)), qb[ks], sc);
     }
-    // ---- online softmax (base 2); lane holds keys hf*16 + 4g + jj of head hq
-    float z[8];
+    float z[4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float v = s_valid[buf][hf * 16 + 4 * g + jj] ? sc[hf][jj] * scale_log2 : -INFINITY;
-        z[hf * 4 + jj] = v;
-        tmax = fmaxf(tmax, v);
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      const float v = s_valid[buf][hf * 16 + 4 * g + jj] ? sc[jj] * scale_log2 : -INFINITY;
+      z[jj] = v;
+      tmax = fmaxf(tmax, v);
+    }
     tmax = fmaxf(tmax, xor_lane(tmax, 16));
     tmax = fmaxf(tmax, xor_lane(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float p[8];
-    float psum = 0.f;
+    if (g == 0) s_max[hf][hq] = tmax;
+    __syncthreads();
+    const float tile_max = fmaxf(s_max[0][hq], s_max[1][hq]);
+    const float m_new = tile_max > m_ref + kRescaleLog2 ? tile_max : m_ref;
+    const float alpha = exp2f(m_ref - m_new);
+    m_ref = m_new;
+    float p[4];
+    float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(z[i] - m_new);
-      psum += p[i];
+    for (int jj = 0; jj < 4; ++jj) {
+      p[jj] = exp2f(z[jj] - m_new);
+      ps += p[jj];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_part = l_part * alpha + ps;
+    *reinterpret_cast<u32x2*>(&pT[hq * kPLds + hf * 16 + 4 * g]) =
+        u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    if (hf == 0 && g == 0) s_alpha[hq] = alpha;
+    __syncthreads();
+    // ---- PV
+    {
+      float al[4];
+      bool need = false;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] *= alpha;
-    const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-    // ---- PV: K element i of K-group g is key (i<4 ? 4g+i : 16+4g+i-4)
+      for (int j = 0; j < 4; ++j) {
+        al[j] = s_alpha[16 * j + l16];
+        need |= al[j] != 1.f;
+      }
+      if (__any(need)) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[e][j] *= al[j];
+      }
       u32x2 v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = (i < 4) ? 4 * g + i : 16 + 4 * g + (i - 4);
-        v[i] = *reinterpret_cast<const u32x2*>(tb + key * kKvLds + 64 * a + 4 * l16);
-      }
+      for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const u32x2*>(tb + (8 * g + i) * kKvLds + 64 * wave + 4 * l16);
+      bf16x8 pb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pb[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pT[(16 * j + l16) * kPLds + 8 * g]));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -179,41 +226,46 @@ __global__ __launch_bounds__(256) void mla_core_kernel(
           const uint32_t x1 = (e < 2) ? v[2 * d + 1].x : v[2 * d + 1].y;
           f[d] = __builtin_amdgcn_perm(x1, x0, sel);
         }
-        o[4 * a + e] = mfma16(as_bf16x8(f), pb, o[4 * a + e]);
+        const bf16x8 fa = as_bf16x8(f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[e][j] = mfma16(fa, pb[j], o[e][j]);
       }
     }
     if (tt + 1 < ntiles) lstore(buf ^ 1, tt + 1);
     __syncthreads();
   }
 
-  // ---- finish: the four K-groups of a head share m_run; sum their l.
-  float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += xor_lane(l_tot, 32);
-  // o[4a+e][jj] is dim 64a + 16g + 4jj + e of head hq.
-  if (S == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* dst = o_lat + ((int64_t)t * kHeads + hq) * kLat;
+  // ---- finish: l of a head = its lanes' partial sums over both key halves
+  float l_sum = l_part + xor_lane(l_part, 16);
+  l_sum += xor_lane(l_sum, 32);
+  if (g == 0) {
+    s_l[hf][hq] = l_sum;
+    if (hf == 0) s_m[hq] = m_ref;
+  }
+  __syncthreads();
+  const int dim0 = 64 * wave + 16 * g;
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+  for (int j = 0; j < 4; ++j) {
+    const int h = 16 * j + l16;
+    const float L = s_l[0][h] + s_l[1][h];
+    if (S == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* dst = o_lat + ((int64_t)t * kHeads + h) * kLat + dim0;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const u32x2 v = {pack_bf16x2(o[4 * a][jj] * inv, o[4 * a + 1][jj] * inv),
-                         pack_bf16x2(o[4 * a + 2][jj] * inv, o[4 * a + 3][jj] * inv)};
-        *reinterpret_cast<u32x2*>(dst + 64 * a + 16 * g + 4 * jj) = v;
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<u32x2*>(dst + 4 * jj) =
+            u32x2{pack_bf16x2(o[0][j][jj] * inv, o[1][j][jj] * inv),
+                  pack_bf16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
+    } else {
+      const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
+      float* dst = o_part + base * kLat + dim0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4*>(dst + 4 * jj) = f32x4{o[0][j][jj], o[1][j][jj], o[2][j][jj], o[3][j][jj]};
+      if (wave == 0 && g == 0) {
+        ml_part[base * 2] = s_m[h];
+        ml_part[base * 2 + 1] = L;
       }
-  } else {
-    const int64_t base = ((int64_t)t * S + sp) * kHeads + hq;
-    float* dst = o_part + base * kLat;
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 v = {o[4 * a][jj], o[4 * a + 1][jj], o[4 * a + 2][jj], o[4 * a + 3][jj]};
-        *reinterpret_cast<f32x4*>(dst + 64 * a + 16 * g + 4 * jj) = v;
-      }
-    if (g == 0) {
-      ml_part[base * 2] = m_run;
-      ml_part[base * 2 + 1] = l_tot;
     }
   }
 }
@@ -225,8 +277,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict_
                                                         uint16_t* __restrict__ o_lat) {
   const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   float mstar = -1e30f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml_part[(((int64_t)t * S + s) * kHeads + h) * 2]);
   float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const int64_t base = ((int64_t)t * S + s) * kHeads + h;
     const float wgt = exp2f(ml_part[base * 2] - mstar);
@@ -246,7 +300,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict_
 // (8 consecutive c for one e) is one 16-byte LDS read.  Waves: (N-tile of 32
 // dims) x (half of the 512-long K); the two K halves are summed through LDS.
 constexpr int kUpEB = 64;
-constexpr int kUpMT = 4;
+constexpr int kUpMT = 16;  // 32-query tiles per workgroup
 constexpr int kWvLds = kLat + 8;
 
 __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict__ o_lat,
@@ -349,11 +403,13 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   float* o_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.part_off) : nullptr;
   float* ml_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
   const int T = b.T;
-  absorb_kernel<<<dim3(kHeads, kLat / 128, (T + 31) / 32), 256, 0, st>>>(q_nope, w_uk, q_lat, T);
+  const int ntb = (T + 31) / 32;
+  absorb_kernel<<<dim3(kHeads, kLat / 128, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 256, 0,
+                  st>>>(q_nope, w_uk, q_lat, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.4426950408889634f;
-  mla_core_kernel<<<dim3(T, p.splits), 256, 0, st>>>(b.q_seq, b.seq_row0, q_lat, q_rope, kv, idx,
+  mla_core_kernel<<<dim3(T, p.splits), kCoreThreads, 0, st>>>(b.q_seq, b.seq_row0, q_lat, q_rope, kv, idx,
                                                      p.k, scale_log2, p.keys_per_split, p.splits,
                                                      o_lat, o_part, ml_part);
   e = hipGetLastError();

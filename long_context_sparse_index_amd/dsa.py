@@ -22,6 +22,7 @@ MAX_TOPK = 2048
 DEFAULT_SCALE = 1.0 / 16.0
 
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
+NO_WORKSPACE = "no-workspace"  # dsa_topk(ws=NO_WORKSPACE): pass NULL (one workgroup per row)
 OUT_BF16, OUT_F32 = 0, 1
 
 
@@ -153,15 +154,20 @@ def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tenso
 
 
 def dsa_topk(batch: Batch, scores: torch.Tensor, k: int = MAX_TOPK,
-             idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+             idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Top-k positions [T, k] int32, ascending, -1 padded."""
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores: expected a row-major 2-D fp32 tensor")
     if idx is None:
         idx = torch.empty((batch.T, k), dtype=torch.int32, device=scores.device)
+    if isinstance(ws, str) and ws == NO_WORKSPACE:
+        ws = None
+    elif ws is None:
+        need = dsa_workspace_bytes(OP_TOPK, batch.T, batch.max_ctx, k)
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device) if need else None
     cb = batch.c()
     _check("dsa_topk", lib().dsa_topk(ctypes.byref(cb), _ptr(scores), scores.stride(0), k, _ptr(idx),
-                                      None, 0, _stream()))
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return idx
 
 

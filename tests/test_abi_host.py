@@ -103,7 +103,8 @@ def test_forward_validation(L):
 
 def test_workspace_bytes(L):
     assert L.dsa_workspace_bytes(dsa.OP_INDEX_SCORES, 8, 1000, 2048) == 0
-    assert L.dsa_workspace_bytes(dsa.OP_TOPK, 8, 1000, 2048) == 0
+    assert L.dsa_workspace_bytes(dsa.OP_TOPK, 8, 1000, 2048) > 0        # few rows: split path
+    assert L.dsa_workspace_bytes(dsa.OP_TOPK, 4096, 1000, 2048) == 0     # many rows: one workgroup each
     assert L.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, 8, 1000, 0) == 0        # invalid k
     assert L.dsa_workspace_bytes(99, 8, 1000, 16) == 0
     # decode (8 queries): q_lat + o_lat (64 KB each per query) + split partials

@@ -90,10 +90,11 @@ TOPK_CASES = {
 }
 
 
+@pytest.mark.parametrize("path", ["split", "row"])
 @pytest.mark.parametrize("case", list(TOPK_CASES))
-def test_topk_bit_exact_on_oracle_scores(case):
+def test_topk_bit_exact_on_oracle_scores(case, path):
     kind, ns, k = TOPK_CASES[case]
-    _say(f"[topk] {case} k={k} n={ns}")
+    _say(f"[topk] {case} ({path}) k={k} n={ns}")
     rows = _topk_rows(kind, ns, 31)
     T = len(rows)
     ld = (max(ns) + 3) // 4 * 4
@@ -104,7 +105,8 @@ def test_topk_bit_exact_on_oracle_scores(case):
     b = dsa.Batch(torch.zeros(T, dtype=torch.int32, device="cuda"),
                   torch.tensor([len(r) - 1 for r in rows], dtype=torch.int32, device="cuda"),
                   torch.zeros(1, dtype=torch.int64, device="cuda"), max(ns))
-    idx = dsa.dsa_topk(b, sc, k).cpu().numpy()
+    ws = dsa.NO_WORKSPACE if path == "row" else None
+    idx = dsa.dsa_topk(b, sc, k, ws=ws).cpu().numpy()
     for t, r in enumerate(rows):
         assert np.array_equal(idx[t], O.topk_select(r, k)), f"row {t} (n={len(r)})"
 
@@ -129,9 +131,10 @@ def test_topk_special_values():
                   torch.full((T,), n - 1, dtype=torch.int32, device="cuda"),
                   torch.zeros(1, dtype=torch.int64, device="cuda"), n)
     for k in (1, 2048):
-        idx = dsa.dsa_topk(b, torch.from_numpy(host).cuda(), k).cpu().numpy()
-        for t, x in enumerate(rows):
-            assert np.array_equal(idx[t], O.topk_select(x, k)), f"row {t} k={k}"
+        for ws in (None, dsa.NO_WORKSPACE):
+            idx = dsa.dsa_topk(b, torch.from_numpy(host).cuda(), k, ws=ws).cpu().numpy()
+            for t, x in enumerate(rows):
+                assert np.array_equal(idx[t], O.topk_select(x, k)), f"row {t} k={k} ws={ws}"
 
 
 # ------------------------------------------------------------------ sparse MLA
