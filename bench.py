@@ -148,6 +148,11 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill chunk (prints no result line)")
     ap.add_argument("--no-ops", action="store_true", help="profiling aid: skip the per-op timing loops")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="profiling aid: run only the decode workload (prints no result line)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="profiling aid: run a plain 1 GiB device-to-device copy 3 times and exit "
+                         "(reference for HBM byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -157,7 +162,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 1 GiB 3 times")
+        return
     dsa.lib()
+    if args.decode_only:
+        run_workload(DECODE, args.steps, args.warmup, not args.no_ops)
+        return
     if args.prefill_only:
         run_workload(PREFILL, args.steps, args.warmup, not args.no_ops)
         return

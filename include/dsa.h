@@ -86,7 +86,7 @@ enum { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_F
 typedef struct dsa_batch {
   int32_t num_queries;       /* T >= 0 */
   int32_t num_seqs;          /* B >= 1 */
-  int32_t max_ctx;           /* >= max_t(q_pos[t]) + 1, >= 1: bounds grids and score rows */
+  int32_t max_ctx;           /* >= max_t(q_pos[t]) + 1, 1 .. 2^21: bounds grids and score rows */
   int32_t reserved;          /* must be 0 */
   const int32_t* q_seq;      /* [T] device: sequence of each query */
   const int32_t* q_pos;      /* [T] device: position of each query (inclusive causal limit) */

@@ -17,7 +17,7 @@ std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 // Upper bounds that keep every grid dimension and 32-bit index in range.
 constexpr int32_t kMaxQueries = 1 << 21;
-constexpr int32_t kMaxCtx = 1 << 24;
+constexpr int32_t kMaxCtx = 1 << 21;  // 2,097,152 positions; row offsets fit 32 bits
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

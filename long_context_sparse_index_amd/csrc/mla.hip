@@ -12,6 +12,8 @@
 //            o_lat[t,h] = sum_j p_j c_j                       (split over keys)
 //   merge    combine key splits (log-sum-exp)                 (bf16 out)
 //   upproj   out[t,h] = o_lat[t,h] W_UV[h]
+#include <type_traits>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -55,8 +57,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- core
-// grid (T, key splits); 8 waves.  Tiles of 32 gathered rows are staged in LDS
-// (double buffered).  Per tile:
+// grid (T, key splits); 8 waves.  Tiles of 32 gathered rows land in a
+// 3-deep LDS ring through direct-to-LDS loads (two tiles in flight while one
+// is computed).  Per tile:
 //   QK   wave (hg, hf) computes logits^T[16 keys of half hf][16 heads of group
 //        hg] = c_tile . q^T with the group's q (576 = 512 latent + 64 rope)
 //        resident as the B operand of 16x16x32 MFMAs;
@@ -66,13 +69,29 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 //   PV   wave w accumulates o^T[64 latent dims of slice w][64 heads] =
 //        c_tile^T . P^T; the latent operand is read transposed from LDS as
 //        4 consecutive dims x 8 keys and repacked with v_perm.
+// LDS tile layout: row r (one gathered key) = 72 slots of 16 bytes; logical
+// slot c of row r sits at r*72 + ((c & ~7) | ((c ^ r) & 7)), which keeps the
+// row reads of QK and the column reads of PV free of bank conflicts.
 constexpr int kKT = 32;
-constexpr int kKvLds = kRow + 8;  // 584 bf16 = 1168 B per LDS row
+constexpr int kSlots = kRow / 8;                  // 72 slots of 16 B per row
+constexpr int kTileSlots = kKT * kSlots;          // 2304
 constexpr int kCoreThreads = 512;
-constexpr int kGatherChunks = kKT * (kRow / 8);  // 16-byte chunks per tile
-constexpr int kGatherPerThread = (kGatherChunks + kCoreThreads - 1) / kCoreThreads;
+constexpr int kRing = 3;
 constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
+
+__device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) (n < 16), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const int32_t* __restrict__ q_seq, const int64_t* __restrict__ seq_row0,
@@ -80,13 +99,17 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int k, float scale_log2,
     int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
     float* __restrict__ ml_part) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][kKT * kKvLds];
+  // Three distinct arrays (not one indexed array): the compiler then waits
+  // only for the direct-to-LDS loads that target the array being read.
+  __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileSlots * 8];
   __shared__ __attribute__((aligned(16))) uint16_t pT[kHeads * kPLds];
   __shared__ float s_max[2][kHeads];
   __shared__ float s_alpha[kHeads];
   __shared__ float s_l[2][kHeads];
   __shared__ float s_m[kHeads];
-  __shared__ int s_valid[2][kKT];
+  __shared__ int s_valid[kRing][kKT];
   __shared__ int s_idx[kMaxTopk];
   const int t = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,7 +117,8 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   const int hg = wave & 3, hf = wave >> 2;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
-  const int64_t row0 = seq_row0[q_seq[t]];
+  // rows of this query's sequence; positions < 2^21, so 32-bit offsets suffice
+  const uint16_t* const kv_seq = kv + seq_row0[q_seq[t]] * kRow;
   const int32_t* irow = idx + (int64_t)t * k;
   const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
 
@@ -120,50 +144,55 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // The split's positions go to LDS first, so that no row gather waits on a
   // dependent global load of its index.
   for (int j = j0 + tid; j < j1; j += kCoreThreads) s_idx[j - j0] = irow[j];
+  __builtin_amdgcn_s_waitcnt(0);  // q and the index list are in place before any gather
   __syncthreads();
-  u32x4 stage[kGatherPerThread];
-  auto gload = [&](int tt) {
+
+  // Gather of tile tt into ring slot buf: wave instruction i covers the 64
+  // physical slots [(8i + w) * 64, +64).  2304 slots = 4.5 instructions per
+  // wave; every wave issues exactly 5 (waves 4-7 repeat the last chunk of
+  // waves 0-3: same source, same destination) so that the number of
+  // outstanding loads per tile is the same constant for every wave.
+  auto gather = [&](int tt, uint16_t* dstt, int buf) {
 #pragma unroll
-    for (int c = 0; c < kGatherPerThread; ++c) {
-      const int lin = tid + kCoreThreads * c;
-      const int key = lin / (kRow / 8);
-      const int col = lin - key * (kRow / 8);
-      const int jl = tt * kKT + key;
-      const int s = (lin < kGatherChunks && j0 + jl < j1) ? s_idx[jl] : -1;
-      stage[c] = s >= 0 ? ld16(kv + (row0 + s) * kRow + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&](int buf, int tt) {
-#pragma unroll
-    for (int c = 0; c < kGatherPerThread; ++c) {
-      const int lin = tid + kCoreThreads * c;
-      if (lin >= kGatherChunks) break;
-      const int key = lin / (kRow / 8);
-      const int col = lin - key * (kRow / 8);
-      st16(&tile[buf][key * kKvLds + col * 8], stage[c]);
+    for (int i = 0; i < 5; ++i) {
+      const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
+      // The DMA writes lane L of the instruction to physical slot base + L; that
+      // slot holds logical column (pc & ~7) | ((pc ^ row) & 7) of its row (the
+      // swizzle is an involution within groups of 8), so fetch that chunk.
+      const int lin = blk * 64 + lane;  // physical slot, < 2304
+      const int r = lin / kSlots, pc = lin - r * kSlots;
+      const int lc = (pc & ~7) | ((pc ^ r) & 7);
+      const int jl = tt * kKT + r;
+      const int sidx = (j0 + jl < j1) ? s_idx[jl] : -1;
+      // absent keys (and tiles past the end) fetch row 0 of the sequence: finite data, masked later
+      const uint32_t off = (uint32_t)(sidx >= 0 ? sidx : 0) * (uint32_t)kRow + (uint32_t)lc * 8u;
+      __builtin_amdgcn_global_load_lds(kv_seq + off, dstt + blk * 64 * 8, 16, 0, 0);
     }
     if (tid < kKT) {
       const int jl = tt * kKT + tid;
       s_valid[buf][tid] = (j0 + jl < j1) && s_idx[jl] >= 0;
     }
   };
+  // Every step issues the gather of the tile three ahead, past the end too, so
+  // that exactly two tiles (10 loads per wave) are in flight at each wait.
+  gather(0, tile0, 0);
+  gather(1, tile1, 1);
+  gather(2, tile2, 2);
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0, 0);
-  }
-  __syncthreads();
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int buf = tt & 1;
-    if (tt + 1 < ntiles) gload(tt + 1);
-    const uint16_t* tb = tile[buf];
+  auto step = [&](int tt, auto BUFC) {
+    constexpr int buf = decltype(BUFC)::value;
+    uint16_t* const tbw = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
+    wait_vm<10>();
+    lds_barrier();
+    if (tt < ntiles) {
+    const uint16_t* tb = tbw;
     // ---- QK: keys hf*16 + 4g + jj of head hq
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     {
-      const uint16_t* ap = tb + (hf * 16 + l16) * kKvLds + 8 * g;
+      const int r = hf * 16 + l16;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks)
-        sc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 32 * ks)), qb[ks], sc);
+        sc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(tb + swz(r, 4 * ks + g) * 8)), qb[ks], sc);
     }
     float z[4];
     float tmax = -INFINITY;
@@ -176,7 +205,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     tmax = fmaxf(tmax, xor_lane(tmax, 16));
     tmax = fmaxf(tmax, xor_lane(tmax, 32));
     if (g == 0) s_max[hf][hq] = tmax;
-    __syncthreads();
+    lds_barrier();
     const float tile_max = fmaxf(s_max[0][hq], s_max[1][hq]);
     const float m_new = tile_max > m_ref + kRescaleLog2 ? tile_max : m_ref;
     const float alpha = exp2f(m_ref - m_new);
@@ -192,7 +221,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     *reinterpret_cast<u32x2*>(&pT[hq * kPLds + hf * 16 + 4 * g]) =
         u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     if (hf == 0 && g == 0) s_alpha[hq] = alpha;
-    __syncthreads();
+    lds_barrier();
     // ---- PV
     {
       float al[4];
@@ -208,10 +237,13 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[e][j] *= al[j];
       }
+      // dims 64*wave + 4*l16 .. +3 live in logical slot 8*wave + l16/2, half l16&1
       u32x2 v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = *reinterpret_cast<const u32x2*>(tb + (8 * g + i) * kKvLds + 64 * wave + 4 * l16);
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * g + i;
+        v[i] = *reinterpret_cast<const u32x2*>(tb + swz(r, 8 * wave + (l16 >> 1)) * 8 + 4 * (l16 & 1));
+      }
       bf16x8 pb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -231,9 +263,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
         for (int j = 0; j < 4; ++j) o[e][j] = mfma16(fa, pb[j], o[e][j]);
       }
     }
-    if (tt + 1 < ntiles) lstore(buf ^ 1, tt + 1);
-    __syncthreads();
+    }
+    lds_barrier();  // everyone is done with ring slot buf and with pT
+    gather(tt + kRing, tbw, buf);
+  };
+  for (int tt = 0; tt < ntiles; tt += kRing) {
+    step(tt, std::integral_constant<int, 0>{});
+    step(tt + 1, std::integral_constant<int, 1>{});
+    step(tt + 2, std::integral_constant<int, 2>{});
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still target this workgroup's LDS at exit
 
   // ---- finish: l of a head = its lanes' partial sums over both key halves
   float l_sum = l_part + xor_lane(l_part, 16);
