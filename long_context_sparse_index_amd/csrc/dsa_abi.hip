@@ -151,7 +151,7 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const
   if ((s = check_device()) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_index_scores(to_launch(batch, 0, batch->num_queries), q_idx, w,
-                                                k_idx, scores, ld_scores, use_gemm(batch),
+                                                k_idx, scores, ld_scores, use_gemm(batch), nullptr,
                                                 (hipStream_t)stream));
 }
 
@@ -171,7 +171,7 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
   if ((s = check_device()) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_topk(to_launch(batch, 0, batch->num_queries), scores,
-                                        ld_scores, k, idx, ws, (hipStream_t)stream));
+                                        ld_scores, k, idx, ws, false, (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
@@ -245,10 +245,13 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
     const dsa::LaunchBatch lb = to_launch(batch, t0, n);
     float* scores = reinterpret_cast<float*>(base + p.scores_off);
     int32_t* idx = need_idx ? reinterpret_cast<int32_t*>(base + p.idx_off) : idx_out + (int64_t)t0 * k;
+    // The key scan writes the split top-k's slice lists as it goes.
+    void* topk_ws = base + p.topk_off;
+    const bool fused_lists = !gemm && dsa::topk_split(n, topk_ws);
     hipError_t e = dsa::launch_index_scores(lb, q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
                                             w + (int64_t)t0 * DSA_INDEX_HEADS, k_idx, scores, ld,
-                                            gemm, st);
-    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, base + p.topk_off, st);
+                                            gemm, fused_lists ? topk_ws : nullptr, st);
+    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, topk_ws, fused_lists, st);
     if (e == hipSuccess)
       e = dsa::launch_sparse_mla(lb, p.mla, q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM,
                                  q_rope + (int64_t)t0 * DSA_HEADS * DSA_QK_ROPE_DIM, kv, w_uk,

@@ -15,17 +15,21 @@ struct LaunchBatch {
   const int64_t* seq_row0; // [B] device
 };
 
-// Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries.
+// Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries;
+// else the per-query key scan, which also writes the split top-k's slice bin
+// lists into topk_ws when that is not null.
 hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
-                               hipStream_t st);
+                               void* topk_ws, hipStream_t st);
 
 // Top-k selection.  Batches of few rows use a split path that needs
 // topk_workspace_bytes(T, max_ctx) of workspace; with ws == nullptr every row
-// runs on one workgroup (same result).
+// runs on one workgroup (same result).  lists_ready: the key scan already
+// wrote the slice bin lists into ws.
 size_t topk_workspace_bytes(int T, int max_ctx);
+bool topk_split(int T, const void* ws);
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, hipStream_t st);
+                       void* ws, bool lists_ready, hipStream_t st);
 
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {

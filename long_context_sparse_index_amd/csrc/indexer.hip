@@ -11,35 +11,44 @@
 // of each key column (16 per lane, then one cross-half lane exchange).
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+#include "topk_plan.h"
 
 namespace dsa {
 
 // ---------------------------------------------------------------- decode scan
-// One workgroup = one query x kScanKeys keys, in tiles of 128 keys (32 KB).
-// A tile is read with fully coalesced 16-byte non-temporal loads (keys are
+// One workgroup = one query x one slice of the row (slice_keys keys, a whole
+// number of 128-key tiles; the slicing fills the chip in whole rounds).  A tile
+// (32 KB) is read with fully coalesced 16-byte non-temporal loads (keys are
 // touched once per decode step) into LDS, double buffered; each of the 4 waves
 // then takes 32 keys of the tile as the MFMA B operand from LDS.  Reading the
 // MFMA layout straight from HBM (2 lanes per 256-byte key row per load) was
 // measured at about half the bandwidth of this coalesced form.
-constexpr int kScanKeys = 1024;
-constexpr int kScanTile = 128;
+// With `lists` set, the workgroup also counts the top digit of its scores in
+// LDS and writes the slice's sparse bin list for the split top-k.
 constexpr int kScanLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 
 __global__ __launch_bounds__(256) void idx_scan_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
     const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, int slice_keys, char* __restrict__ lists,
+    SplitWs sw) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kScanTile * kScanLds];
+  __shared__ uint32_t hist[kTkBins / 2];
+  __shared__ int wave_tot[4];
   const int t = blockIdx.x;
   const int pos = q_pos[t];
-  const int k0 = blockIdx.y * kScanKeys;
+  const int k0 = blockIdx.y * slice_keys;
   if (k0 > pos) return;
-  const int kend = min(k0 + kScanKeys, pos + 1);
+  const int kend = min(k0 + slice_keys, pos + 1);
   const int ntiles = (kend - k0 + kScanTile - 1) / kScanTile;
   const int64_t row0 = seq_row0[q_seq[t]];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
+  if (lists) {
+#pragma unroll
+    for (int i = 0; i < kTkBins / 2 / 256; ++i) hist[tid + 256 * i] = 0u;
+  }
 
   // A operand: head n of query t, K-group g (dims 16j + 8g .. +8 at step j).
   bf16x8 qa[8];
@@ -84,10 +93,18 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     for (int r = 0; r < 16; ++r) part = fmaf(wr[r], relu(acc[r]), part);
     const float tot = part + xor_lane(part, 32);
     const int s = k0 + tile * kScanTile + wave * 32 + n;
-    if (g == 0 && s <= pos) srow[s] = tot;
+    if (g == 0 && s <= pos) {
+      srow[s] = tot;
+      if (lists) hist16_add(hist, score_key(tot));
+    }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();
   }
+  if (lists)
+    write_bin_list<256>(hist,
+                        reinterpret_cast<uint32_t*>(lists + (size_t)t * sw.per_query + sw.list_off +
+                                                    (size_t)blockIdx.y * sw.list_stride),
+                        wave_tot);
 }
 
 // ---------------------------------------------------------------- prefill GEMM
@@ -214,15 +231,16 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
 // ---------------------------------------------------------------- launchers
 hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
-                               hipStream_t st) {
+                               void* topk_ws, hipStream_t st) {
   if (gemm) {
     dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (b.max_ctx + kGemmSplit - 1) / kGemmSplit);
     idx_gemm_kernel<<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx,
                                                    scores, ld, b.T);
   } else {
-    dim3 grid(b.T, (b.max_ctx + kScanKeys - 1) / kScanKeys);
-    idx_scan_kernel<<<grid, 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx, scores,
-                                          ld);
+    const SplitWs sw = split_ws(b.T, b.max_ctx);
+    idx_scan_kernel<<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx,
+                                                     scores, ld, sw.slice_keys,
+                                                     static_cast<char*>(topk_ws), sw);
   }
   return hipGetLastError();
 }

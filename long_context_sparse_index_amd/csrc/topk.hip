@@ -23,22 +23,21 @@
 // Two launch shapes compute the same result:
 //   * one 1024-thread workgroup per row (many rows, e.g. a prefill chunk);
 //   * for few rows (decode), steps 1 and 2 are split over slices of the row:
-//     slice suffix histograms; then per slice the row total (b1, the slice's
-//     output offsets) and the compaction into global A / candidate lists; then
-//     one workgroup per row runs steps 3/4.
+//     each slice's sparse top-digit list (written by the key scan itself, or by
+//     a histogram pass); then per slice the row histogram and the slice's output
+//     offsets from the lists, and the compaction into global A / candidate
+//     lists; then one workgroup per row runs steps 3/4.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+#include "topk_plan.h"
 
 namespace dsa {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kTkBins = 4096;
-constexpr int kCandCap = 12288;
 constexpr int kPerThread = 16;                   // scores per thread per pass step
 constexpr int kStep = kPerThread * kTkThreads;   // scores per pass step
 
-constexpr int kSlice = 8192;          // scores per slice in the split path
 constexpr int kSliceThreads = 256;
 
 struct TkShared {
@@ -51,52 +50,37 @@ struct TkShared {
   int list_c[kMaxTopk];
 };
 
-// Exclusive prefix sum over the workgroup in thread order; total in `total`.
-template <int NW>
-__device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_inclusive_scan(v);
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int x = wave_tot[i];
-    pre += (i < wave) ? x : 0;
-    tot += x;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + incl - v;
-}
-
 // Finds the bin holding the krem-th largest element (1-based, counting from
 // the highest bin) and the number of elements in higher bins.
-__device__ void find_bin(TkShared& sh, int nbins, int krem) {
+__device__ void find_bin(const uint32_t* hist, int nbins, int krem, int* wave_tot, int* sel_bin,
+                         int* sel_above) {
   const int tid = threadIdx.x;
   const int bpt = nbins >= kTkThreads ? nbins / kTkThreads : 1;
   const int top = nbins - 1 - tid * bpt;
   int local = 0;
   for (int b = 0; b < bpt; ++b) {
     const int bin = top - b;
-    if (bin >= 0) local += (int)sh.hist[bin];
+    if (bin >= 0) local += (int)hist[bin];
   }
   int total;
-  const int above = block_excl_scan<kTkWaves>(local, sh.wave_tot, total);
+  const int above = block_excl_scan<kTkWaves>(local, wave_tot, total);
   if (local > 0 && above < krem && krem <= above + local) {
     int acc = above;
     for (int b = 0; b < bpt; ++b) {
       const int bin = top - b;
-      const int c = (int)sh.hist[bin];
+      const int c = (int)hist[bin];
       if (acc + c >= krem) {
-        sh.sel_bin = bin;
-        sh.sel_above = acc;
+        *sel_bin = bin;
+        *sel_above = acc;
         break;
       }
       acc += c;
     }
   }
   __syncthreads();
+}
+__device__ __forceinline__ void find_bin(TkShared& sh, int nbins, int krem) {
+  find_bin(sh.hist, nbins, krem, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
 }
 
 // kPerThread consecutive scores starting at i (i is a multiple of 4).
@@ -320,92 +304,47 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __r
 }
 
 // ---------------------------------------------------------------- split path
-// Workspace, per query: slice suffix histograms [S][4096] u16 (entry b = number
-// of the slice's scores whose top digit is >= b), a header {b1, above1, c1},
-// list A [k_max] and candidates (key, position) [kCandCap][2].
-struct SplitWs {
-  int S;
-  size_t hist_off, hdr_off, a_off, c_off, per_query;
-};
+// Workspace per query (SplitWs): the slice bin lists, a header {b1, above1,
+// c1}, list A [k_max] and candidates (key, position) [kCandCap][2].
 
-__host__ __device__ inline SplitWs split_ws(int max_ctx) {
-  SplitWs w;
-  w.S = (max_ctx + kSlice - 1) / kSlice;
-  size_t o = 0;
-  w.hist_off = o;
-  o += (size_t)w.S * kTkBins * sizeof(uint16_t);
-  w.hdr_off = o;  // {b1, above1, c1, 0}
-  o += 16;
-  w.a_off = o;
-  o += (size_t)kMaxTopk * sizeof(int);
-  w.c_off = o;
-  o += (size_t)kCandCap * 2 * sizeof(uint32_t);
-  w.per_query = (o + 255) / 256 * 256;
-  return w;
-}
-
-// Kernel 1 (grid T x S): suffix histogram of the top digit over one slice.
+// Kernel 1 (grid T x S), only where the key scan did not write the lists:
+// the sparse top-digit list of one slice of stored scores.
 __global__ __launch_bounds__(kSliceThreads) void topk_slice_hist_kernel(
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int64_t ld, int k,
     char* __restrict__ ws, SplitWs w) {
-  __shared__ uint32_t hist[kTkBins];
+  __shared__ uint32_t hist[kTkBins / 2];
   __shared__ int wave_tot[kSliceThreads / 64];
   const int t = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int n = q_pos[t] + 1;
-  const int s0 = s * kSlice;
+  const int s0 = s * w.slice_keys;
   if (n <= k || s0 >= n) return;
-  char* base = ws + (size_t)t * w.per_query;
   const float* row = scores + (int64_t)t * ld;
-  for (int i = tid; i < kTkBins; i += kSliceThreads) hist[i] = 0;
+  for (int i = tid; i < kTkBins / 2; i += kSliceThreads) hist[i] = 0u;
   __syncthreads();
-  const int end = min(n, s0 + kSlice);
-#pragma unroll
-  for (int q = 0; q < kSlice / (4 * kSliceThreads); ++q) {
-    const int b = s0 + 4 * (tid + kSliceThreads * q);
+  const int end = min(n, s0 + w.slice_keys);
+  for (int b = s0 + 4 * tid; b < end; b += 4 * kSliceThreads) {
     if (b + 3 < end) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(row + b);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&hist[score_key(v[e]) >> 20], 1u);
+      for (int e = 0; e < 4; ++e) hist16_add(hist, score_key(v[e]));
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (b + e < end) atomicAdd(&hist[score_key(row[b + e]) >> 20], 1u);
+      for (int e = 0; b + e < end; ++e) hist16_add(hist, score_key(row[b + e]));
     }
   }
   __syncthreads();
-  // suffix sums: thread i owns bins 16i .. 16i+15; threads in descending bin order
-  constexpr int kPerT = kTkBins / kSliceThreads;
-  const int hi_t = kSliceThreads - 1 - tid;  // block of bins, scanned from the top
-  uint32_t v[kPerT];
-  int sum = 0;
-#pragma unroll
-  for (int e = kPerT - 1; e >= 0; --e) {
-    v[e] = hist[hi_t * kPerT + e];
-    sum += (int)v[e];
-  }
-  int tot;
-  int run = block_excl_scan<kSliceThreads / 64>(sum, wave_tot, tot);  // scores in higher blocks
-  uint16_t* dst = reinterpret_cast<uint16_t*>(base + w.hist_off) + (size_t)s * kTkBins;
-  uint32_t out[kPerT];
-#pragma unroll
-  for (int e = kPerT - 1; e >= 0; --e) {
-    run += (int)v[e];
-    out[e] = (uint32_t)run;
-  }
-#pragma unroll
-  for (int q = 0; q < kPerT / 8; ++q) {
-    u32x4 pk;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) pk[d] = out[8 * q + 2 * d] | (out[8 * q + 2 * d + 1] << 16);
-    st16(dst + hi_t * kPerT + 8 * q, pk);
-  }
+  write_bin_list<kSliceThreads>(
+      hist, reinterpret_cast<uint32_t*>(ws + (size_t)t * w.per_query + w.list_off + (size_t)s * w.list_stride),
+      wave_tot);
 }
 
-// Kernel 2 (grid T x S): every workgroup sums the row's slice suffix
-// histograms (finds b1 and its own output offsets) and compacts its slice into
-// list A and the candidate list in position order.
+// Kernel 2 (grid T x S): every workgroup merges the row's slice lists into the
+// row histogram (finds b1) and into the histogram of the earlier slices (its
+// own output offsets), then compacts its slice into list A and the candidate
+// list in position order.
 struct SelShared {
-  uint32_t hist[kTkBins];
+  uint32_t all[kTkBins];
+  uint32_t pre[kTkBins];
+  int start[kMaxSlices + 1];
   int wave_tot[kTkWaves];
   int sel_bin, sel_above;
 };
@@ -417,95 +356,90 @@ __global__ __launch_bounds__(kTkThreads) void topk_slice_select_kernel(
   const int t = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int n = q_pos[t] + 1;
   if (n <= k) return;
-  const int S = (n + kSlice - 1) / kSlice;
+  const int S = (n + w.slice_keys - 1) / w.slice_keys;  // slices holding keys (<= kMaxSlices)
   if (s >= S) return;
   char* base = ws + (size_t)t * w.per_query;
-  const uint16_t* suf = reinterpret_cast<const uint16_t*>(base + w.hist_off);
-  // ---- total suffix histogram; thread owns bins 4*tid .. 4*tid+3
-  uint32_t acc[4] = {0u, 0u, 0u, 0u};
-  for (int j = 0; j < S; ++j) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(suf + (size_t)j * kTkBins + 4 * tid);
-    acc[0] += v.x & 0xFFFFu;
-    acc[1] += v.x >> 16;
-    acc[2] += v.y & 0xFFFFu;
-    acc[3] += v.y >> 16;
+  const char* lists = base + w.list_off;
+  for (int i = tid; i < kTkBins; i += kTkThreads) {
+    sh.all[i] = 0u;
+    sh.pre[i] = 0u;
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) sh.hist[4 * tid + e] = acc[e];
+  // ---- list lengths -> start of each list in the flat entry range
+  const int len = tid < S ? (int)*reinterpret_cast<const uint32_t*>(lists + (size_t)tid * w.list_stride) : 0;
+  int E;
+  const int st0 = block_excl_scan<kTkWaves>(len, sh.wave_tot, E);
+  if (tid < S) sh.start[tid] = st0;
+  if (tid == 0) sh.start[S] = E;
   __syncthreads();
-  // b1: the highest bin whose suffix count reaches k
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int b = 4 * tid + e;
-    const uint32_t above = b + 1 < kTkBins ? sh.hist[b + 1] : 0u;
-    if (sh.hist[b] >= (uint32_t)k && above < (uint32_t)k) {
-      sh.sel_bin = b;
-      sh.sel_above = (int)above;
+  // ---- merge every entry: row histogram, and histogram of slices before s
+  for (int f = tid; f < E; f += kTkThreads) {
+    int lo = 0, hi = S;  // largest j with start[j] <= f
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh.start[mid] <= f) lo = mid; else hi = mid;
     }
+    const uint32_t ent = reinterpret_cast<const uint32_t*>(lists + (size_t)lo * w.list_stride)[1 + f - sh.start[lo]];
+    atomicAdd(&sh.all[ent >> 16], ent & 0xFFFFu);
+    if (lo < s) atomicAdd(&sh.pre[ent >> 16], ent & 0xFFFFu);
   }
   __syncthreads();
+  find_bin(sh.all, kTkBins, k, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
   const uint32_t b1 = (uint32_t)sh.sel_bin;
   const int above1 = sh.sel_above;
-  const int c1 = (int)sh.hist[b1] - above1;
+  const int c1 = (int)sh.all[b1];
   if (s == 0 && tid == 0) {
     int* hdr = reinterpret_cast<int*>(base + w.hdr_off);
     hdr[0] = (int)b1;
     hdr[1] = above1;
     hdr[2] = c1;
   }
-  const bool cand_fit = c1 <= kCandCap;
+  if (c1 > kCandCap) return;  // heavy ties: the row's finish re-reads the row
+  // ---- this slice's offsets: earlier slices' counts above b1 and in b1
+  int ga = 0;
+#pragma unroll
+  for (int e = 0; e < kTkBins / kTkThreads; ++e) {
+    const int b = tid * (kTkBins / kTkThreads) + e;
+    ga += (uint32_t)b > b1 ? (int)sh.pre[b] : 0;
+  }
+  int offA;
+  (void)block_excl_scan<kTkWaves>(ga, sh.wave_tot, offA);
+  int offC = (int)sh.pre[b1];
+  // ---- ordered compaction of the slice, 4 consecutive scores per thread per step
   const float* row = scores + (int64_t)t * ld;
   int* list_a = reinterpret_cast<int*>(base + w.a_off);
   uint32_t* cand = reinterpret_cast<uint32_t*>(base + w.c_off);
-  if (cand_fit) {  // else the row's finish re-reads the row (heavy ties)
-    // ---- this slice's offsets: sums over the earlier slices
-    int ga = 0, gc = 0;
-    for (int j = tid; j < s; j += kTkThreads) {
-      const uint16_t* h = suf + (size_t)j * kTkBins;
-      const int hb = h[b1];
-      const int ha = b1 + 1 < kTkBins ? h[b1 + 1] : 0;
-      ga += ha;
-      gc += hb - ha;
-    }
-    int tot;
-    (void)block_excl_scan<kTkWaves>((ga << 16) | gc, sh.wave_tot, tot);  // 16-bit halves: offsets < 65536
-    int offA = tot >> 16, offC = tot & 0xFFFF;
-    // ---- ordered compaction of the slice (8 consecutive scores per thread)
-    constexpr int kPer = kSlice / kTkThreads;
-    const int s0 = s * kSlice;
-    const int end = min(n, s0 + kSlice);
-    const int i0 = s0 + kPer * tid;
-    uint32_t key[kPer];
-    bool ok[kPer];
+  const int s0 = s * w.slice_keys;
+  const int end = min(n, s0 + w.slice_keys);
+  for (int c0 = s0; c0 < end; c0 += 4 * kTkThreads) {
+    const int i0 = c0 + 4 * tid;
+    uint32_t key[4];
+    bool ok[4];
+    if (i0 + 3 < end) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + i0);
 #pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const int b = i0 + 4 * q;
-      if (b + 3 < end) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(row + b);
+      for (int e = 0; e < 4; ++e) {
+        key[e] = score_key(v[e]);
+        ok[e] = true;
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          key[4 * q + e] = score_key(v[e]);
-          ok[4 * q + e] = true;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ok[4 * q + e] = b + e < end;
-          key[4 * q + e] = ok[4 * q + e] ? score_key(row[b + e]) : 0u;
-        }
+      for (int e = 0; e < 4; ++e) {
+        ok[e] = i0 + e < end;
+        key[e] = ok[e] ? score_key(row[i0 + e]) : 0u;
       }
     }
     int ca = 0, cc = 0;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const uint32_t d = key[e] >> 20;
       ca += ok[e] && d > b1;
       cc += ok[e] && d == b1;
     }
-    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);
+    int tot;
+    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);  // < 4096 each
     int oa = offA + (ex >> 16), oc = offC + (ex & 0xFFFF);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
+    for (int e = 0; e < 4; ++e) {
       if (!ok[e]) continue;
       const uint32_t d = key[e] >> 20;
       if (d > b1) {
@@ -515,6 +449,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_slice_select_kernel(
         ++oc;
       }
     }
+    offA += tot >> 16;
+    offC += tot & 0xFFFF;
   }
 }
 
@@ -557,23 +493,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
 }
 
 // ---------------------------------------------------------------- launch
-// Rows below this count use the split path.
-constexpr int kSplitRows = 128;
+bool topk_split(int T, const void* ws) { return ws != nullptr && T > 0 && T < kSplitRows; }
 
 size_t topk_workspace_bytes(int T, int max_ctx) {
   if (T <= 0 || T >= kSplitRows) return 0;
-  return (size_t)T * split_ws(max_ctx).per_query;
+  return (size_t)T * split_ws(T, max_ctx).per_query;
 }
 
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, hipStream_t st) {
-  if (b.T >= kSplitRows || ws == nullptr) {
+                       void* ws, bool lists_ready, hipStream_t st) {
+  if (!topk_split(b.T, ws)) {
     topk_row_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
     return hipGetLastError();
   }
-  const SplitWs w = split_ws(b.max_ctx);
+  const SplitWs w = split_ws(b.T, b.max_ctx);
   char* wsb = static_cast<char*>(ws);
-  topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
+  if (!lists_ready)
+    topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_slice_select_kernel<<<dim3(b.T, w.S), kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_finish_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w);
   return hipGetLastError();
