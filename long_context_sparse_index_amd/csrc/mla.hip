@@ -79,6 +79,7 @@ constexpr int kCoreThreads = 512;
 constexpr int kRing = 3;
 constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
+constexpr int kPartSlab = kHeads * kLat;  // floats of one split partial
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
 
@@ -122,16 +123,6 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   const int32_t* irow = idx + (int64_t)t * k;
   const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
 
-  bf16x8 qb[18];
-  {
-    const uint16_t* ql = q_lat + ((int64_t)t * kHeads + hq) * kLat + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(ld16(ql + 32 * ks));
-    const uint16_t* qr = q_rope + ((int64_t)t * kHeads + hq) * kRope + 8 * g;
-    qb[16] = as_bf16x8(ld16(qr));
-    qb[17] = as_bf16x8(ld16(qr + 32));
-  }
-
   // o[e][j]: latent dim 64*wave + 16g + 4jj + e, head 16j + l16 (element jj)
   f32x4 o[4][4];
 #pragma unroll
@@ -142,9 +133,10 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 
   const int ntiles = j1 > j0 ? (j1 - j0 + kKT - 1) / kKT : 0;
   // The split's positions go to LDS first, so that no row gather waits on a
-  // dependent global load of its index.
+  // dependent global load of its index; the query operand loads are issued
+  // just ahead of the first gathers.
   for (int j = j0 + tid; j < j1; j += kCoreThreads) s_idx[j - j0] = irow[j];
-  __builtin_amdgcn_s_waitcnt(0);  // q and the index list are in place before any gather
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Gather of tile tt into ring slot buf: wave instruction i covers the 64
@@ -173,11 +165,23 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       s_valid[buf][tid] = (j0 + jl < j1) && s_idx[jl] >= 0;
     }
   };
+  bf16x8 qb[18];
+  {
+    const uint16_t* ql = q_lat + ((int64_t)t * kHeads + hq) * kLat + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(ld16(ql + 32 * ks));
+    const uint16_t* qr = q_rope + ((int64_t)t * kHeads + hq) * kRope + 8 * g;
+    qb[16] = as_bf16x8(ld16(qr));
+    qb[17] = as_bf16x8(ld16(qr + 32));
+  }
   // Every step issues the gather of the tile three ahead, past the end too, so
   // that exactly two tiles (10 loads per wave) are in flight at each wait.
   gather(0, tile0, 0);
   gather(1, tile1, 1);
   gather(2, tile2, 2);
+  // Vector loads complete in issue order: with the 15 gather loads of this
+  // wave the most recent, vmcnt <= 15 means the query operands are in place.
+  wait_vm<15>();
 
   auto step = [&](int tt, auto BUFC) {
     constexpr int buf = decltype(BUFC)::value;
@@ -296,12 +300,14 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
             u32x2{pack_bf16x2(o[0][j][jj] * inv, o[1][j][jj] * inv),
                   pack_bf16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
     } else {
-      const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
-      float* dst = o_part + base * kLat + dim0;
+      // Partials keep the accumulator order (see mla_merge_kernel), so that each
+      // store instruction writes 1 KB of consecutive memory.
+      float* dst = o_part + ((int64_t)t * S + sp) * kPartSlab + ((wave * 4 + j) * 4) * 256 + lane * 4;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<f32x4*>(dst + 4 * jj) = f32x4{o[0][j][jj], o[1][j][jj], o[2][j][jj], o[3][j][jj]};
+        *reinterpret_cast<f32x4*>(dst + jj * 256) = f32x4{o[0][j][jj], o[1][j][jj], o[2][j][jj], o[3][j][jj]};
       if (wave == 0 && g == 0) {
+        const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
         ml_part[base * 2] = s_m[h];
         ml_part[base * 2 + 1] = L;
       }
@@ -310,27 +316,34 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 }
 
 // ---------------------------------------------------------------- merge
-// grid (T, 64 heads); thread i combines latent dims 2i, 2i+1 over the splits.
+// Split partials of (query t, split s) form one slab of kHeads * kLat floats in
+// the core's accumulator order: element e of f32x4 number
+// ((w * 4 + j) * 4 + jj) * 64 + lane is latent dim 64w + 16(lane / 16) + 4jj + e
+// of head 16j + lane % 16.  ml_part[t][s][h] = (reference max m, sum l).
+// grid (T, 32): workgroup (t, 4w + j) combines latent dims 64w .. 64w+63 of
+// heads 16j .. 16j+15, one f32x4 of every split per thread.
 __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ o_part,
                                                         const float* __restrict__ ml_part, int S,
                                                         uint16_t* __restrict__ o_lat) {
-  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int t = blockIdx.x, w = blockIdx.y >> 2, j = blockIdx.y & 3, tid = threadIdx.x;
+  const int lane = tid & 63, jj = tid >> 6;
+  const int h = 16 * j + (lane & 15), g = lane >> 4;
+  const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
+  const float* src = o_part + (int64_t)t * S * kPartSlab + (((w * 4 + j) * 4 + jj) * 64 + lane) * 4;
   float mstar = -1e30f;
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml_part[(((int64_t)t * S + s) * kHeads + h) * 2]);
-  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml[s * kHeads * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const int64_t base = ((int64_t)t * S + s) * kHeads + h;
-    const float wgt = exp2f(ml_part[base * 2] - mstar);
-    L += wgt * ml_part[base * 2 + 1];
-    const float* src = o_part + base * kLat + 2 * tid;
-    a0 += wgt * src[0];
-    a1 += wgt * src[1];
+    const float wgt = exp2f(ml[s * kHeads * 2] - mstar);
+    L += wgt * ml[s * kHeads * 2 + 1];
+    acc += wgt * *reinterpret_cast<const f32x4*>(src + (int64_t)s * kPartSlab);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  *reinterpret_cast<uint32_t*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 2 * tid) =
-      pack_bf16x2(a0 * inv, a1 * inv);
+  *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 64 * w + 16 * g + 4 * jj) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
 }
 
 // ---------------------------------------------------------------- upproj
@@ -454,7 +467,7 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
-    mla_merge_kernel<<<dim3(T, kHeads), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+    mla_merge_kernel<<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

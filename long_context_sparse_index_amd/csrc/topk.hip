@@ -51,36 +51,39 @@ struct TkShared {
 };
 
 // Finds the bin holding the krem-th largest element (1-based, counting from
-// the highest bin) and the number of elements in higher bins.
-__device__ void find_bin(const uint32_t* hist, int nbins, int krem, int* wave_tot, int* sel_bin,
-                         int* sel_above) {
+// the highest bin) and the number of elements in higher bins (NT threads,
+// NBINS bins; thread i owns a block of bins counted from the top).
+template <int NT, int NBINS>
+__device__ void find_bin(const uint32_t* hist, int krem, int* wave_tot, int* sel_bin, int* sel_above) {
+  constexpr int kBpt = NBINS >= NT ? NBINS / NT : 1;
   const int tid = threadIdx.x;
-  const int bpt = nbins >= kTkThreads ? nbins / kTkThreads : 1;
-  const int top = nbins - 1 - tid * bpt;
+  const int top = NBINS - 1 - tid * kBpt;
+  uint32_t c[kBpt];
   int local = 0;
-  for (int b = 0; b < bpt; ++b) {
-    const int bin = top - b;
-    if (bin >= 0) local += (int)hist[bin];
+#pragma unroll
+  for (int b = 0; b < kBpt; ++b) {
+    c[b] = top - b >= 0 ? hist[top - b] : 0u;
+    local += (int)c[b];
   }
   int total;
-  const int above = block_excl_scan<kTkWaves>(local, wave_tot, total);
+  const int above = block_excl_scan<NT / 64>(local, wave_tot, total);
   if (local > 0 && above < krem && krem <= above + local) {
     int acc = above;
-    for (int b = 0; b < bpt; ++b) {
-      const int bin = top - b;
-      const int c = (int)hist[bin];
-      if (acc + c >= krem) {
-        *sel_bin = bin;
+#pragma unroll
+    for (int b = 0; b < kBpt; ++b) {
+      if (acc + (int)c[b] >= krem) {
+        *sel_bin = top - b;
         *sel_above = acc;
         break;
       }
-      acc += c;
+      acc += (int)c[b];
     }
   }
   __syncthreads();
 }
-__device__ __forceinline__ void find_bin(TkShared& sh, int nbins, int krem) {
-  find_bin(sh.hist, nbins, krem, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
+template <int NBINS>
+__device__ __forceinline__ void find_bin(TkShared& sh, int krem) {
+  find_bin<kTkThreads, NBINS>(sh.hist, krem, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
 }
 
 // kPerThread consecutive scores starting at i (i is a multiple of 4).
@@ -124,7 +127,7 @@ __device__ void finish_from_candidates(TkShared& sh, uint32_t b1, int above1, in
   __syncthreads();
   for (int j = tid; j < c1; j += kTkThreads) atomicAdd(&sh.hist[(sh.cand_key[j] >> 8) & 0xFFFu], 1u);
   __syncthreads();
-  find_bin(sh, kTkBins, krem);
+  find_bin<kTkBins>(sh, krem);
   const uint32_t b2 = (uint32_t)sh.sel_bin;
   const int krem2 = krem - sh.sel_above;
   __syncthreads();
@@ -135,7 +138,7 @@ __device__ void finish_from_candidates(TkShared& sh, uint32_t b1, int above1, in
     if (((key >> 8) & 0xFFFu) == b2) atomicAdd(&sh.hist[key & 0xFFu], 1u);
   }
   __syncthreads();
-  find_bin(sh, 256, krem2);
+  find_bin<256>(sh, krem2);
   const uint32_t b3 = (uint32_t)sh.sel_bin;
   const int r = krem2 - sh.sel_above;  // ties at the threshold key to keep (lowest positions)
   const uint32_t kstar = (b1 << 20) | (b2 << 8) | b3;
@@ -183,7 +186,7 @@ __device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t 
       if (ok[e] && (key[e] >> 20) == b1) atomicAdd(&sh.hist[(key[e] >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
-  find_bin(sh, kTkBins, krem);
+  find_bin<kTkBins>(sh, krem);
   const uint32_t b2 = (uint32_t)sh.sel_bin;
   const int krem2 = krem - sh.sel_above;
   __syncthreads();
@@ -199,7 +202,7 @@ __device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t 
       if (ok[e] && (key[e] >> 8) == pre) atomicAdd(&sh.hist[key[e] & 0xFFu], 1u);
   }
   __syncthreads();
-  find_bin(sh, 256, krem2);
+  find_bin<256>(sh, krem2);
   const int r = krem2 - sh.sel_above;
   const uint32_t kstar = (pre << 8) | (uint32_t)sh.sel_bin;
   int nG = 0, nE = 0;
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __r
       if (ok[e]) atomicAdd(&sh.hist[key[e] >> 20], 1u);
   }
   __syncthreads();
-  find_bin(sh, kTkBins, k);
+  find_bin<kTkBins>(sh, k);
   const uint32_t b1 = (uint32_t)sh.sel_bin;
   const int above1 = sh.sel_above;
   const int c1 = (int)sh.hist[b1];
@@ -341,52 +344,149 @@ __global__ __launch_bounds__(kSliceThreads) void topk_slice_hist_kernel(
 // row histogram (finds b1) and into the histogram of the earlier slices (its
 // own output offsets), then compacts its slice into list A and the candidate
 // list in position order.
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelKeys = 16;                       // consecutive scores per thread per step
+constexpr int kSelStep = kSelKeys * kSelThreads;   // 4096 scores per step
+constexpr int kSelBinsPT = kTkBins / kSelThreads;  // 16 bins per thread
+constexpr int kListBatch = 16;                     // lists in flight per wave (64 per workgroup)
+
 struct SelShared {
-  uint32_t all[kTkBins];
-  uint32_t pre[kTkBins];
-  int start[kMaxSlices + 1];
-  int wave_tot[kTkWaves];
-  int sel_bin, sel_above;
+  uint32_t all[kTkBins];  // row histogram of the top digit
+  uint32_t pre[kTkBins];  // the same over the slices before this one
+  uint64_t wave_tot64[kSelWaves];
+  int wave_tot[kSelWaves];
+  int b1, above1, c1, offA, offC;
 };
 
-__global__ __launch_bounds__(kTkThreads) void topk_slice_select_kernel(
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int o) {
+  const int lo = __shfl_up((int)(uint32_t)v, o, 64), hi = __shfl_up((int)(uint32_t)(v >> 32), o, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int64_t ld, int k,
     char* __restrict__ ws, SplitWs w) {
   __shared__ SelShared sh;
-  const int t = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int t = blockIdx.x, s = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  char* base = ws + (size_t)t * w.per_query;
+  const char* lists = base + w.list_off;
+  const float* row = scores + (int64_t)t * ld;
+  const int s0 = s * w.slice_keys;
+  // Loads that do not depend on the row length go out first.  Lists: wave v
+  // reads lists v, v+4, ..., one 4-byte word per lane (word 0 = count); lists
+  // past the row's end are stale and skipped below.  Scores: the first
+  // kSelStep of the slice, 16 consecutive per thread (the slice starts inside
+  // the row, and reads stop at ld).
+  uint32_t word[kListBatch];
+#pragma unroll
+  for (int u = 0; u < kListBatch; ++u) {
+    const int j = wave + kSelWaves * u;
+    word[u] = j < w.S ? reinterpret_cast<const uint32_t*>(lists + (size_t)j * w.list_stride)[lane] : 0u;
+  }
+  auto load16 = [&](int i0, int lim, float v[kSelKeys]) {
+#pragma unroll
+    for (int q = 0; q < kSelKeys / 4; ++q) {
+      const int b = i0 + 4 * q;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (b + 3 < lim) x = *reinterpret_cast<const f32x4*>(row + b);
+      else
+        for (int e = 0; e < 4; ++e)
+          if (b + e < lim) x[e] = row[b + e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+  };
+  float v0[kSelKeys];
+  {
+    const int lim = (int)min((int64_t)s0 + min(w.slice_keys, kSelStep), ld);
+    load16(s0 + kSelKeys * tid, lim, v0);
+  }
   const int n = q_pos[t] + 1;
   if (n <= k) return;
   const int S = (n + w.slice_keys - 1) / w.slice_keys;  // slices holding keys (<= kMaxSlices)
   if (s >= S) return;
-  char* base = ws + (size_t)t * w.per_query;
-  const char* lists = base + w.list_off;
-  for (int i = tid; i < kTkBins; i += kTkThreads) {
-    sh.all[i] = 0u;
-    sh.pre[i] = 0u;
+  for (int i = tid; i < kTkBins / 4; i += kSelThreads) {
+    reinterpret_cast<u32x4*>(sh.all)[i] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(sh.pre)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  // ---- list lengths -> start of each list in the flat entry range
-  const int len = tid < S ? (int)*reinterpret_cast<const uint32_t*>(lists + (size_t)tid * w.list_stride) : 0;
-  int E;
-  const int st0 = block_excl_scan<kTkWaves>(len, sh.wave_tot, E);
-  if (tid < S) sh.start[tid] = st0;
-  if (tid == 0) sh.start[S] = E;
   __syncthreads();
-  // ---- merge every entry: row histogram, and histogram of slices before s
-  for (int f = tid; f < E; f += kTkThreads) {
-    int lo = 0, hi = S;  // largest j with start[j] <= f
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sh.start[mid] <= f) lo = mid; else hi = mid;
+  // ---- merge the lists: row histogram, and histogram of the slices before s
+  for (int j0 = 0; j0 < S; j0 += kSelWaves * kListBatch) {
+    if (j0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kListBatch; ++u) {
+        const int j = j0 + wave + kSelWaves * u;
+        word[u] = j < S ? reinterpret_cast<const uint32_t*>(lists + (size_t)j * w.list_stride)[lane] : 0u;
+      }
     }
-    const uint32_t ent = reinterpret_cast<const uint32_t*>(lists + (size_t)lo * w.list_stride)[1 + f - sh.start[lo]];
-    atomicAdd(&sh.all[ent >> 16], ent & 0xFFFFu);
-    if (lo < s) atomicAdd(&sh.pre[ent >> 16], ent & 0xFFFFu);
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int j = j0 + wave + kSelWaves * u;
+      if (j >= S) continue;  // wave-uniform
+      const uint32_t* lst = reinterpret_cast<const uint32_t*>(lists + (size_t)j * w.list_stride);
+      const int cnt = __shfl(word[u], 0, 64);
+      for (int e0 = 0; e0 <= cnt; e0 += 64) {  // words e0 .. e0+63 (entries are words 1..cnt)
+        const uint32_t ent = e0 == 0 ? word[u] : (e0 + lane <= cnt ? lst[e0 + lane] : 0u);
+        const int widx = e0 + lane;
+        if (widx >= 1 && widx <= cnt) {
+          atomicAdd(&sh.all[ent >> 16], ent & 0xFFFFu);
+          if (j < s) atomicAdd(&sh.pre[ent >> 16], ent & 0xFFFFu);
+        }
+      }
+    }
   }
   __syncthreads();
-  find_bin(sh.all, kTkBins, k, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
-  const uint32_t b1 = (uint32_t)sh.sel_bin;
-  const int above1 = sh.sel_above;
-  const int c1 = (int)sh.all[b1];
+  // ---- b1 and this slice's offsets from one scan over (row, earlier-slice)
+  // counts in descending bin order; thread i owns bins 4095-16i-15 .. 4095-16i
+  {
+    const int lo_bin = kTkBins - kSelBinsPT * (tid + 1);
+    uint32_t ca[kSelBinsPT], cp[kSelBinsPT];
+#pragma unroll
+    for (int q = 0; q < kSelBinsPT / 4; ++q) {
+      const u32x4 a4 = reinterpret_cast<const u32x4*>(sh.all + lo_bin)[q];
+      const u32x4 p4 = reinterpret_cast<const u32x4*>(sh.pre + lo_bin)[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ca[4 * q + e] = a4[e];
+        cp[4 * q + e] = p4[e];
+      }
+    }
+    uint64_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < kSelBinsPT; ++e) mine += ((uint64_t)ca[e] << 32) | cp[e];
+    uint64_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = shfl_up64(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh.wave_tot64[wave] = incl;
+    __syncthreads();
+    uint64_t ex = incl - mine;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) ex += i < wave ? sh.wave_tot64[i] : 0ull;
+    uint32_t above = (uint32_t)(ex >> 32), pre_above = (uint32_t)ex;
+    const uint32_t mine_all = (uint32_t)(mine >> 32);
+    if (above < (uint32_t)k && (uint32_t)k <= above + mine_all) {
+#pragma unroll
+      for (int e = kSelBinsPT - 1; e >= 0; --e) {
+        if (above + ca[e] >= (uint32_t)k) {
+          sh.b1 = lo_bin + e;
+          sh.above1 = (int)above;
+          sh.c1 = (int)ca[e];
+          sh.offA = (int)pre_above;
+          sh.offC = (int)cp[e];
+          break;
+        }
+        above += ca[e];
+        pre_above += cp[e];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t b1 = (uint32_t)sh.b1;
+  const int above1 = sh.above1, c1 = sh.c1;
   if (s == 0 && tid == 0) {
     int* hdr = reinterpret_cast<int*>(base + w.hdr_off);
     hdr[0] = (int)b1;
@@ -394,53 +494,36 @@ __global__ __launch_bounds__(kTkThreads) void topk_slice_select_kernel(
     hdr[2] = c1;
   }
   if (c1 > kCandCap) return;  // heavy ties: the row's finish re-reads the row
-  // ---- this slice's offsets: earlier slices' counts above b1 and in b1
-  int ga = 0;
-#pragma unroll
-  for (int e = 0; e < kTkBins / kTkThreads; ++e) {
-    const int b = tid * (kTkBins / kTkThreads) + e;
-    ga += (uint32_t)b > b1 ? (int)sh.pre[b] : 0;
-  }
-  int offA;
-  (void)block_excl_scan<kTkWaves>(ga, sh.wave_tot, offA);
-  int offC = (int)sh.pre[b1];
-  // ---- ordered compaction of the slice, 4 consecutive scores per thread per step
-  const float* row = scores + (int64_t)t * ld;
+  int offA = sh.offA, offC = sh.offC;
+  // ---- ordered compaction of the slice, 16 consecutive scores per thread per step
   int* list_a = reinterpret_cast<int*>(base + w.a_off);
   uint32_t* cand = reinterpret_cast<uint32_t*>(base + w.c_off);
-  const int s0 = s * w.slice_keys;
   const int end = min(n, s0 + w.slice_keys);
-  for (int c0 = s0; c0 < end; c0 += 4 * kTkThreads) {
-    const int i0 = c0 + 4 * tid;
-    uint32_t key[4];
-    bool ok[4];
-    if (i0 + 3 < end) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + i0);
+  for (int c0 = s0; c0 < end; c0 += kSelStep) {
+    const int i0 = c0 + kSelKeys * tid;
+    float v[kSelKeys];
+    if (c0 == s0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = score_key(v[e]);
-        ok[e] = true;
-      }
+      for (int e = 0; e < kSelKeys; ++e) v[e] = v0[e];
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ok[e] = i0 + e < end;
-        key[e] = ok[e] ? score_key(row[i0 + e]) : 0u;
-      }
+      load16(i0, end, v);
     }
+    uint32_t key[kSelKeys];
     int ca = 0, cc = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kSelKeys; ++e) {
+      const bool ok = i0 + e < end;
+      key[e] = ok ? score_key(v[e]) : 0u;  // unused when !ok
       const uint32_t d = key[e] >> 20;
-      ca += ok[e] && d > b1;
-      cc += ok[e] && d == b1;
+      ca += ok && d > b1;
+      cc += ok && d == b1;
     }
     int tot;
-    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);  // < 4096 each
-    int oa = offA + (ex >> 16), oc = offC + (ex & 0xFFFF);
+    const int exs = block_excl_scan<kSelWaves>((ca << 16) | cc, sh.wave_tot, tot);  // < 4096 each
+    int oa = offA + (exs >> 16), oc = offC + (exs & 0xFFFF);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!ok[e]) continue;
+    for (int e = 0; e < kSelKeys; ++e) {
+      if (i0 + e >= end) continue;
       const uint32_t d = key[e] >> 20;
       if (d > b1) {
         list_a[oa++] = i0 + e;
@@ -464,13 +547,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
                                                                  SplitWs w) {
   __shared__ TkShared sh;
   const int t = blockIdx.x, tid = threadIdx.x;
+  const char* base = ws + (size_t)t * w.per_query;
+  const int* list_a = reinterpret_cast<const int*>(base + w.a_off);
+  const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
+  // List A (at most kMaxTopk entries) and the first 2048 candidates are read
+  // together with the header; entries past the counts are stale and unused.
+  constexpr int kSpec = kMaxTopk / kTkThreads;
+  int a_spec[kSpec];
+  u32x2 c_spec[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    a_spec[u] = list_a[tid + u * kTkThreads];
+    c_spec[u] = *reinterpret_cast<const u32x2*>(cand + 2 * (tid + u * kTkThreads));
+  }
   const int n = q_pos[t] + 1;
   int32_t* out = idx + (int64_t)t * k;
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const char* base = ws + (size_t)t * w.per_query;
   const int* hdr = reinterpret_cast<const int*>(base + w.hdr_off);
   const uint32_t b1 = (uint32_t)hdr[0];
   const int above1 = hdr[1];
@@ -480,10 +575,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
     finish_from_row(sh, scores + (int64_t)t * ld, n, b1, krem, out);
     return;
   }
-  const int* list_a = reinterpret_cast<const int*>(base + w.a_off);
-  const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
-  for (int i = tid; i < above1; i += kTkThreads) sh.list_a[i] = list_a[i];
-  for (int j = tid; j < c1; j += kTkThreads) {
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int i = tid + u * kTkThreads;
+    if (i < above1) sh.list_a[i] = a_spec[u];
+    if (i < c1) {
+      sh.cand_key[i] = c_spec[u].x;
+      sh.cand_pos[i] = (int)c_spec[u].y;
+    }
+  }
+  for (int j = kMaxTopk + tid; j < c1; j += kTkThreads) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(cand + 2 * j);
     sh.cand_key[j] = v.x;
     sh.cand_pos[j] = (int)v.y;
@@ -510,7 +611,7 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
   char* wsb = static_cast<char*>(ws);
   if (!lists_ready)
     topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
-  topk_slice_select_kernel<<<dim3(b.T, w.S), kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
+  topk_slice_select_kernel<<<dim3(b.T, w.S), kSelThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_finish_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w);
   return hipGetLastError();
 }

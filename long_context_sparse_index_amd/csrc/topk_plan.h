@@ -19,7 +19,8 @@ constexpr int kScanTile = 128;   // keys per scan tile and slice granularity
 constexpr int kTkBins = 4096;    // top-digit bins
 constexpr int kCandCap = 12288;  // candidates of the threshold bin kept in LDS
 constexpr int kSplitRows = 128;  // batches with fewer rows use the split top-k
-constexpr int kMaxSlices = 1024; // slices per row (one per select thread)
+constexpr int kMaxSlices = 1024; // slices per row
+constexpr int kScanSlots = 512;  // resident key-scan workgroups (two per CU)
 
 struct SplitWs {
   int S;               // slices per row (for max_ctx)
@@ -31,7 +32,7 @@ struct SplitWs {
 // Slicing for T rows of up to max_ctx keys: slices are 1..511 tiles long (so a
 // slice's bin counts fit 16 bits) and a row has at most kMaxSlices of them.
 // Among those, the longest slices are taken whose T x S workgroups fill the
-// 512 resident scan workgroups (2 per CU) in whole rounds to >= 90%.
+// kScanSlots resident scan workgroups in whole rounds to >= 90%.
 inline SplitWs split_ws(int T, int max_ctx) {
   const int tpr = (max_ctx + kScanTile - 1) / kScanTile;
   const int lo = tpr > 1024 ? (tpr + 1023) / 1024 : 1;
@@ -40,7 +41,7 @@ inline SplitWs split_ws(int T, int max_ctx) {
   double best_eff = -1.0;
   for (int tpw = hi; tpw >= lo; --tpw) {
     const int S = (tpr + tpw - 1) / tpw;
-    const double rounds = (double)T * S / 512.0;
+    const double rounds = (double)T * S / (double)kScanSlots;
     const double full = rounds <= 1.0 ? 1.0 : (double)(long long)(rounds + 0.999999);
     const double eff = rounds / full;
     if (eff > best_eff + 1e-9) {
