@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __shared__ float s_l[2][kHeads];
   __shared__ float s_m[kHeads];
   __shared__ int s_valid[kRing][kKT];
-  __shared__ int s_idx[kMaxTopk];
+  __shared__ int s_idx[kMaxTopk + 4 * kKT];  // the split's positions, -1 padded
   const int t = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -134,36 +134,60 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   const int ntiles = j1 > j0 ? (j1 - j0 + kKT - 1) / kKT : 0;
   // The split's positions go to LDS first, so that no row gather waits on a
   // dependent global load of its index; the query operand loads are issued
-  // just ahead of the first gathers.
-  for (int j = j0 + tid; j < j1; j += kCoreThreads) s_idx[j - j0] = irow[j];
+  // just ahead of the first gathers.  Entries past the split are -1: the loop
+  // (unrolled by 3) gathers up to four tiles past its last one.
+  {
+    constexpr int kPer = (kMaxTopk + 4 * kKT + kCoreThreads - 1) / kCoreThreads;
+    const int nfill = (ntiles + 4) * kKT;
+    int v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {  // all loads first, then the stores
+      const int j = tid + u * kCoreThreads;
+      const int e = irow[min(j0 + j, k - 1)];  // in-row read, replaced past the split
+      v[u] = j0 + j < j1 ? e : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kCoreThreads;
+      if (j < nfill) s_idx[j] = v[u];
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Gather of tile tt into ring slot buf: wave instruction i covers the 64
+  // Gather of a tile into a ring slot: wave instruction i covers the 64
   // physical slots [(8i + w) * 64, +64).  2304 slots = 4.5 instructions per
   // wave; every wave issues exactly 5 (waves 4-7 repeat the last chunk of
   // waves 0-3: same source, same destination) so that the number of
-  // outstanding loads per tile is the same constant for every wave.
-  auto gather = [&](int tt, uint16_t* dstt, int buf) {
+  // outstanding loads per tile is the same constant for every wave.  The DMA
+  // writes lane L of an instruction to physical slot base + L; that slot holds
+  // logical column (pc & ~7) | ((pc ^ row) & 7) of its row (the swizzle is an
+  // involution within groups of 8), so the lane fetches that chunk.  Row and
+  // column of each lane's five chunks are the same for every tile.
+  int g_row[5];
+  uint32_t g_col[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
+    const int lin = blk * 64 + lane;  // physical slot, < 2304
+    const int r = lin / kSlots, pc = lin - r * kSlots;
+    g_row[i] = r;
+    g_col[i] = (uint32_t)((pc & ~7) | ((pc ^ r) & 7)) * 8u;
+  }
+  auto gather_idx = [&](int tt, int sidx[5], int& valid) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) sidx[i] = s_idx[tt * kKT + g_row[i]];
+    valid = tid < kKT ? s_idx[tt * kKT + tid] : -1;
+  };
+  auto gather_issue = [&](const int sidx[5], int valid, uint16_t* dstt, int buf) {
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
-      // The DMA writes lane L of the instruction to physical slot base + L; that
-      // slot holds logical column (pc & ~7) | ((pc ^ row) & 7) of its row (the
-      // swizzle is an involution within groups of 8), so fetch that chunk.
-      const int lin = blk * 64 + lane;  // physical slot, < 2304
-      const int r = lin / kSlots, pc = lin - r * kSlots;
-      const int lc = (pc & ~7) | ((pc ^ r) & 7);
-      const int jl = tt * kKT + r;
-      const int sidx = (j0 + jl < j1) ? s_idx[jl] : -1;
       // absent keys (and tiles past the end) fetch row 0 of the sequence: finite data, masked later
-      const uint32_t off = (uint32_t)(sidx >= 0 ? sidx : 0) * (uint32_t)kRow + (uint32_t)lc * 8u;
+      const uint32_t off = (uint32_t)(sidx[i] >= 0 ? sidx[i] : 0) * (uint32_t)kRow + g_col[i];
       __builtin_amdgcn_global_load_lds(kv_seq + off, dstt + blk * 64 * 8, 16, 0, 0);
     }
-    if (tid < kKT) {
-      const int jl = tt * kKT + tid;
-      s_valid[buf][tid] = (j0 + jl < j1) && s_idx[jl] >= 0;
-    }
+    if (tid < kKT) s_valid[buf][tid] = valid >= 0;
   };
   bf16x8 qb[18];
   {
@@ -174,22 +198,36 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     qb[16] = as_bf16x8(ld16(qr));
     qb[17] = as_bf16x8(ld16(qr + 32));
   }
-  // Every step issues the gather of the tile three ahead, past the end too, so
-  // that exactly two tiles (10 loads per wave) are in flight at each wait.
-  gather(0, tile0, 0);
-  gather(1, tile1, 1);
-  gather(2, tile2, 2);
-  // Vector loads complete in issue order: with the 15 gather loads of this
-  // wave the most recent, vmcnt <= 15 means the query operands are in place.
-  wait_vm<15>();
+  // Step tt issues the gather of tile tt + 2 (past the end too) right after
+  // its barrier, into the slot that step tt - 1 used: every wave has passed
+  // that barrier, so no wave still reads the slot.  One tile (5 loads per wave)
+  // is then in flight at each wait.
+  {
+    int sidx[5], valid;
+    gather_idx(0, sidx, valid);
+    gather_issue(sidx, valid, tile0, 0);
+    gather_idx(1, sidx, valid);
+    gather_issue(sidx, valid, tile1, 1);
+  }
+  // Vector loads complete in issue order: with the 10 gather loads of this
+  // wave the most recent, vmcnt <= 10 means the query operands are in place.
+  wait_vm<10>();
 
   auto step = [&](int tt, auto BUFC) {
     constexpr int buf = decltype(BUFC)::value;
+    constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (used by step tt - 1)
     uint16_t* const tbw = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
-    wait_vm<10>();
+    uint16_t* const nbw = nbuf == 0 ? tile0 : (nbuf == 1 ? tile1 : tile2);
+    int sidx[5], valid;
+    gather_idx(tt + 2, sidx, valid);  // positions are static: read ahead of the barrier
+    wait_vm<5>();
     lds_barrier();
+    gather_issue(sidx, valid, nbw, nbuf);
     if (tt < ntiles) {
     const uint16_t* tb = tbw;
+    int vmask[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[buf][hf * 16 + 4 * g + jj];
     // ---- QK: keys hf*16 + 4g + jj of head hq
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     {
@@ -202,7 +240,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     float tmax = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float v = s_valid[buf][hf * 16 + 4 * g + jj] ? sc[jj] * scale_log2 : -INFINITY;
+      const float v = vmask[jj] ? sc[jj] * scale_log2 : -INFINITY;
       z[jj] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -268,8 +306,6 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       }
     }
     }
-    lds_barrier();  // everyone is done with ring slot buf and with pT
-    gather(tt + kRing, tbw, buf);
   };
   for (int tt = 0; tt < ntiles; tt += kRing) {
     step(tt, std::integral_constant<int, 0>{});
