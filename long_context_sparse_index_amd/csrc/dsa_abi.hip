@@ -171,7 +171,8 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
   if ((s = check_device()) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_topk(to_launch(batch, 0, batch->num_queries), scores,
-                                        ld_scores, k, idx, ws, false, (hipStream_t)stream));
+                                        ld_scores, k, idx, ws, false, nullptr,
+                                        (hipStream_t)stream));
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
@@ -197,7 +198,7 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
   (void)hipGetLastError();
   return launch_status(dsa::launch_sparse_mla(to_launch(batch, 0, batch->num_queries), plan,
                                               q_nope, q_rope, kv, w_uk, w_uv, idx, softmax_scale,
-                                              out, out_dtype == DSA_OUT_F32, ws,
+                                              out, out_dtype == DSA_OUT_F32, ws, false,
                                               (hipStream_t)stream));
 }
 
@@ -251,13 +252,20 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
     hipError_t e = dsa::launch_index_scores(lb, q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
                                             w + (int64_t)t0 * DSA_INDEX_HEADS, k_idx, scores, ld,
                                             gemm, fused_lists ? topk_ws : nullptr, st);
-    if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, topk_ws, fused_lists, st);
+    // With the split top-k, the query absorption runs on the finish kernel's
+    // spare workgroups instead of its own launch.
+    const dsa_bf16* q_nope_c = q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM;
+    const bool ride = dsa::topk_split(n, topk_ws);
+    const dsa::AbsorbJob job{q_nope_c, w_uk,
+                             reinterpret_cast<uint16_t*>(base + p.mla_off + p.mla.q_lat_off)};
     if (e == hipSuccess)
-      e = dsa::launch_sparse_mla(lb, p.mla, q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM,
+      e = dsa::launch_topk(lb, scores, ld, k, idx, topk_ws, fused_lists, ride ? &job : nullptr, st);
+    if (e == hipSuccess)
+      e = dsa::launch_sparse_mla(lb, p.mla, q_nope_c,
                                  q_rope + (int64_t)t0 * DSA_HEADS * DSA_QK_ROPE_DIM, kv, w_uk,
                                  w_uv, idx, softmax_scale,
                                  static_cast<char*>(out) + (size_t)t0 * DSA_HEADS * DSA_V_DIM * out_elem,
-                                 out_dtype == DSA_OUT_F32, base + p.mla_off, st);
+                                 out_dtype == DSA_OUT_F32, base + p.mla_off, ride, st);
     if (e != hipSuccess) return launch_status(e);
   }
   return DSA_OK;

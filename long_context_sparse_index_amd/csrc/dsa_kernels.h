@@ -28,8 +28,15 @@ hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, cons
 // wrote the slice bin lists into ws.
 size_t topk_workspace_bytes(int T, int max_ctx);
 bool topk_split(int T, const void* ws);
+// Query absorption that the split top-k may run on its spare workgroups
+// (q_lat = W_UK q_nope for the launch's T queries).
+struct AbsorbJob {
+  const uint16_t* q_nope;
+  const uint16_t* w_uk;
+  uint16_t* q_lat;
+};
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, bool lists_ready, hipStream_t st);
+                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st);
 
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {
@@ -40,6 +47,6 @@ MlaPlan plan_mla(int T, int k);
 hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
                              const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
                              const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
-                             int out_f32, void* ws, hipStream_t st);
+                             int out_f32, void* ws, bool q_lat_ready, hipStream_t st);
 
 }  // namespace dsa

@@ -14,6 +14,7 @@
 //   upproj   out[t,h] = o_lat[t,h] W_UV[h]
 #include <type_traits>
 
+#include "absorb.h"
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -21,39 +22,17 @@ namespace dsa {
 
 // ---------------------------------------------------------------- absorb
 // grid (64 heads, 4 blocks of 128 latent columns, query groups); wave w owns
-// 32 latent columns and keeps their W_UK fragments resident (B[k=d][n=c] =
-// W_UK[h][c][d], contiguous 16-byte loads), then walks 32-query tiles (A =
-// q_nope rows).
+// 32 latent columns (absorb_wave) and walks up to kAbsorbTilesPerWg 32-query
+// tiles.
 constexpr int kAbsorbTilesPerWg = 8;
 
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ w_uk,
                                                      uint16_t* __restrict__ q_lat, int T) {
-  const int h = blockIdx.x, cb = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 5, n = lane & 31;
-  const int c = cb * 128 + wave * 32 + n;
-  bf16x8 bw[kNope / 16];
-  const uint16_t* bp = w_uk + ((int64_t)h * kLat + c) * kNope + 8 * g;
-#pragma unroll
-  for (int j = 0; j < kNope / 16; ++j) bw[j] = as_bf16x8(ld16(bp + 16 * j));
   const int ntb = (T + 31) / 32;
-  for (int tb = blockIdx.z * kAbsorbTilesPerWg; tb < min(ntb, (int)(blockIdx.z + 1) * kAbsorbTilesPerWg);
-       ++tb) {
-    const int t = min(tb * 32 + n, T - 1);
-    const uint16_t* ap = q_nope + ((int64_t)t * kHeads + h) * kNope + 8 * g;
-    bf16x8 a[kNope / 16];
-#pragma unroll
-    for (int j = 0; j < kNope / 16; ++j) a[j] = as_bf16x8(ld16(ap + 16 * j));
-    f32x16 acc = {};
-#pragma unroll
-    for (int j = 0; j < kNope / 16; ++j) acc = mfma32(a[j], bw[j], acc);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = tb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tr < T) q_lat[((int64_t)tr * kHeads + h) * kLat + c] = (uint16_t)f32_to_bf16_bits(acc[r]);
-    }
-  }
+  const int tb0 = blockIdx.z * kAbsorbTilesPerWg;
+  absorb_wave(q_nope, w_uk, q_lat, T, blockIdx.x, blockIdx.y * 128 + (threadIdx.x >> 6) * 32, tb0,
+              min(ntb, tb0 + kAbsorbTilesPerWg));
 }
 
 // ---------------------------------------------------------------- core
@@ -484,7 +463,7 @@ MlaPlan plan_mla(int T, int k) {
 hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
                              const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
                              const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
-                             int out_f32, void* ws, hipStream_t st) {
+                             int out_f32, void* ws, bool q_lat_ready, hipStream_t st) {
   char* base = static_cast<char*>(ws);
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(base + p.q_lat_off);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(base + p.o_lat_off);
@@ -492,10 +471,13 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   float* ml_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
   const int T = b.T;
   const int ntb = (T + 31) / 32;
-  absorb_kernel<<<dim3(kHeads, kLat / 128, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 256, 0,
-                  st>>>(q_nope, w_uk, q_lat, T);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!q_lat_ready) {
+    absorb_kernel<<<dim3(kHeads, kLat / 128, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 256, 0,
+                    st>>>(q_nope, w_uk, q_lat, T);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const float scale_log2 = scale * 1.4426950408889634f;
   mla_core_kernel<<<dim3(T, p.splits), kCoreThreads, 0, st>>>(b.q_seq, b.seq_row0, q_lat, q_rope, kv, idx,
                                                      p.k, scale_log2, p.keys_per_split, p.splits,

@@ -27,6 +27,7 @@
 //     a histogram pass); then per slice the row histogram and the slice's output
 //     offsets from the lists, and the compaction into global A / candidate
 //     lists; then one workgroup per row runs steps 3/4.
+#include "absorb.h"
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 #include "topk_plan.h"
@@ -537,16 +538,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
   }
 }
 
-// Kernel 3 (grid T): load list A and the candidates, resolve the lower
-// digits, merge into the output.
+// Kernel 3 (grid T, plus 64 workgroups when an absorb job rides along): load
+// list A and the candidates, resolve the lower digits, merge into the output.
+// Workgroup T + h, if launched, computes q_lat of head h for every query (16
+// waves x 32 latent columns) on CUs the T row workgroups leave idle.
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* __restrict__ q_pos,
                                                                  const float* __restrict__ scores,
                                                                  int64_t ld, int k,
                                                                  int32_t* __restrict__ idx,
                                                                  const char* __restrict__ ws,
-                                                                 SplitWs w) {
+                                                                 SplitWs w, int T, AbsorbJob ab) {
   __shared__ TkShared sh;
   const int t = blockIdx.x, tid = threadIdx.x;
+  if (t >= T) {
+    absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, (tid >> 6) * 32, 0, (T + 31) / 32);
+    return;
+  }
   const char* base = ws + (size_t)t * w.per_query;
   const int* list_a = reinterpret_cast<const int*>(base + w.a_off);
   const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
@@ -602,7 +609,7 @@ size_t topk_workspace_bytes(int T, int max_ctx) {
 }
 
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, bool lists_ready, hipStream_t st) {
+                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st) {
   if (!topk_split(b.T, ws)) {
     topk_row_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
     return hipGetLastError();
@@ -612,7 +619,9 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
   if (!lists_ready)
     topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_slice_select_kernel<<<dim3(b.T, w.S), kSelThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
-  topk_finish_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w);
+  const AbsorbJob ab = absorb ? *absorb : AbsorbJob{nullptr, nullptr, nullptr};
+  topk_finish_kernel<<<b.T + (absorb ? kHeads : 0), kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w,
+                                                                         b.T, ab);
   return hipGetLastError();
 }
 
