@@ -355,15 +355,10 @@ constexpr int kListBatch = 16;                     // lists in flight per wave (
 struct SelShared {
   uint32_t all[kTkBins];  // row histogram of the top digit
   uint32_t pre[kTkBins];  // the same over the slices before this one
-  uint64_t wave_tot64[kSelWaves];
   int wave_tot[kSelWaves];
+  int wave_tot2[kSelWaves];
   int b1, above1, c1, offA, offC;
 };
-
-__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int o) {
-  const int lo = __shfl_up((int)(uint32_t)v, o, 64), hi = __shfl_up((int)(uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
 
 __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
     const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int64_t ld, int k,
@@ -426,7 +421,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
       const int j = j0 + wave + kSelWaves * u;
       if (j >= S) continue;  // wave-uniform
       const uint32_t* lst = reinterpret_cast<const uint32_t*>(lists + (size_t)j * w.list_stride);
-      const int cnt = __shfl(word[u], 0, 64);
+      const int cnt = __builtin_amdgcn_readfirstlane(word[u]);  // lane 0 read word 0: the count
       for (int e0 = 0; e0 <= cnt; e0 += 64) {  // words e0 .. e0+63 (entries are words 1..cnt)
         const uint32_t ent = e0 == 0 ? word[u] : (e0 + lane <= cnt ? lst[e0 + lane] : 0u);
         const int widx = e0 + lane;
@@ -453,22 +448,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
         cp[4 * q + e] = p4[e];
       }
     }
-    uint64_t mine = 0;
+    // both counts stay below 2^21, so the two scans are plain 32-bit scans
+    uint32_t mine_all = 0, mine_pre = 0;
 #pragma unroll
-    for (int e = 0; e < kSelBinsPT; ++e) mine += ((uint64_t)ca[e] << 32) | cp[e];
-    uint64_t incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t y = shfl_up64(incl, o);
-      if (lane >= o) incl += y;
+    for (int e = 0; e < kSelBinsPT; ++e) {
+      mine_all += ca[e];
+      mine_pre += cp[e];
     }
-    if (lane == 63) sh.wave_tot64[wave] = incl;
+    const int inc_all = wave_inclusive_scan((int)mine_all), inc_pre = wave_inclusive_scan((int)mine_pre);
+    if (lane == 63) {
+      sh.wave_tot[wave] = inc_all;
+      sh.wave_tot2[wave] = inc_pre;
+    }
     __syncthreads();
-    uint64_t ex = incl - mine;
+    uint32_t above = (uint32_t)inc_all - mine_all, pre_above = (uint32_t)inc_pre - mine_pre;
 #pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) ex += i < wave ? sh.wave_tot64[i] : 0ull;
-    uint32_t above = (uint32_t)(ex >> 32), pre_above = (uint32_t)ex;
-    const uint32_t mine_all = (uint32_t)(mine >> 32);
+    for (int i = 0; i < kSelWaves; ++i) {
+      above += i < wave ? (uint32_t)sh.wave_tot[i] : 0u;
+      pre_above += i < wave ? (uint32_t)sh.wave_tot2[i] : 0u;
+    }
     if (above < (uint32_t)k && (uint32_t)k <= above + mine_all) {
 #pragma unroll
       for (int e = kSelBinsPT - 1; e >= 0; --e) {
