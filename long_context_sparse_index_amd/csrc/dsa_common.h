@@ -90,6 +90,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its global loads and stores (__syncthreads also drains those, which
+// would cancel any load issued ahead of the barrier).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Sum over the 64 lanes of a wave (every lane gets it).
 __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane(wave_inclusive_scan(v), 63);

@@ -80,7 +80,7 @@ __device__ void find_bin(const uint32_t* hist, int krem, int* wave_tot, int* sel
       acc += (int)c[b];
     }
   }
-  __syncthreads();
+  lds_sync();
 }
 template <int NBINS>
 __device__ __forceinline__ void find_bin(TkShared& sh, int krem) {
@@ -119,24 +119,42 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
   return lo;
 }
 
-// Step 3: sh.cand_* holds the c1 candidates of bin b1 in position order and
-// sh.list_a the above1 positions above it (ascending); krem = k - above1.
+// Step 3: sh.cand_* holds c1 candidates in position order and sh.list_a the
+// above1 positions above every candidate (ascending); krem = k - above1 of the
+// candidates are kept.  With `window`, the candidates span several top-digit
+// bins and the threshold bin among them is found first; otherwise all of them
+// are in bin b1.
 __device__ void finish_from_candidates(TkShared& sh, uint32_t b1, int above1, int c1, int krem,
-                                       int32_t* out) {
+                                       int32_t* out, bool window = false) {
   const int tid = threadIdx.x;
+  int krem1 = krem;
+  if (window) {
+    for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < c1; j += kTkThreads) atomicAdd(&sh.hist[sh.cand_key[j] >> 20], 1u);
+    __syncthreads();
+    find_bin<kTkBins>(sh, krem);
+    b1 = (uint32_t)sh.sel_bin;
+    krem1 = krem - sh.sel_above;
+    __syncthreads();
+  }
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
-  __syncthreads();
-  for (int j = tid; j < c1; j += kTkThreads) atomicAdd(&sh.hist[(sh.cand_key[j] >> 8) & 0xFFFu], 1u);
-  __syncthreads();
-  find_bin<kTkBins>(sh, krem);
-  const uint32_t b2 = (uint32_t)sh.sel_bin;
-  const int krem2 = krem - sh.sel_above;
-  __syncthreads();
-  for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
   for (int j = tid; j < c1; j += kTkThreads) {
     const uint32_t key = sh.cand_key[j];
-    if (((key >> 8) & 0xFFFu) == b2) atomicAdd(&sh.hist[key & 0xFFu], 1u);
+    if ((key >> 20) == b1) atomicAdd(&sh.hist[(key >> 8) & 0xFFFu], 1u);
+  }
+  __syncthreads();
+  find_bin<kTkBins>(sh, krem1);
+  const uint32_t b2 = (uint32_t)sh.sel_bin;
+  const int krem2 = krem1 - sh.sel_above;
+  __syncthreads();
+  for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  const uint32_t pre12 = (b1 << 12) | b2;
+  for (int j = tid; j < c1; j += kTkThreads) {
+    const uint32_t key = sh.cand_key[j];
+    if ((key >> 8) == pre12) atomicAdd(&sh.hist[key & 0xFFu], 1u);
   }
   __syncthreads();
   find_bin<256>(sh, krem2);
@@ -237,6 +255,120 @@ __device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t 
   }
 }
 
+// ---------------------------------------------------------------- sampled window
+// Long rows: the top-digit histogram of a 1/16 sample of the row (every 16th
+// block of 64 scores) locates the bin of the k-th largest score; one exact
+// ordered pass then keeps everything above a window of bins around it
+// (list A) and collects the window's scores as candidates.  The pass checks
+// that the k-th largest lies inside the window (A holds fewer than k, A plus
+// the window at least k, the candidates fit); then the candidates are
+// resolved as usual and the result is the same as the full histogram path's.
+// Returns false (and the caller runs the full path) when the check fails.
+constexpr int kSampleMinRow = 65536;
+constexpr int kSampleBlock = 64;    // scores per sampled block
+constexpr int kSampleStride = 16;   // one block in 16 is sampled
+constexpr int kWindowHalf = 1;      // window = sample bin +- this many bins
+
+__device__ bool window_select(TkShared& sh, const float* row, int n, int k, int32_t* out) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  // ---- sample: 16 threads x 4 scores per sampled block, 64 blocks per step;
+  // four steps' loads are issued before any is counted
+  int ns = 0;
+  constexpr int kBlocksPerStep = kTkThreads / (kSampleBlock / 4);
+  constexpr int kU = 4;
+  for (int m0 = 0; (int64_t)m0 * kSampleStride * kSampleBlock < n; m0 += kU * kBlocksPerStep) {
+    f32x4 v[kU];
+    int ii[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int m = m0 + u * kBlocksPerStep + tid / (kSampleBlock / 4);
+      const int64_t i64 = (int64_t)m * kSampleStride * kSampleBlock + 4 * (tid % (kSampleBlock / 4));
+      ii[u] = i64 < n ? (int)i64 : n;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ii[u] + 3 < n) v[u] = *reinterpret_cast<const f32x4*>(row + ii[u]);
+      else
+        for (int e = 0; ii[u] + e < n && e < 4; ++e) v[u][e] = row[ii[u] + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ii[u] + e < n) {
+          atomicAdd(&sh.hist[score_key(v[u][e]) >> 20], 1u);
+          ++ns;
+        }
+  }
+  int ns_tot;
+  (void)block_excl_scan<kTkWaves>(ns, sh.wave_tot, ns_tot);
+  const int ks = max(1, (int)((int64_t)k * ns_tot / n));
+  find_bin<kTkBins>(sh, ks);
+  const int bs = sh.sel_bin;
+  const uint32_t b_lo = (uint32_t)max(bs - kWindowHalf, 0), b_hi = (uint32_t)min(bs + kWindowHalf, kTkBins - 1);
+  // ---- exact ordered pass: above the window -> A, inside -> candidates;
+  // the next step's scores are loaded while this step is compacted
+  int nA = 0, nC = 0;
+  f32x4 nx[kPerThread / 4];
+  auto fetch = [&](int i) {
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q) {
+      const int b = i + 4 * q;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (b + 3 < n) v = *reinterpret_cast<const f32x4*>(row + b);
+      else
+        for (int e = 0; e < 4; ++e)
+          if (b + e < n) v[e] = row[b + e];
+      nx[q] = v;
+    }
+  };
+  fetch(kPerThread * tid);
+  for (int base = 0; base < n; base += kStep) {
+    const int i = base + kPerThread * tid;
+    uint32_t key[kPerThread];
+    bool ok[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok[4 * q + e] = i + 4 * q + e < n;
+        key[4 * q + e] = score_key(nx[q][e]);
+      }
+    if (base + kStep < n) fetch(i + kStep);
+    int ca = 0, cc = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const uint32_t d = key[e] >> 20;
+      ca += ok[e] && d > b_hi;
+      cc += ok[e] && d >= b_lo && d <= b_hi;
+    }
+    int tot;
+    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);  // <= kStep each
+    int oa = nA + (ex >> 16), oc = nC + (ex & 0xFFFF);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (!ok[e]) continue;
+      const uint32_t d = key[e] >> 20;
+      if (d > b_hi) {
+        if (oa < kMaxTopk) sh.list_a[oa] = i + e;
+        ++oa;
+      } else if (d >= b_lo) {
+        if (oc < kCandCap) {
+          sh.cand_key[oc] = key[e];
+          sh.cand_pos[oc] = i + e;
+        }
+        ++oc;
+      }
+    }
+    nA += tot >> 16;
+    nC += tot & 0xFFFF;
+  }
+  __syncthreads();
+  if (!(nA < k && nA + nC >= k && nC <= kCandCap)) return false;  // uniform: every thread has the totals
+  finish_from_candidates(sh, 0u, nA, nC, k - nA, out, true);
+  return true;
+}
+
 // ---------------------------------------------------------------- one workgroup per row
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __restrict__ q_pos,
                                                               const float* __restrict__ scores,
@@ -251,6 +383,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __r
     return;
   }
   const float* row = scores + (int64_t)t * ld;
+  if (n >= kSampleMinRow && window_select(sh, row, n, k, out)) return;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
   for (int base = 0; base < n; base += kStep) {

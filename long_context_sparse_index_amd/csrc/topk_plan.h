@@ -72,13 +72,14 @@ inline SplitWs split_ws(int T, int max_ctx) {
 }
 
 // Exclusive prefix sum over the workgroup (NW waves) in thread order; the
-// workgroup total goes to `total`.  Contains two barriers.
+// workgroup total goes to `total`.  Contains two LDS barriers (global loads in
+// flight stay in flight).
 template <int NW>
 __device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = wave_inclusive_scan(v);
   if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
+  lds_sync();
   int pre = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -86,7 +87,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total)
     pre += (i < wave) ? x : 0;
     tot += x;
   }
-  __syncthreads();
+  lds_sync();
   total = tot;
   return pre + incl - v;
 }

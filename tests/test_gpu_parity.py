@@ -78,6 +78,18 @@ def test_index_scores_write_only_the_causal_prefix():
 # ------------------------------------------------------------------ top-k (bit-exact)
 def _topk_rows(kind, n_list, seed):
     rng = np.random.default_rng(seed)
+    if kind.startswith("sample_"):
+        # Rows whose every 16th block of 64 scores (the blocks a 1/16 sample of
+        # a long row reads) sits far below or far above the rest: a threshold
+        # estimated from those blocks is wrong, so the exact check must fail
+        # and the full-histogram path must give the result.
+        shift = np.float32(-4.0 if kind == "sample_low" else 4.0)
+        rows = []
+        for n in n_list:
+            r = synth.random_scores(rng, 1, n, "normal")[0]
+            r[(np.arange(n) // 64) % 16 == 0] += shift
+            rows.append(r)
+        return rows
     return [synth.random_scores(rng, 1, n, kind)[0] for n in n_list]
 
 
@@ -87,6 +99,10 @@ TOPK_CASES = {
     "heavy_ties": ("few_values", [2100, 100000], 2048),   # threshold bin overflows LDS -> global passes
     "small_k": ("normal", [5000, 100], 7),
     "k1": ("signed", [1000, 1], 1),
+    "long_rows": ("normal", [65536, 204800, 300001], 2048),   # sampled-window path
+    "long_small_k": ("normal", [70000, 200000], 7),
+    "sample_low": ("sample_low", [100000, 204800], 2048),       # window too low -> full path
+    "sample_high": ("sample_high", [100000, 204800], 2048),     # window too high -> full path
 }
 
 
