@@ -11,6 +11,7 @@ Prints one JSON line.  Run `python bench.py --help` for options.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -65,6 +66,22 @@ def algorithmic(inp):
         "attn_flops": 139264 * n_kept,
         "flops": 8192 * n_scan + 139264 * n_kept + 2 * 64 * 512 * (192 + 256) * T,
     }
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch recorded with rocprofv3 counters under profiles/
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy-kernel calibration), or None
+    when the kernel's sources have changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def time_calls(fn, steps, warmup):
@@ -198,7 +215,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": DECODE, "sequences": 8, "ctx": 204800, "queries": T, "index_topk": TOPK},
         "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic("idx_scan_kernel_hbm_traffic_decode_b8_ctx204k.json"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+                     "algorithmic_bytes": alg["scan_bytes"]},
         "whole_step": {"algorithmic_bytes": alg["bytes"],
                        "hbm_frac": alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "ops_ms": ops,
