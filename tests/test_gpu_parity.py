@@ -287,6 +287,9 @@ FULL = {
     "decode_b32_ctx32k": [0, 31],
     "decode_b8_ctx204k": [0, 5],
     "prefill_chunk4096_ctx131k": [0, 2047, 4095],
+    # every query of one 65,536-token sequence (16 GEMM chunks of 4,096 in one call); queries
+    # below position 2048 keep all earlier tokens, later ones their top-2048 of a planted row
+    "causal_prefill_65k_planted": [0, 1, 2046, 2047, 2048, 4095, 30001, 65535],
 }
 
 
