@@ -41,7 +41,7 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {
   int T, k, splits, keys_per_split;
-  size_t q_lat_off, o_lat_off, part_off, ml_off, total;
+  size_t q_lat_off, o_lat_off, part_off, ml_off, wuvt_off, total;
 };
 MlaPlan plan_mla(int T, int k);
 hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,

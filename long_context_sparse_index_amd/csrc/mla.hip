@@ -21,18 +21,20 @@
 namespace dsa {
 
 // ---------------------------------------------------------------- absorb
-// grid (64 heads, 4 blocks of 128 latent columns, query groups); wave w owns
-// 32 latent columns (absorb_wave) and walks up to kAbsorbTilesPerWg 32-query
-// tiles.
+// grid (64 heads, query groups of kAbsorbTilesPerWg 32-query tiles); 16 waves
+// cover the 512 latent columns (absorb_wave, 32 each), so the q_nope tile of
+// a step is fetched once per workgroup and shared by its waves through L1.
 constexpr int kAbsorbTilesPerWg = 8;
 
-__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
-                                                     const uint16_t* __restrict__ w_uk,
-                                                     uint16_t* __restrict__ q_lat, int T) {
+__global__ __launch_bounds__(1024) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                      const uint16_t* __restrict__ w_uk,
+                                                      uint16_t* __restrict__ q_lat, int T) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[16][kAbsorbStage];
   const int ntb = (T + 31) / 32;
-  const int tb0 = blockIdx.z * kAbsorbTilesPerWg;
-  absorb_wave(q_nope, w_uk, q_lat, T, blockIdx.x, blockIdx.y * 128 + (threadIdx.x >> 6) * 32, tb0,
-              min(ntb, tb0 + kAbsorbTilesPerWg));
+  const int tb0 = blockIdx.y * kAbsorbTilesPerWg;
+  const int wave = threadIdx.x >> 6;
+  absorb_wave(q_nope, w_uk, q_lat, T, blockIdx.x, wave * 32, tb0, min(ntb, tb0 + kAbsorbTilesPerWg),
+              stage[wave]);
 }
 
 // ---------------------------------------------------------------- core
@@ -429,6 +431,118 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- upproj, many queries
+// W_UV[h] is [c][e] with e contiguous, while MFMA operands take 8 consecutive
+// c per lane.  For large batches the weights are transposed once per call into
+// the workspace (W_UVt [64][256 e][512 c], 16.8 MB), and 8 waves per (head,
+// group of 32-query tiles) each keep the W_UVt fragments of 32 output dims
+// resident (32 K-steps) while the o_lat rows of a tile, read by all 8 waves,
+// come through L1.  Output blocks (32 queries x 32 dims) are staged in LDS and
+// written as whole 16-byte pieces of output rows.
+constexpr int kUpTMin = 256;        // batches from this size use the transposed path
+constexpr int kUpTilesPerWg = 8;
+constexpr int kUpStageRow = 36;     // fp32 per staged row (32 + pad)
+
+__global__ __launch_bounds__(256) void wuv_transpose_kernel(const uint16_t* __restrict__ w_uv,
+                                                            uint16_t* __restrict__ w_uvt) {
+  // grid (64 heads, 8 blocks of 64 c, 4 blocks of 64 e): one 64 x 64 tile via LDS
+  __shared__ uint16_t tile[64][66];
+  const int h = blockIdx.x, c0 = blockIdx.y * 64, e0 = blockIdx.z * 64, tid = threadIdx.x;
+  const int r = tid >> 2, q = tid & 3;  // row of the tile, 16-element quarter
+  {
+    const uint16_t* src = w_uv + ((int64_t)h * kLat + c0 + r) * kV + e0 + 16 * q;
+    const u32x4 v0 = ld16(src), v1 = ld16(src + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[r][16 * q + 2 * i] = (uint16_t)(v0[i] & 0xFFFFu);
+      tile[r][16 * q + 2 * i + 1] = (uint16_t)(v0[i] >> 16);
+      tile[r][16 * q + 8 + 2 * i] = (uint16_t)(v1[i] & 0xFFFFu);
+      tile[r][16 * q + 8 + 2 * i + 1] = (uint16_t)(v1[i] >> 16);
+    }
+  }
+  __syncthreads();
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = (uint32_t)tile[16 * q + 2 * i][r] | ((uint32_t)tile[16 * q + 2 * i + 1][r] << 16);
+    o1[i] = (uint32_t)tile[16 * q + 8 + 2 * i][r] | ((uint32_t)tile[16 * q + 8 + 2 * i + 1][r] << 16);
+  }
+  uint16_t* dst = w_uvt + ((int64_t)h * kV + e0 + r) * kLat + c0 + 16 * q;
+  st16(dst, o0);
+  st16(dst + 8, o1);
+}
+
+__global__ __launch_bounds__(512) void upproj_t_kernel(const uint16_t* __restrict__ o_lat,
+                                                       const uint16_t* __restrict__ w_uvt,
+                                                       void* __restrict__ out, int out_f32, int T) {
+  __shared__ __attribute__((aligned(16))) float stage[8][32 * kUpStageRow];
+  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int e0 = wave * 32;
+  bf16x8 bw[kLat / 16];
+  const uint16_t* bp = w_uvt + ((int64_t)h * kV + e0 + n) * kLat + 8 * g;
+#pragma unroll
+  for (int j = 0; j < kLat / 16; ++j) bw[j] = as_bf16x8(ld16(bp + 16 * j));
+  const int ntb = (T + 31) / 32;
+  const int tb0 = blockIdx.y * kUpTilesPerWg, tb1 = min(ntb, tb0 + kUpTilesPerWg);
+  float* st = stage[wave];
+  // A operand in groups of 8 K-steps; the next group (of this tile or of the
+  // next tile) loads while the current group's MFMAs run
+  auto load_grp = [&](int tb, int j0, bf16x8* a) {
+    const int t = min(tb * 32 + n, T - 1);
+    const uint16_t* ap = o_lat + ((int64_t)t * kHeads + h) * kLat + 8 * g + 16 * j0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = as_bf16x8(ld16(ap + 16 * j));
+  };
+  bf16x8 a[8], an[8];
+  if (tb0 < tb1) load_grp(tb0, 0, a);
+  for (int tb = tb0; tb < tb1; ++tb) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int j0 = 0; j0 < kLat / 16; j0 += 8) {
+      if (j0 + 8 < kLat / 16) load_grp(tb, j0 + 8, an);
+      else if (tb + 1 < tb1) load_grp(tb + 1, 0, an);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = mfma32(a[j], bw[j0 + j], acc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = an[j];
+    }
+    // element r of lane (g, n): query row 8(r/4) + 4g + r%4 of the tile, output dim e0 + n
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[(8 * (r >> 2) + 4 * g + (r & 3)) * kUpStageRow + n] = acc[r];
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int row = lane >> 1, half = lane & 1;  // lane writes 16 dims of one row
+    const int tr = tb * 32 + row;
+    const float* sp = st + row * kUpStageRow + 16 * half;
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(sp + 4 * i);
+    if (tr < T) {
+      const int64_t o = ((int64_t)tr * kHeads + h) * kV + e0 + 16 * half;
+      if (out_f32) {
+        float* dst = reinterpret_cast<float*>(out) + o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 4 * i) = v[i];
+      } else {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+        u32x4 p0, p1;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          p0[2 * i] = pack_bf16x2(v[i][0], v[i][1]);
+          p0[2 * i + 1] = pack_bf16x2(v[i][2], v[i][3]);
+          p1[2 * i] = pack_bf16x2(v[2 + i][0], v[2 + i][1]);
+          p1[2 * i + 1] = pack_bf16x2(v[2 + i][2], v[2 + i][3]);
+        }
+        st16(dst, p0);
+        st16(dst + 8, p1);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile's writes
+  }
+}
+
 // ---------------------------------------------------------------- plan + launch
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -456,6 +570,10 @@ MlaPlan plan_mla(int T, int k) {
     p.ml_off = end;
     end += align_up((size_t)T * p.splits * kHeads * 2 * sizeof(float), 256);
   }
+  if (T >= kUpTMin) {
+    p.wuvt_off = end;
+    end += align_up((size_t)kHeads * kV * kLat * sizeof(uint16_t), 256);
+  }
   p.total = end;
   return p;
 }
@@ -473,8 +591,8 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   const int ntb = (T + 31) / 32;
   hipError_t e;
   if (!q_lat_ready) {
-    absorb_kernel<<<dim3(kHeads, kLat / 128, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 256, 0,
-                    st>>>(q_nope, w_uk, q_lat, T);
+    absorb_kernel<<<dim3(kHeads, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 1024, 0, st>>>(
+        q_nope, w_uk, q_lat, T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -488,6 +606,15 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     mla_merge_kernel<<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (T >= kUpTMin) {
+    uint16_t* w_uvt = reinterpret_cast<uint16_t*>(base + p.wuvt_off);
+    wuv_transpose_kernel<<<dim3(kHeads, kLat / 64, kV / 64), 256, 0, st>>>(w_uv, w_uvt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    upproj_t_kernel<<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
+        o_lat, w_uvt, out, out_f32, T);
+    return hipGetLastError();
   }
   upproj_kernel<<<dim3(kHeads, kV / kUpEB, (T + 32 * kUpMT - 1) / (32 * kUpMT)), 256, 0, st>>>(
       o_lat, w_uv, out, out_f32, T);

@@ -45,7 +45,7 @@ struct TkShared {
   uint32_t hist[kTkBins];
   int wave_tot[kTkWaves];
   int sel_bin, sel_above;
-  uint32_t cand_key[kCandCap];
+  alignas(16) uint32_t cand_key[kCandCap];  // 16-aligned: also staging for the absorb workgroups
   int cand_pos[kCandCap];
   int list_a[kMaxTopk];
   int list_c[kMaxTopk];
@@ -681,8 +681,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
                                                                  SplitWs w, int T, AbsorbJob ab) {
   __shared__ TkShared sh;
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (t >= T) {
-    absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, (tid >> 6) * 32, 0, (T + 31) / 32);
+  if (t >= T) {  // the top-k LDS of this workgroup is free: per-wave staging for the absorption
+    uint16_t* stage = reinterpret_cast<uint16_t*>(sh.cand_key) + (tid >> 6) * kAbsorbStage;
+    absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, (tid >> 6) * 32, 0, (T + 31) / 32, stage);
     return;
   }
   const char* base = ws + (size_t)t * w.per_query;
