@@ -34,7 +34,7 @@
 
 namespace dsa {
 
-constexpr int kTkThreads = 1024;
+constexpr int kTkThreads = 512;  // two row workgroups fit a CU (LDS ~74 KB each)
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kPerThread = 16;                   // scores per thread per pass step
 constexpr int kStep = kPerThread * kTkThreads;   // scores per pass step
@@ -258,8 +258,8 @@ __device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t 
 // ---------------------------------------------------------------- sampled window
 // Long rows: the top-digit histogram of a 1/16 sample of the row (every 16th
 // block of 64 scores) locates the bin of the k-th largest score; one exact
-// ordered pass then keeps everything above a window of bins around it
-// (list A) and collects the window's scores as candidates.  The pass checks
+// ordered pass then keeps everything above a window of one to three bins
+// around it (list A) and collects the window's scores as candidates.  The pass checks
 // that the k-th largest lies inside the window (A holds fewer than k, A plus
 // the window at least k, the candidates fit); then the candidates are
 // resolved as usual and the result is the same as the full histogram path's.
@@ -267,7 +267,6 @@ __device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t 
 constexpr int kSampleMinRow = 65536;
 constexpr int kSampleBlock = 64;    // scores per sampled block
 constexpr int kSampleStride = 16;   // one block in 16 is sampled
-constexpr int kWindowHalf = 1;      // window = sample bin +- this many bins
 
 __device__ bool window_select(TkShared& sh, const float* row, int n, int k, int32_t* out) {
   const int tid = threadIdx.x;
@@ -305,7 +304,14 @@ __device__ bool window_select(TkShared& sh, const float* row, int n, int k, int3
   const int ks = max(1, (int)((int64_t)k * ns_tot / n));
   find_bin<kTkBins>(sh, ks);
   const int bs = sh.sel_bin;
-  const uint32_t b_lo = (uint32_t)max(bs - kWindowHalf, 0), b_hi = (uint32_t)min(bs + kWindowHalf, kTkBins - 1);
+  // The sample's threshold sits at rank r of the ins sampled scores of bin bs,
+  // below `above` sampled scores of higher bins.  A neighbouring bin joins the
+  // window only when the threshold lies within ~3 sampling deviations of that
+  // edge (sampled counts of the row vary by about the square root).
+  const int above = sh.sel_above, ins = (int)sh.hist[bs], r = ks - above;
+  const float margin = 3.f * sqrtf((float)max(above, 1)) + 2.f;
+  const uint32_t b_hi = (uint32_t)min(bs + ((float)r <= margin ? 1 : 0), kTkBins - 1);
+  const uint32_t b_lo = (uint32_t)max(bs - ((float)(ins - r) < margin ? 1 : 0), 0);
   // ---- exact ordered pass: above the window -> A, inside -> candidates;
   // the next step's scores are loaded while this step is compacted
   int nA = 0, nC = 0;
@@ -671,8 +677,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
 
 // Kernel 3 (grid T, plus 64 workgroups when an absorb job rides along): load
 // list A and the candidates, resolve the lower digits, merge into the output.
-// Workgroup T + h, if launched, computes q_lat of head h for every query (16
-// waves x 32 latent columns) on CUs the T row workgroups leave idle.
+// Workgroup T + h, if launched, computes q_lat of head h for every query (each
+// wave two or more blocks of 32 latent columns) on CUs the T row workgroups
+// leave idle.
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* __restrict__ q_pos,
                                                                  const float* __restrict__ scores,
                                                                  int64_t ld, int k,
@@ -682,8 +689,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   __shared__ TkShared sh;
   const int t = blockIdx.x, tid = threadIdx.x;
   if (t >= T) {  // the top-k LDS of this workgroup is free: per-wave staging for the absorption
+    static_assert(kTkWaves * kAbsorbStage * sizeof(uint16_t) <= sizeof(sh.cand_key), "absorb staging");
     uint16_t* stage = reinterpret_cast<uint16_t*>(sh.cand_key) + (tid >> 6) * kAbsorbStage;
-    absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, (tid >> 6) * 32, 0, (T + 31) / 32, stage);
+    for (int c0 = (tid >> 6) * 32; c0 < kLat; c0 += kTkWaves * 32)
+      absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, c0, 0, (T + 31) / 32, stage);
     return;
   }
   const char* base = ws + (size_t)t * w.per_query;

@@ -17,7 +17,7 @@ namespace dsa {
 
 constexpr int kScanTile = 128;   // keys per scan tile and slice granularity
 constexpr int kTkBins = 4096;    // top-digit bins
-constexpr int kCandCap = 12288;  // candidates of the threshold bin kept in LDS
+constexpr int kCandCap = 5120;   // candidates of the threshold bin(s) kept in LDS
 constexpr int kSplitRows = 128;  // batches with fewer rows use the split top-k
 constexpr int kMaxSlices = 1024; // slices per row
 constexpr int kScanSlots = 512;  // resident key-scan workgroups (two per CU)
