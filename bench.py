@@ -5,7 +5,8 @@ seeded synthetic inputs that are already resident in HBM:
   * headline: long decode, 8 sequences x 204,800 cached tokens, one query each
     (value = decode queries/s);
   * also reported: a prefill chunk of 4,096 queries at positions
-    200,704..204,799 of one 204,800-token sequence (query-tokens/s).
+    200,704..204,799 of one 204,800-token sequence (query-tokens/s), and an
+    IndexShare group of 4 decode layers (one selects, three reuse).
 Prints one JSON line.  Run `python bench.py --help` for options.
 """
 from __future__ import annotations
@@ -136,6 +137,56 @@ def run_workload(name, steps, warmup, with_ops=True):
     return inp, ms, ops
 
 
+def index_share_group(inp, steps, warmup, freq=4):
+    """IndexShare on the decode workload: one group of `freq` layers, the first
+    running the whole path and keeping its selection, the other freq-1 running
+    sparse MLA alone on their own caches at those positions.  The shared
+    layers' caches, queries and weights are drawn on the device from a seeded
+    generator (same distributions as the synthetic recipe)."""
+    batch, d = to_device(inp)
+    T = batch.T
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4099)
+    rows = d["kv"].shape[0]
+
+    def normal_bf16(shape, scale=1.0):
+        return (torch.randn(shape, generator=g, device="cuda") * scale).to(torch.bfloat16)
+
+    shared = []
+    for _ in range(freq - 1):
+        shared.append({"kv": normal_bf16((rows, 576)), "q_nope": normal_bf16((T, 64, 192)),
+                       "q_rope": normal_bf16((T, 64, 64)), "w_uk": normal_bf16((64, 512, 192), 512 ** -0.5),
+                       "w_uv": normal_bf16((64, 512, 256), 512 ** -0.5),
+                       "out": torch.empty((T, 64, 256), dtype=torch.bfloat16, device="cuda")})
+    out = torch.empty((T, 64, 256), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, TOPK), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.OP_FORWARD, T, batch.max_ctx, TOPK), dtype=torch.uint8,
+                     device="cuda")
+    mla_ws = torch.empty(max(dsa.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, T, batch.max_ctx, TOPK), 256),
+                         dtype=torch.uint8, device="cuda")
+
+    def group():
+        dsa.dsa_forward(batch, d["q_idx"], d["w"], d["k_idx"], d["q_nope"], d["q_rope"], d["kv"], d["w_uk"],
+                        d["w_uv"], k=TOPK, out=out, idx=idx, ws=ws)
+        for L in shared:
+            dsa.dsa_sparse_mla_attn(batch, L["q_nope"], L["q_rope"], L["kv"], L["w_uk"], L["w_uv"], idx,
+                                    out=L["out"], ws=mla_ws)
+
+    log(f"[bench] index share: timing {steps} groups of {freq} layers")
+    ms = time_calls(group, steps, warmup)
+    alg = algorithmic(inp)
+    n_kept = int(np.minimum(inp.q_pos.astype(np.int64) + 1, TOPK).sum())
+    shared_bytes = 1152 * n_kept + (64 * 192 * 2 + 64 * 64 * 2 + 64 * 256 * 2) * T + 64 * 512 * (192 + 256) * 2
+    group_bytes = alg["bytes"] + (freq - 1) * shared_bytes
+    log(f"[bench] index share: {ms:.3f} ms per group")
+    return {"workload": DECODE, "layers_per_group": freq,
+            "schedule": f"1 full layer (indexer + top-k + sparse MLA) + {freq - 1} shared (sparse MLA on the "
+                        "full layer's selection)",
+            "value": T * freq / (ms * 1e-3), "unit": "decode query-layers/s", "ms_per_group": ms,
+            "ms_per_layer": ms / freq, "algorithmic_bytes_per_group": group_bytes,
+            "hbm_frac": group_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle as it stands (numpy fp64), on a bounded sample of queries."""
     from oracle import dsa_oracle as O
@@ -162,6 +213,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--no-index-share", action="store_true", help="skip the IndexShare layer-group measurement")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill chunk (prints no result line)")
     ap.add_argument("--no-ops", action="store_true", help="profiling aid: skip the per-op timing loops")
@@ -223,6 +275,9 @@ def main():
                        "hbm_frac": alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "ops_ms": ops,
     }
+    if not args.no_index_share:
+        result["index_share"] = index_share_group(inp, args.steps, args.warmup)
+        torch.cuda.empty_cache()
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     del inp

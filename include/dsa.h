@@ -161,6 +161,29 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * IndexShare layer schedule (page 5, IndexShare section and the config fields
+ * it lists: index_topk_freq 4, 78 layers of which the first 3 are dense, 21
+ * layers with their own indexer and 57 that reuse one).  Host-only; writes
+ * source[l] for l < num_layers (HOST array):
+ *   source[l] == l  -> layer l runs its own indexer + top-k ("full": dsa_forward
+ *                      with idx_out),
+ *   source[l] <  l  -> layer l reuses the selection of full layer source[l]
+ *                      ("shared": dsa_sparse_mla_attn on its own cache and
+ *                      weights with that layer's idx).
+ * Layers 0 .. num_dense-1 are full; the sparse layers after them form runs of
+ * index_topk_freq consecutive layers whose last layer is full, and a shared
+ * layer reuses the nearest full layer before it (a layer can only reuse a
+ * selection that was computed earlier in the forward pass).  With
+ * (78, 3, 4): full layers 0,1,2,6,10,...,74 (21), shared 3-5,7-9,...,75-77
+ * (57).  index_topk_freq == 1 makes every layer full (DSA without sharing).
+ * Errors: DSA_ERR_NULL (source NULL), DSA_ERR_SHAPE (num_layers < 1,
+ * num_dense < 1 or > num_layers, index_topk_freq < 1).  Nothing is written on
+ * error.
+ */
+dsa_status dsa_index_share_schedule(int32_t num_layers, int32_t num_dense, int32_t index_topk_freq,
+                                    int32_t* source);
+
 /* Workspace bytes an op needs for num_queries queries (host only; 0 = none).
  * Returns 0 as well for invalid arguments (then the op itself reports them). */
 size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int32_t k);

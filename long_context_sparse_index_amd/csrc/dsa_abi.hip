@@ -139,6 +139,24 @@ size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int
   }
 }
 
+dsa_status dsa_index_share_schedule(int32_t num_layers, int32_t num_dense, int32_t index_topk_freq,
+                                    int32_t* source) {
+  if (!source) return DSA_ERR_NULL;
+  if (num_layers < 1 || num_dense < 1 || num_dense > num_layers || index_topk_freq < 1)
+    return DSA_ERR_SHAPE;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (l < num_dense) {
+      source[l] = l;
+      continue;
+    }
+    // Place of l in its run of index_topk_freq sparse layers; the run's last
+    // layer is full, the others reuse the full layer just before the run.
+    const int32_t r = (l - num_dense) % index_topk_freq;
+    source[l] = r == index_topk_freq - 1 ? l : l - r - 1;
+  }
+  return DSA_OK;
+}
+
 dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
                             const dsa_bf16* k_idx, float* scores, int64_t ld_scores,
                             void* stream) {

@@ -56,6 +56,7 @@ _SIGS = {
                              _P, ctypes.c_int32, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "dsa_forward": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                      _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "dsa_index_share_schedule": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P], ctypes.c_int),
     "dsa_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], ctypes.c_size_t),
     "dsa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "dsa_abi_version": ([], ctypes.c_int32),
@@ -135,6 +136,15 @@ def score_ld(max_ctx: int) -> int:
 
 def dsa_workspace_bytes(op: int, num_queries: int, max_ctx: int, k: int) -> int:
     return int(lib().dsa_workspace_bytes(op, num_queries, max_ctx, k))
+
+
+def dsa_index_share_schedule(num_layers: int = 78, num_dense: int = 3, index_topk_freq: int = 4) -> list:
+    """IndexShare schedule: source[l] == l for a layer that runs its own indexer
+    and top-k, else the earlier full layer whose selection layer l reuses."""
+    src = (ctypes.c_int32 * max(num_layers, 1))()
+    _check("dsa_index_share_schedule",
+           lib().dsa_index_share_schedule(num_layers, num_dense, index_topk_freq, src))
+    return list(src[:num_layers])
 
 
 def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tensor] = None) -> torch.Tensor:

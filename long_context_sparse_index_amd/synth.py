@@ -176,6 +176,30 @@ def make_inputs(wl: Workload, with_queries: bool = True) -> Inputs:
                   w_uk, w_uv, planted)
 
 
+def make_layer_stack(wl: Workload, num_layers: int) -> List[Inputs]:
+    """Inputs of ``num_layers`` layers over one batch geometry: layer l draws
+    everything of ``make_inputs`` from ``default_rng(wl.seed + 7919 * l)``
+    (own caches, queries and weights per layer)."""
+    return [make_inputs(dataclasses.replace(wl, seed=wl.seed + 7919 * l)) for l in range(num_layers)]
+
+
+def derive_layer(inp: Inputs, seed: int) -> Inputs:
+    """Another layer over the same batch, cheap to draw at full size: fresh
+    q_nope, q_rope, W_UK, W_UV (distributions as above, drawn in that order
+    from ``default_rng(seed)``), the latent cache of ``inp`` moved down one row
+    (row r holds row r-1 of ``inp``, row 0 the last row), and the indexer
+    arrays of ``inp`` (a layer that reuses another's selection reads none)."""
+    rng = np.random.default_rng(seed)
+    t = inp.q_nope.shape[0]
+    inv_sqrt_lat = float(1.0 / np.sqrt(np.float32(D_LAT)))
+    q_nope = _normal_bf16(rng, (t, HEADS, D_NOPE))
+    q_rope = _normal_bf16(rng, (t, HEADS, D_ROPE))
+    w_uk = _normal_bf16(rng, (HEADS, D_LAT, D_NOPE), inv_sqrt_lat)
+    w_uv = _normal_bf16(rng, (HEADS, D_LAT, D_V), inv_sqrt_lat)
+    return dataclasses.replace(inp, kv=np.roll(inp.kv, 1, axis=0), q_nope=q_nope, q_rope=q_rope,
+                               w_uk=w_uk, w_uv=w_uv)
+
+
 def custom(seq_lens: Sequence[int], queries: Sequence[Tuple[int, int]], seed: int,
            planted_blocks: int = 0, name: str = "custom") -> Inputs:
     return make_inputs(Workload(name, list(seq_lens), list(queries), seed, planted_blocks))

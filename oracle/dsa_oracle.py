@@ -15,7 +15,10 @@ Sources (the pages have no code; every step below is restated from prose):
   [N2]  page "（五）一万亿次点积砍到两千次：DSA 怎么破 N²", sections on the indexer
         (low-dimensional 32x128 dot products over every token), the full DSA
         flow (indexer top-2048, then full Q.K.V, softmax, weighted V over those
-        only) and the cache division of labour (skipped K/V stay cached).
+        only) and the cache division of labour (skipped K/V stay cached); its
+        IndexShare section (one indexer per 4 layers, the group figure, the
+        21 full / 57 shared count) and the config fields listed at its end
+        (index_topk_freq 4, num_hidden_layers 78, 3 dense + 75 sparse).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -25,6 +28,10 @@ design notes of the repository):
   * scores are rounded once to fp32; selection compares fp32 values (so -0.0
     equals +0.0), ties go to the lower position; the kept positions are
     returned ascending and padded with -1 to length k; with n <= k all n are kept.
+  * IndexShare: a shared layer runs no indexer and reuses the selection of
+    the nearest earlier full layer (a forward pass cannot use a later one);
+    the group figure, which pairs layers 3-5 with layer 6, is read with each
+    full layer feeding the three layers after it.
   * MLA over the kept rows with explicit per-head up-projection
     K_nope = c @ W_UK[h], V = c @ W_UV[h]; logits (q_nope.K_nope + q_rope.r)
     times softmax_scale (1/sqrt(192+64) = 1/16 by default); softmax in full.
@@ -196,3 +203,67 @@ def forward(inp, queries: Optional[Iterable[int]] = None, k: int = INDEX_TOPK,
     qs = range(len(inp.q_seq)) if queries is None else list(queries)
     res = [query_forward(inp, t, k, scale, with_output) for t in qs]
     return [r[0] for r in res], [r[1] for r in res], [r[2] for r in res]
+
+
+# ---------------------------------------------------------------- IndexShare
+def index_share_schedule(num_layers: int = 78, num_dense: int = 3, freq: int = 4):
+    """For every layer, the layer whose indexer selection it attends with.
+
+    [N2] IndexShare section: every group of 4 adjacent layers runs the indexer
+    once ("full") and the other 3 reuse it ("shared"); the first dense layers
+    keep their own indexer and join no group; config: 78 layers, 3 dense,
+    index_topk_freq 4, 21 full and 57 shared.  Walking the layers in forward
+    order: a dense layer is full; a sparse layer is full when it completes a
+    run of ``freq`` sparse layers, otherwise it reuses the last full layer seen.
+    Returns a list: entry l is l for a full layer, else its source (< l).
+    """
+    source = []
+    last_full = None
+    sparse_seen = 0
+    for layer in range(num_layers):
+        if layer < num_dense:
+            full = True
+        else:
+            sparse_seen += 1
+            full = sparse_seen % freq == 0
+        if full:
+            last_full = layer
+            source.append(layer)
+        else:
+            if last_full is None:
+                raise ValueError("a shared layer has no earlier full layer")
+            source.append(last_full)
+    return source
+
+
+def layer_stack_forward(layers, schedule, queries: Optional[Iterable[int]] = None,
+                        k: int = INDEX_TOPK, scale: float = DEFAULT_SCALE):
+    """DSA with IndexShare over a stack of layers.
+
+    ``layers[l]`` holds layer l's inputs (as for ``query_forward``: the same
+    batch geometry in every layer; a shared layer's indexer arrays are unused).
+    A full layer selects with its own indexer; a shared layer attends over its
+    own latent cache at the positions its source layer selected ([N2]
+    IndexShare: the shared members take the representative's indices and do
+    not compute their own).  Returns (idx, out): per layer, lists over the
+    queries of int32 [k] and float64 [64,256].
+    """
+    qs = range(len(layers[0].q_seq)) if queries is None else list(queries)
+    idx_of = {}
+    out_all = []
+    idx_all = []
+    for layer, inp in enumerate(layers):
+        src = schedule[layer]
+        if src == layer:
+            idx_of[layer] = [query_forward(inp, t, k, scale, with_output=False)[1] for t in qs]
+        sel = idx_of[src]
+        outs = []
+        for j, t in enumerate(qs):
+            b = int(inp.q_seq[t])
+            r0 = int(inp.seq_row0[b])
+            kept = sel[j][sel[j] >= 0].astype(np.int64)
+            outs.append(mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept],
+                                     inp.w_uk, inp.w_uv, scale))
+        idx_all.append(sel)
+        out_all.append(outs)
+    return idx_all, out_all

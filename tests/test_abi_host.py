@@ -120,3 +120,19 @@ def test_valid_call_without_gpu_reports_device_error(L):
         pytest.skip("a GPU is present; this checks the no-device path")
     b = _batch()
     assert L.dsa_index_scores(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None) == 7
+
+
+def test_index_share_schedule_matches_oracle(L):
+    """Host-only call: the library's IndexShare schedule equals the oracle's
+    for the page's configuration and a sweep of others; bad sizes are rejected."""
+    from oracle import dsa_oracle as O
+    for layers, dense, freq in [(78, 3, 4)] + [(n, d, f) for n in (1, 2, 5, 17, 40) for d in (1, 2, 3)
+                                               for f in (1, 2, 3, 4, 8) if d <= n]:
+        assert dsa.dsa_index_share_schedule(layers, dense, freq) == O.index_share_schedule(layers, dense, freq)
+    src = (ctypes.c_int32 * 4)(-7, -7, -7, -7)
+    assert L.dsa_index_share_schedule(4, 1, 2, None) == 1
+    assert L.dsa_index_share_schedule(0, 1, 2, src) == 2
+    assert L.dsa_index_share_schedule(4, 0, 2, src) == 2
+    assert L.dsa_index_share_schedule(4, 5, 2, src) == 2
+    assert L.dsa_index_share_schedule(4, 1, 0, src) == 2
+    assert list(src) == [-7] * 4  # nothing written on error

@@ -166,7 +166,12 @@ def _sdpa_reference(inp, t):
     """Dense causal attention by torch's SDPA in fp64 with explicitly up-projected K/V."""
     b, p = int(inp.q_seq[t]), int(inp.q_pos[t])
     r0 = int(inp.seq_row0[b])
-    rows = torch.from_numpy(synth.bf16_to_f32(inp.kv[r0: r0 + p + 1]).astype(np.float64))
+    return _sdpa_rows(inp, t, inp.kv[r0: r0 + p + 1])
+
+
+def _sdpa_rows(inp, t, kv_rows):
+    """torch SDPA (fp64) of query t over the given cache rows, K/V up-projected."""
+    rows = torch.from_numpy(synth.bf16_to_f32(kv_rows).astype(np.float64))
     c, r = rows[:, :512], rows[:, 512:]
     wuk = torch.from_numpy(synth.bf16_to_f32(inp.w_uk).astype(np.float64))
     wuv = torch.from_numpy(synth.bf16_to_f32(inp.w_uv).astype(np.float64))
@@ -283,3 +288,72 @@ def test_selection_matters_beyond_k():
     inp3 = synth.Inputs(**{**inp.__dict__, "kv": kv3})
     _, _, out3 = O.query_forward(inp3, 0, k=k)
     assert not np.allclose(out, out3)
+
+
+# ------------------------------------------------------------------ IndexShare
+def test_index_share_schedule_page_counts(golden_dir):
+    """The page's own numbers: 78 layers, 3 dense, one indexer per 4 layers ->
+    21 full (dense ones included) and 57 shared; the group figure's first
+    groups."""
+    g = json.load(open(os.path.join(golden_dir, "index_share_schedule.json")))
+    src = O.index_share_schedule(g["num_hidden_layers"], g["dense_layers"], g["index_topk_freq"])
+    assert len(src) == g["num_hidden_layers"]
+    full = [l for l, s in enumerate(src) if s == l]
+    assert len(full) == g["full_layers"]
+    assert len(src) - len(full) == g["shared_layers"]
+    for l in g["dense_layers_with_own_indexer"]:
+        assert src[l] == l
+    for grp in g["first_groups_shared"]:
+        assert all(src[l] != l for l in grp), grp
+    for l in g["first_groups_full"]:
+        assert src[l] == l
+
+
+def test_index_share_schedule_structure():
+    """Invariants any reading must keep: a shared layer reuses an earlier full
+    layer; among the sparse layers, every run of freq consecutive layers runs
+    the indexer exactly once; freq 1 is DSA without sharing."""
+    for layers, dense, freq in [(78, 3, 4), (40, 1, 3), (9, 2, 7), (12, 12, 4), (30, 5, 2)]:
+        src = O.index_share_schedule(layers, dense, freq)
+        for l, s in enumerate(src):
+            assert s <= l and src[s] == s
+        full = [src[l] == l for l in range(dense, layers)]
+        for i in range(len(full) - freq + 1):
+            assert sum(full[i:i + freq]) == 1, (layers, dense, freq, i)
+        assert O.index_share_schedule(layers, dense, 1) == list(range(layers))
+
+
+def _stack(n_layers, seed):
+    wl = synth.Workload("stack", [300, 180], [(0, 299), (1, 150), (0, 40)], seed)
+    return synth.make_layer_stack(wl, n_layers)
+
+
+def test_layer_stack_without_sharing_is_per_layer_dsa():
+    """freq 1: every layer is plain DSA on its own inputs."""
+    layers = _stack(3, 21)
+    idx, out = O.layer_stack_forward(layers, [0, 1, 2], k=64)
+    for l, inp in enumerate(layers):
+        _, ref_idx, ref_out = O.forward(inp, k=64)
+        for t in range(3):
+            assert idx[l][t].tolist() == ref_idx[t].tolist()
+            np.testing.assert_array_equal(out[l][t], ref_out[t])
+
+
+def test_layer_stack_shared_layer_reuses_source_selection():
+    """A shared layer attends with its source's positions, not its own
+    indexer's, over its own cache; given its source's inputs it reproduces the
+    source's output exactly."""
+    layers = _stack(3, 22)
+    layers[2] = layers[0]
+    idx, out = O.layer_stack_forward(layers, [0, 0, 0], k=64)
+    for t in range(3):
+        assert idx[1][t].tolist() == idx[0][t].tolist()
+        np.testing.assert_array_equal(out[2][t], out[0][t])
+        if int(layers[1].q_pos[t]) + 1 > 64:  # (shorter histories keep every position)
+            own = O.query_forward(layers[1], t, k=64)[1]
+            assert own.tolist() != idx[1][t].tolist()  # its own indexer would select otherwise
+        inp = layers[1]
+        r0 = int(inp.seq_row0[int(inp.q_seq[t])])
+        kept = idx[0][t][idx[0][t] >= 0].astype(np.int64)
+        dense_sub = _sdpa_rows(inp, t, inp.kv[r0 + kept])
+        np.testing.assert_allclose(out[1][t], dense_sub, rtol=1e-10, atol=1e-12)
