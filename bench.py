@@ -99,7 +99,7 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms
 
 
-def run_workload(name, steps, warmup, with_ops=True):
+def run_workload(name, steps, warmup, with_ops=True, extra_k=()):
     log(f"[bench] {name}: generating inputs")
     t0 = time.time()
     inp = synth.make_inputs(synth.workload(name))
@@ -118,9 +118,23 @@ def run_workload(name, steps, warmup, with_ops=True):
     log(f"[bench] {name}: timing {steps} steps after {warmup} warmup")
     torch.cuda.synchronize()
     ms = time_calls(step, steps, warmup)
+    # index_topk as a runtime parameter: the same resident inputs with larger k
+    by_k = {}
+    for k in extra_k:
+        idx_k = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        ws_k = torch.empty(dsa.dsa_workspace_bytes(dsa.OP_FORWARD, T, batch.max_ctx, k), dtype=torch.uint8,
+                           device="cuda")
+
+        def step_k():
+            dsa.dsa_forward(batch, d["q_idx"], d["w"], d["k_idx"], d["q_nope"], d["q_rope"], d["kv"], d["w_uk"],
+                            d["w_uv"], k=k, out=out, idx=idx_k, ws=ws_k)
+
+        by_k[k] = time_calls(step_k, steps, warmup)
+        log(f"[bench] {name}: k={k} {by_k[k]:.3f} ms/step")
+        del idx_k, ws_k
     if not with_ops:
         log(f"[bench] {name}: {ms:.3f} ms/step")
-        return inp, ms, {}
+        return inp, ms, {}, by_k
     # per-op breakdown: each ABI call below launches that op's kernels only
     scores = torch.empty((T, dsa.score_ld(batch.max_ctx)), dtype=torch.float32, device="cuda")
     mla_ws = torch.empty(max(dsa.dsa_workspace_bytes(dsa.OP_SPARSE_MLA, T, batch.max_ctx, TOPK), 256),
@@ -134,7 +148,7 @@ def run_workload(name, steps, warmup, with_ops=True):
                                  steps, warmup),
     }
     log(f"[bench] {name}: {ms:.3f} ms/step; ops(ms) " + ", ".join(f"{k}={v:.3f}" for k, v in ops.items()))
-    return inp, ms, ops
+    return inp, ms, ops, by_k
 
 
 def index_share_group(inp, steps, warmup, freq=4):
@@ -214,6 +228,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-index-share", action="store_true", help="skip the IndexShare layer-group measurement")
+    ap.add_argument("--no-topk-variants", action="store_true",
+                    help="skip the index_topk 4096/8192 measurements (decode) and 8192 (prefill)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill chunk (prints no result line)")
     ap.add_argument("--no-ops", action="store_true", help="profiling aid: skip the per-op timing loops")
@@ -240,14 +256,15 @@ def main():
         log("[bench] copied 1 GiB 3 times")
         return
     dsa.lib()
+    extra_k = () if args.no_topk_variants else (4096, 8192)
     if args.decode_only:
-        run_workload(DECODE, args.steps, args.warmup, not args.no_ops)
+        run_workload(DECODE, args.steps, args.warmup, not args.no_ops, extra_k)
         return
     if args.prefill_only:
-        run_workload(PREFILL, args.steps, args.warmup, not args.no_ops)
+        run_workload(PREFILL, args.steps, args.warmup, not args.no_ops, extra_k[-1:])
         return
 
-    inp, ms, ops = run_workload(DECODE, args.steps, args.warmup)
+    inp, ms, ops, dec_k = run_workload(DECODE, args.steps, args.warmup, extra_k=extra_k)
     alg = algorithmic(inp)
     T = len(inp.q_pos)
     scan_ms = ops["index_scores"]
@@ -274,6 +291,8 @@ def main():
         "whole_step": {"algorithmic_bytes": alg["bytes"],
                        "hbm_frac": alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "ops_ms": ops,
+        "index_topk_variants": {str(k): {"ms_per_step": v, "value": T / (v * 1e-3), "unit": "decode queries/s"}
+                                for k, v in dec_k.items()},
     }
     if not args.no_index_share:
         result["index_share"] = index_share_group(inp, args.steps, args.warmup)
@@ -282,12 +301,15 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     del inp
     if not args.no_prefill:
-        pinp, pms, pops = run_workload(PREFILL, max(3, args.steps // 5), min(args.warmup, 3))
+        pinp, pms, pops, pre_k = run_workload(PREFILL, max(3, args.steps // 5), min(args.warmup, 3),
+                                              extra_k=extra_k[-1:])
         palg = algorithmic(pinp)
         pach = palg["index_flops"] / (pops["index_scores"] * 1e-3) / 1e12
         result["prefill"] = {
             "workload": PREFILL, "value": len(pinp.q_pos) / (pms * 1e-3), "unit": "query-tokens/s",
             "ms_per_step": pms, "ops_ms": pops,
+            "index_topk_variants": {str(k): {"ms_per_step": v, "value": len(pinp.q_pos) / (v * 1e-3),
+                                             "unit": "query-tokens/s"} for k, v in pre_k.items()},
             "mfma_frac_whole_step": palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "idx_gemm_kernel", "achieved": pach,
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pach / MFMA_BF16_PEAK_TFLOPS,

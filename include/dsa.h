@@ -61,7 +61,8 @@ extern "C" {
 #define DSA_V_DIM 256
 #define DSA_LATENT_DIM 512
 #define DSA_KV_ROW 576           /* 512 latent | 64 rope */
-#define DSA_MAX_TOPK 2048        /* index_topk of the page-4 table */
+#define DSA_INDEX_TOPK 2048      /* index_topk of the page-4 table */
+#define DSA_MAX_TOPK 8192        /* largest k (page 4, §2.2 and §6.1, discuss index_topk 4096 and 8192) */
 
 typedef uint16_t dsa_bf16;       /* raw bf16 bits */
 
@@ -117,6 +118,8 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const
  * position order, padded with -1.  Bit-exact: equal inputs give equal outputs.
  * NaN scores are unsupported (unspecified result).
  *   scores [T, ld_scores] fp32 (as above), 1 <= k <= DSA_MAX_TOPK, idx [T,k] int32.
+ *   Any k in range is a runtime choice (DSA_INDEX_TOPK is the tables' value);
+ *   k above 2048 runs one row workgroup per CU instead of two.
  *   ws: NULL, or at least dsa_workspace_bytes(DSA_OP_TOPK, T, max_ctx, k) bytes
  *   (DSA_ERR_WORKSPACE otherwise).  Batches of few rows split each row over
  *   many workgroups when a workspace is given; with NULL every row runs on one

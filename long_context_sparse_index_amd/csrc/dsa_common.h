@@ -15,7 +15,8 @@ constexpr int kQk = kNope + kRope;    // 256
 constexpr int kV = 256;
 constexpr int kLat = 512;
 constexpr int kRow = kLat + kRope;    // 576 bf16 per latent-cache row
-constexpr int kMaxTopk = 2048;
+constexpr int kMaxTopk = 8192;    // largest index_topk accepted
+constexpr int kTopkSmall = 2048;  // index_topk of the configuration tables; kernels specialise up to it
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __shared__ float s_l[2][kHeads];
   __shared__ float s_m[kHeads];
   __shared__ int s_valid[kRing][kKT];
-  __shared__ int s_idx[kMaxTopk + 4 * kKT];  // the split's positions, -1 padded
+  __shared__ int s_idx[kMaxTopk + 4 * kKT];  // the split's positions (<= k), -1 padded
   const int t = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -118,19 +118,23 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // just ahead of the first gathers.  Entries past the split are -1: the loop
   // (unrolled by 3) gathers up to four tiles past its last one.
   {
-    constexpr int kPer = (kMaxTopk + 4 * kKT + kCoreThreads - 1) / kCoreThreads;
-    const int nfill = (ntiles + 4) * kKT;
-    int v[kPer];
+    // batches of kPer loads per thread (one batch covers splits of up to
+    // kTopkSmall positions); all loads of a batch go out before its stores
+    constexpr int kPer = (kTopkSmall + 4 * kKT + kCoreThreads - 1) / kCoreThreads;
+    const int nfill = (ntiles + 4) * kKT;  // <= kMaxTopk + 4 * kKT
+    for (int b0 = 0; b0 < nfill; b0 += kPer * kCoreThreads) {
+      int v[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {  // all loads first, then the stores
-      const int j = tid + u * kCoreThreads;
-      const int e = irow[min(j0 + j, k - 1)];  // in-row read, replaced past the split
-      v[u] = j0 + j < j1 ? e : -1;
-    }
+      for (int u = 0; u < kPer; ++u) {
+        const int j = b0 + tid + u * kCoreThreads;
+        const int e = irow[min(j0 + j, k - 1)];  // in-row read, replaced past the split
+        v[u] = j0 + j < j1 ? e : -1;
+      }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = tid + u * kCoreThreads;
-      if (j < nfill) s_idx[j] = v[u];
+      for (int u = 0; u < kPer; ++u) {
+        const int j = b0 + tid + u * kCoreThreads;
+        if (j < nfill) s_idx[j] = v[u];
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -550,9 +554,12 @@ MlaPlan plan_mla(int T, int k) {
   MlaPlan p{};
   p.T = T;
   p.k = k;
+  // Small batches split each query's keys so that about 256 workgroups run,
+  // with at least 128 keys (4 tiles) per split.
   int s = 1;
   if (T > 0 && T < 256) s = (256 + T - 1) / T;
-  s = s < 16 ? s : 16;
+  const int cap = k / 128 > 16 ? k / 128 : 16;
+  s = s < cap ? s : cap;
   const int max_s = (k + kKT - 1) / kKT;
   s = s < max_s ? s : max_s;
   if (s < 1) s = 1;

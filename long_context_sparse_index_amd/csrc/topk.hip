@@ -34,21 +34,26 @@
 
 namespace dsa {
 
-constexpr int kTkThreads = 512;  // two row workgroups fit a CU (LDS ~74 KB each)
+constexpr int kTkThreads = 512;  // for k <= kTopkSmall two row workgroups fit a CU (LDS ~74 KB each)
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kPerThread = 16;                   // scores per thread per pass step
 constexpr int kStep = kPerThread * kTkThreads;   // scores per pass step
 
 constexpr int kSliceThreads = 256;
 
+// KMAX: the largest k a launch handles.  List A holds fewer than k positions,
+// list C at most min(k, candidates) of them.  With KMAX = kTopkSmall two row
+// workgroups fit a CU; larger k (up to kMaxTopk) runs one per CU.
+template <int KMAX>
 struct TkShared {
+  static constexpr int kListC = KMAX < kCandCap ? KMAX : kCandCap;
   uint32_t hist[kTkBins];
   int wave_tot[kTkWaves];
   int sel_bin, sel_above;
   alignas(16) uint32_t cand_key[kCandCap];  // 16-aligned: also staging for the absorb workgroups
   int cand_pos[kCandCap];
-  int list_a[kMaxTopk];
-  int list_c[kMaxTopk];
+  int list_a[KMAX];
+  int list_c[kListC];
 };
 
 // Finds the bin holding the krem-th largest element (1-based, counting from
@@ -82,8 +87,8 @@ __device__ void find_bin(const uint32_t* hist, int krem, int* wave_tot, int* sel
   }
   lds_sync();
 }
-template <int NBINS>
-__device__ __forceinline__ void find_bin(TkShared& sh, int krem) {
+template <int NBINS, int KMAX>
+__device__ __forceinline__ void find_bin(TkShared<KMAX>& sh, int krem) {
   find_bin<kTkThreads, NBINS>(sh.hist, krem, sh.wave_tot, &sh.sel_bin, &sh.sel_above);
 }
 
@@ -124,7 +129,8 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
 // candidates are kept.  With `window`, the candidates span several top-digit
 // bins and the threshold bin among them is found first; otherwise all of them
 // are in bin b1.
-__device__ void finish_from_candidates(TkShared& sh, uint32_t b1, int above1, int c1, int krem,
+template <int KMAX>
+__device__ void finish_from_candidates(TkShared<KMAX>& sh, uint32_t b1, int above1, int c1, int krem,
                                        int32_t* out, bool window = false) {
   const int tid = threadIdx.x;
   int krem1 = krem;
@@ -191,7 +197,8 @@ __device__ void finish_from_candidates(TkShared& sh, uint32_t b1, int above1, in
 
 // Step 4 (heavy ties): lower digits by passes over the row, then an ordered
 // compaction straight to the output.
-__device__ void finish_from_row(TkShared& sh, const float* row, int n, uint32_t b1, int krem,
+template <int KMAX>
+__device__ void finish_from_row(TkShared<KMAX>& sh, const float* row, int n, uint32_t b1, int krem,
                                 int32_t* out) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
@@ -268,7 +275,8 @@ constexpr int kSampleMinRow = 65536;
 constexpr int kSampleBlock = 64;    // scores per sampled block
 constexpr int kSampleStride = 16;   // one block in 16 is sampled
 
-__device__ bool window_select(TkShared& sh, const float* row, int n, int k, int32_t* out) {
+template <int KMAX>
+__device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k, int32_t* out) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
@@ -356,7 +364,7 @@ __device__ bool window_select(TkShared& sh, const float* row, int n, int k, int3
       if (!ok[e]) continue;
       const uint32_t d = key[e] >> 20;
       if (d > b_hi) {
-        if (oa < kMaxTopk) sh.list_a[oa] = i + e;
+        if (oa < KMAX) sh.list_a[oa] = i + e;
         ++oa;
       } else if (d >= b_lo) {
         if (oc < kCandCap) {
@@ -376,11 +384,12 @@ __device__ bool window_select(TkShared& sh, const float* row, int n, int k, int3
 }
 
 // ---------------------------------------------------------------- one workgroup per row
+template <int KMAX>
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __restrict__ q_pos,
                                                               const float* __restrict__ scores,
                                                               int64_t ld, int k,
                                                               int32_t* __restrict__ idx) {
-  __shared__ TkShared sh;
+  __shared__ TkShared<KMAX> sh;
   const int t = blockIdx.x, tid = threadIdx.x;
   const int n = q_pos[t] + 1;
   int32_t* out = idx + (int64_t)t * k;
@@ -680,13 +689,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
 // Workgroup T + h, if launched, computes q_lat of head h for every query (each
 // wave two or more blocks of 32 latent columns) on CUs the T row workgroups
 // leave idle.
+template <int KMAX>
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* __restrict__ q_pos,
                                                                  const float* __restrict__ scores,
                                                                  int64_t ld, int k,
                                                                  int32_t* __restrict__ idx,
                                                                  const char* __restrict__ ws,
                                                                  SplitWs w, int T, AbsorbJob ab) {
-  __shared__ TkShared sh;
+  __shared__ TkShared<KMAX> sh;
   const int t = blockIdx.x, tid = threadIdx.x;
   if (t >= T) {  // the top-k LDS of this workgroup is free: per-wave staging for the absorption
     static_assert(kTkWaves * kAbsorbStage * sizeof(uint16_t) <= sizeof(sh.cand_key), "absorb staging");
@@ -698,16 +708,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   const char* base = ws + (size_t)t * w.per_query;
   const int* list_a = reinterpret_cast<const int*>(base + w.a_off);
   const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
-  // List A (at most kMaxTopk entries) and the first 2048 candidates are read
-  // together with the header; entries past the counts are stale and unused.
-  constexpr int kSpec = kMaxTopk / kTkThreads;
-  int a_spec[kSpec];
-  u32x2 c_spec[kSpec];
+  // List A (fewer than k <= KMAX entries) and the first kTopkSmall candidates
+  // are read together with the header; entries past the counts are stale and
+  // unused (the workspace holds kMaxTopk entries of A and kCandCap candidates).
+  constexpr int kSpecA = KMAX / kTkThreads;
+  constexpr int kSpecC = kTopkSmall / kTkThreads;
+  int a_spec[kSpecA];
+  u32x2 c_spec[kSpecC];
 #pragma unroll
-  for (int u = 0; u < kSpec; ++u) {
-    a_spec[u] = list_a[tid + u * kTkThreads];
+  for (int u = 0; u < kSpecA; ++u) a_spec[u] = list_a[tid + u * kTkThreads];
+#pragma unroll
+  for (int u = 0; u < kSpecC; ++u)
     c_spec[u] = *reinterpret_cast<const u32x2*>(cand + 2 * (tid + u * kTkThreads));
-  }
   const int n = q_pos[t] + 1;
   int32_t* out = idx + (int64_t)t * k;
   if (n <= k) {
@@ -724,15 +736,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
     return;
   }
 #pragma unroll
-  for (int u = 0; u < kSpec; ++u) {
+  for (int u = 0; u < kSpecA; ++u) {
     const int i = tid + u * kTkThreads;
     if (i < above1) sh.list_a[i] = a_spec[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kSpecC; ++u) {
+    const int i = tid + u * kTkThreads;
     if (i < c1) {
       sh.cand_key[i] = c_spec[u].x;
       sh.cand_pos[i] = (int)c_spec[u].y;
     }
   }
-  for (int j = kMaxTopk + tid; j < c1; j += kTkThreads) {
+  for (int j = kTopkSmall + tid; j < c1; j += kTkThreads) {
     const u32x2 v = *reinterpret_cast<const u32x2*>(cand + 2 * j);
     sh.cand_key[j] = v.x;
     sh.cand_pos[j] = (int)v.y;
@@ -751,8 +767,12 @@ size_t topk_workspace_bytes(int T, int max_ctx) {
 
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
                        void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st) {
+  const bool small = k <= kTopkSmall;
   if (!topk_split(b.T, ws)) {
-    topk_row_kernel<<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
+    if (small)
+      topk_row_kernel<kTopkSmall><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
+    else
+      topk_row_kernel<kMaxTopk><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
     return hipGetLastError();
   }
   const SplitWs w = split_ws(b.T, b.max_ctx);
@@ -761,8 +781,11 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
     topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_slice_select_kernel<<<dim3(b.T, w.S), kSelThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   const AbsorbJob ab = absorb ? *absorb : AbsorbJob{nullptr, nullptr, nullptr};
-  topk_finish_kernel<<<b.T + (absorb ? kHeads : 0), kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w,
-                                                                         b.T, ab);
+  const int grid = b.T + (absorb ? kHeads : 0);
+  if (small)
+    topk_finish_kernel<kTopkSmall><<<grid, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w, b.T, ab);
+  else
+    topk_finish_kernel<kMaxTopk><<<grid, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w, b.T, ab);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so"
 IDX_HEADS, IDX_DIM = 32, 128
 HEADS, D_NOPE, D_ROPE, D_V, D_LAT = 64, 192, 64, 256, 512
 D_KV = D_LAT + D_ROPE
-MAX_TOPK = 2048
+INDEX_TOPK = 2048  # index_topk of the configuration tables (default k)
+MAX_TOPK = 8192    # largest k the library accepts
 DEFAULT_SCALE = 1.0 / 16.0
 
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
@@ -163,7 +164,7 @@ def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tenso
     return scores
 
 
-def dsa_topk(batch: Batch, scores: torch.Tensor, k: int = MAX_TOPK,
+def dsa_topk(batch: Batch, scores: torch.Tensor, k: int = INDEX_TOPK,
              idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Top-k positions [T, k] int32, ascending, -1 padded."""
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
@@ -207,7 +208,7 @@ def dsa_sparse_mla_attn(batch: Batch, q_nope, q_rope, kv, w_uk, w_uv, idx: torch
     return out
 
 
-def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k: int = MAX_TOPK,
+def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k: int = INDEX_TOPK,
                 softmax_scale: float = DEFAULT_SCALE, out_dtype=torch.bfloat16, return_idx: bool = True,
                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 idx: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:

@@ -70,7 +70,7 @@ def test_topk_validation(L):
     b = _batch()
     f = L.dsa_topk
     assert f(ctypes.byref(b), FAKE, 100, 0, FAKE, None, 0, None) == 2
-    assert f(ctypes.byref(b), FAKE, 100, 2049, FAKE, None, 0, None) == 2
+    assert f(ctypes.byref(b), FAKE, 100, 8193, FAKE, None, 0, None) == 2
     assert f(ctypes.byref(b), FAKE, 100, 16, None, None, 0, None) == 1
     assert f(ctypes.byref(b), None, 100, 16, FAKE, None, 0, None) == 1
     assert f(ctypes.byref(_batch(T=0)), FAKE, 100, 16, FAKE, None, 0, None) == 0
@@ -85,7 +85,7 @@ def test_sparse_mla_validation(L):
     assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, FAKE, need - 1, None) == 4   # workspace
     assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 5, FAKE, need, None) == 5       # out dtype
     assert f(ctypes.byref(b), *args, 2048, -1.0, FAKE, 0, FAKE, need, None) == 2         # scale
-    assert f(ctypes.byref(b), *args, 4096, 0.0625, FAKE, 0, FAKE, need, None) == 2       # k
+    assert f(ctypes.byref(b), *args, 8193, 0.0625, FAKE, 0, FAKE, need, None) == 2       # k
     assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, None, need, None) == 1       # ws NULL
     assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, FAKE + 8, need, None) == 3   # ws align
 

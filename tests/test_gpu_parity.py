@@ -103,6 +103,13 @@ TOPK_CASES = {
     "long_small_k": ("normal", [70000, 200000], 7),
     "sample_low": ("sample_low", [100000, 204800], 2048),       # window too low -> full path
     "sample_high": ("sample_high", [100000, 204800], 2048),     # window too high -> full path
+    # index_topk as a runtime parameter above 2048 (kernels with larger LDS lists)
+    "k4096_ragged": ("normal", [1, 4095, 4096, 4097, 9000, 40000], 4096),
+    "k3000_signed": ("signed", [3000, 3001, 70000], 3000),
+    "k8192_ragged": ("normal", [8191, 8192, 8193, 20000, 131071], 8192),
+    "k8192_long": ("normal", [65536, 204800], 8192),
+    "k8192_heavy_ties": ("few_values", [9000, 100000], 8192),
+    "k8192_sample_low": ("sample_low", [204800], 8192),
 }
 
 
@@ -146,7 +153,7 @@ def test_topk_special_values():
     b = dsa.Batch(torch.zeros(T, dtype=torch.int32, device="cuda"),
                   torch.full((T,), n - 1, dtype=torch.int32, device="cuda"),
                   torch.zeros(1, dtype=torch.int64, device="cuda"), n)
-    for k in (1, 2048):
+    for k in (1, 2048, 8192):
         for ws in (None, dsa.NO_WORKSPACE):
             idx = dsa.dsa_topk(b, torch.from_numpy(host).cuda(), k, ws=ws).cpu().numpy()
             for t, x in enumerate(rows):
@@ -155,25 +162,29 @@ def test_topk_special_values():
 
 # ------------------------------------------------------------------ sparse MLA
 MLA_CASES = {
-    "tiny_ref_4k": None,
-    "decode_splits": ([3000, 2100, 5000], [(0, 2999), (1, 2099), (2, 100)]),   # T=3 -> key splits
-    "many_queries_no_split": ([2600], [(0, 2300 + i) for i in range(300)]),       # T=300 -> one split
+    "tiny_ref_4k": (None, 2048),
+    "decode_splits": (([3000, 2100, 5000], [(0, 2999), (1, 2099), (2, 100)]), 2048),   # T=3 -> key splits
+    "many_queries_no_split": (([2600], [(0, 2300 + i) for i in range(300)]), 2048),      # T=300 -> one split
+    # k = 8192: 64 splits of 128 keys for few queries; one split of 8192 keys for many
+    "decode_splits_k8192": (([9000, 12000, 3000], [(0, 8999), (1, 11999), (2, 2999)]), 8192),
+    "many_queries_k8192": (([9000], [(0, 8740 + i) for i in range(260)]), 8192),
 }
 
 
 @pytest.mark.parametrize("case", list(MLA_CASES))
 def test_sparse_mla_matches_oracle_given_oracle_indices(case):
-    _say(f"[sparse_mla] {case}")
-    if MLA_CASES[case] is None:
+    spec, k = MLA_CASES[case]
+    _say(f"[sparse_mla] {case} k={k}")
+    if spec is None:
         inp = synth.make_inputs(synth.workload(case))
     else:
-        lens, qs = MLA_CASES[case]
+        lens, qs = spec
         inp = synth.custom(lens, qs, seed=41)
     T = len(inp.q_pos)
     sample = list(range(T)) if T <= 16 else [0, 1, T // 2, T - 1]
-    idx = np.full((T, 2048), -1, np.int32)
+    idx = np.full((T, k), -1, np.int32)
     for t in range(T):
-        idx[t] = O.topk_select(_oracle_scores(inp, t), 2048)
+        idx[t] = O.topk_select(_oracle_scores(inp, t), k)
     d = to_device(inp)
     out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv,
                                   torch.from_numpy(idx).cuda(), out_dtype=torch.float32)
@@ -245,6 +256,25 @@ def test_forward_small_contexts_equal_dense_attention():
         assert np.array_equal(idx[t, : p + 1], np.arange(p + 1)) and np.all(idx[t, p + 1:] == -1)
 
 
+E2E_K_CASES = {
+    # few queries: split top-k (absorption on its spare workgroups), key-split MLA;
+    # the 70,000-token row takes the sampled-window top-k
+    "decode": ([10000, 20000, 70000, 5000], [(0, 9999), (1, 19999), (2, 69999), (3, 4999)]),
+    # many queries of one sequence: indexer GEMM, one top-k workgroup per row, one split
+    "prefill": ([12000], [(0, 11960 + i) for i in range(40)]),
+}
+
+
+@pytest.mark.parametrize("k", [4096, 8192])
+@pytest.mark.parametrize("case", list(E2E_K_CASES))
+def test_forward_index_topk_above_2048(case, k):
+    lens, qs = E2E_K_CASES[case]
+    _say(f"[forward] {case} k={k}")
+    inp = synth.custom(lens, qs, seed=46)
+    T = len(qs)
+    _e2e(inp, range(T) if T <= 8 else [0, 17, T - 1], k=k)
+
+
 def test_forward_chunking_is_invisible():
     inp = synth.custom([4100], [(0, 4000 + 3 * i) for i in range(20)], seed=44)
     d = to_device(inp)
@@ -284,25 +314,28 @@ def test_empty_batch_is_a_no_op():
 
 # ------------------------------------------------------------------ full sizes, sampled
 FULL = {
-    "decode_b32_ctx32k": [0, 31],
-    "decode_b8_ctx204k": [0, 5],
-    "prefill_chunk4096_ctx131k": [0, 2047, 4095],
+    "decode_b32_ctx32k": ([0, 31], (2048,)),
+    # also with index_topk 8192 on the same inputs
+    "decode_b8_ctx204k": ([0, 5], (2048, 8192)),
+    "prefill_chunk4096_ctx131k": ([0, 2047, 4095], (2048, 4096)),
     # every query of one 65,536-token sequence (16 GEMM chunks of 4,096 in one call); queries
     # below position 2048 keep all earlier tokens, later ones their top-2048 of a planted row
-    "causal_prefill_65k_planted": [0, 1, 2046, 2047, 2048, 4095, 30001, 65535],
+    "causal_prefill_65k_planted": ([0, 1, 2046, 2047, 2048, 4095, 30001, 65535], (2048,)),
 }
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_forward_full_size_sampled(name):
+    sample, ks = FULL[name]
     _say(f"[forward full] {name}: generating inputs")
     inp = synth.make_inputs(synth.workload(name))
     d = to_device(inp)
-    _say(f"  running; sampled queries {FULL[name]}")
-    _e2e(inp, FULL[name], d=d)
+    for k in ks:
+        _say(f"  running k={k}; sampled queries {sample}")
+        _e2e(inp, sample, k=k, d=d)
     sc = dsa.dsa_index_scores(d.batch, d.q_idx, d.w, d.k_idx)
-    rows = sc[FULL[name]].cpu().numpy()
-    for i, t in enumerate(FULL[name]):
+    rows = sc[sample].cpu().numpy()
+    for i, t in enumerate(sample):
         ref = _oracle_scores(inp, t)
         err = float(np.abs(rows[i, : len(ref)].astype(np.float64) - ref).max())
         _say(f"  t={t} max |score err| {err:.2e}")
