@@ -124,6 +124,20 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
   return lo;
 }
 
+// Writes the union of two ascending, disjoint position lists (in LDS) to out
+// in ascending order: each entry's slot is its index plus its rank in the
+// other list.
+__device__ __forceinline__ void merge_lists(const int* la, int na, const int* lc, int nc, int32_t* out) {
+  for (int i = threadIdx.x; i < na; i += blockDim.x) {
+    const int a = la[i];
+    out[i + lower_bound(lc, nc, a)] = a;
+  }
+  for (int j = threadIdx.x; j < nc; j += blockDim.x) {
+    const int c = lc[j];
+    out[j + lower_bound(la, na, c)] = c;
+  }
+}
+
 // Step 3: sh.cand_* holds c1 candidates in position order and sh.list_a the
 // above1 positions above every candidate (ascending); krem = k - above1 of the
 // candidates are kept.  With `window`, the candidates span several top-digit
@@ -185,14 +199,100 @@ __device__ void finish_from_candidates(TkShared<KMAX>& sh, uint32_t b1, int abov
     nE += tot & 0xFFFF;
   }
   __syncthreads();
-  for (int i = tid; i < above1; i += kTkThreads) {
-    const int a = sh.list_a[i];
-    out[i + lower_bound(sh.list_c, krem, a)] = a;
+  merge_lists(sh.list_a, above1, sh.list_c, krem, out);
+}
+
+// Step 3 for a threshold bin whose c1 candidates (key, position pairs in
+// position order) exceed the LDS capacity but sit in global memory (the split
+// workspace): the same digit passes and ordered compaction, reading the
+// candidates from global memory, 16 consecutive per thread per round.  List A
+// is in sh.list_a; list C (krem <= KMAX entries) goes to the LDS of the unused
+// candidate arrays.
+template <int KMAX>
+__device__ void finish_from_global_candidates(TkShared<KMAX>& sh, const uint32_t* __restrict__ cand,
+                                              uint32_t b1, int above1, int c1, int krem, int32_t* out) {
+  static_assert(KMAX <= 2 * kCandCap, "list C fits the candidate arrays");
+  const int tid = threadIdx.x;
+  int* list_c = reinterpret_cast<int*>(sh.cand_key);  // cand_key and cand_pos are contiguous
+  constexpr int kPairs = kPerThread / 2;              // 16-byte loads (two candidates) per thread
+  auto load = [&](int base, u32x4 v[kPairs]) {
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const int j = base + kPerThread * tid + 2 * u;
+      v[u] = j < c1 ? *reinterpret_cast<const u32x4*>(cand + 2 * j) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // digit 2 (every candidate has top digit b1)
+  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  for (int base = 0; base < c1; base += kStep) {
+    u32x4 v[kPairs];
+    load(base, v);
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const int j = base + kPerThread * tid + 2 * u;
+      if (j < c1) atomicAdd(&sh.hist[(v[u].x >> 8) & 0xFFFu], 1u);
+      if (j + 1 < c1) atomicAdd(&sh.hist[(v[u].z >> 8) & 0xFFFu], 1u);
+    }
   }
-  for (int j = tid; j < krem; j += kTkThreads) {
-    const int c = sh.list_c[j];
-    out[j + lower_bound(sh.list_a, above1, c)] = c;
+  __syncthreads();
+  find_bin<kTkBins>(sh, krem);
+  const uint32_t b2 = (uint32_t)sh.sel_bin;
+  const int krem2 = krem - sh.sel_above;
+  __syncthreads();
+  // digit 3
+  for (int i = tid; i < 256; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  const uint32_t pre12 = (b1 << 12) | b2;
+  for (int base = 0; base < c1; base += kStep) {
+    u32x4 v[kPairs];
+    load(base, v);
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const int j = base + kPerThread * tid + 2 * u;
+      if (j < c1 && (v[u].x >> 8) == pre12) atomicAdd(&sh.hist[v[u].x & 0xFFu], 1u);
+      if (j + 1 < c1 && (v[u].z >> 8) == pre12) atomicAdd(&sh.hist[v[u].z & 0xFFu], 1u);
+    }
   }
+  __syncthreads();
+  find_bin<256>(sh, krem2);
+  const int r = krem2 - sh.sel_above;  // ties at the threshold key to keep (lowest positions)
+  const uint32_t kstar = (pre12 << 8) | (uint32_t)sh.sel_bin;
+  // ordered compaction of the kept candidates into list C
+  int nG = 0, nE = 0;
+  for (int base = 0; base < c1; base += kStep) {
+    u32x4 v[kPairs];
+    load(base, v);
+    const int j0 = base + kPerThread * tid;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const uint32_t key = (e & 1) ? v[e >> 1].z : v[e >> 1].x;
+      const bool ok = j0 + e < c1;
+      gt += ok && key > kstar;
+      eq += ok && key == kstar;
+    }
+    int tot;
+    const int ex = block_excl_scan<kTkWaves>((gt << 16) | eq, sh.wave_tot, tot);  // <= kStep each
+    int eg = nG + (ex >> 16), ee = nE + (ex & 0xFFFF);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (j0 + e >= c1) continue;
+      const uint32_t key = (e & 1) ? v[e >> 1].z : v[e >> 1].x;
+      const int pos = (int)((e & 1) ? v[e >> 1].w : v[e >> 1].y);
+      if (key > kstar) {
+        list_c[eg + min(ee, r)] = pos;
+        ++eg;
+      } else if (key == kstar) {
+        if (ee < r) list_c[eg + ee] = pos;
+        ++ee;
+      }
+    }
+    nG += tot >> 16;
+    nE += tot & 0xFFFF;
+  }
+  __syncthreads();
+  merge_lists(sh.list_a, above1, list_c, krem, out);
 }
 
 // Step 4 (heavy ties): lower digits by passes over the row, then an ordered
@@ -457,7 +557,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __r
 
 // ---------------------------------------------------------------- split path
 // Workspace per query (SplitWs): the slice bin lists, a header {b1, above1,
-// c1}, list A [k_max] and candidates (key, position) [kCandCap][2].
+// c1}, list A [kMaxTopk] and candidates (key, position) [kCandCapWs][2].
 
 // Kernel 1 (grid T x S), only where the key scan did not write the lists:
 // the sparse top-digit list of one slice of stored scores.
@@ -640,7 +740,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
     hdr[1] = above1;
     hdr[2] = c1;
   }
-  if (c1 > kCandCap) return;  // heavy ties: the row's finish re-reads the row
+  if (c1 > kCandCapWs) return;  // heavy ties: the row's finish re-reads the row
   int offA = sh.offA, offC = sh.offC;
   // ---- ordered compaction of the slice, 16 consecutive scores per thread per step
   int* list_a = reinterpret_cast<int*>(base + w.a_off);
@@ -710,7 +810,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
   // List A (fewer than k <= KMAX entries) and the first kTopkSmall candidates
   // are read together with the header; entries past the counts are stale and
-  // unused (the workspace holds kMaxTopk entries of A and kCandCap candidates).
+  // unused (the workspace holds kMaxTopk entries of A and kCandCapWs candidates).
   constexpr int kSpecA = KMAX / kTkThreads;
   constexpr int kSpecC = kTopkSmall / kTkThreads;
   int a_spec[kSpecA];
@@ -731,7 +831,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   const int above1 = hdr[1];
   const int c1 = hdr[2];
   const int krem = k - above1;
-  if (c1 > kCandCap) {
+  if (c1 > kCandCapWs) {
     finish_from_row(sh, scores + (int64_t)t * ld, n, b1, krem, out);
     return;
   }
@@ -739,6 +839,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   for (int u = 0; u < kSpecA; ++u) {
     const int i = tid + u * kTkThreads;
     if (i < above1) sh.list_a[i] = a_spec[u];
+  }
+  if (c1 > kCandCap) {  // candidates stay in the workspace
+    __syncthreads();
+    finish_from_global_candidates(sh, cand, b1, above1, c1, krem, out);
+    return;
   }
 #pragma unroll
   for (int u = 0; u < kSpecC; ++u) {

@@ -18,6 +18,7 @@ namespace dsa {
 constexpr int kScanTile = 128;   // keys per scan tile and slice granularity
 constexpr int kTkBins = 4096;    // top-digit bins
 constexpr int kCandCap = 5120;   // candidates of the threshold bin(s) kept in LDS
+constexpr int kCandCapWs = 32768;  // candidates of the threshold bin kept in the split workspace
 constexpr int kSplitRows = 128;  // batches with fewer rows use the split top-k
 constexpr int kMaxSlices = 1024; // slices per row
 constexpr int kScanSlots = 512;  // resident key-scan workgroups (two per CU)
@@ -66,7 +67,7 @@ inline SplitWs split_ws(int T, int max_ctx) {
   w.a_off = o;
   o += (size_t)kMaxTopk * sizeof(int);
   w.c_off = o;
-  o += (size_t)kCandCap * 2 * sizeof(uint32_t);
+  o += (size_t)kCandCapWs * 2 * sizeof(uint32_t);
   w.per_query = (o + 255) / 256 * 256;
   return w;
 }

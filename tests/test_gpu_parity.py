@@ -97,6 +97,7 @@ TOPK_CASES = {
     "normal_ragged": ("normal", [1, 33, 2047, 2048, 2049, 4097, 20000, 131071], 2048),
     "signed": ("signed", [3000, 50000], 2048),
     "heavy_ties": ("few_values", [2100, 100000], 2048),   # threshold bin overflows LDS -> global passes
+    "heavy_ties_huge": ("few_values", [300000], 2048),     # ... and the split workspace -> row passes
     "small_k": ("normal", [5000, 100], 7),
     "k1": ("signed", [1000, 1], 1),
     "long_rows": ("normal", [65536, 204800, 300001], 2048),   # sampled-window path
