@@ -6,7 +6,8 @@ seeded synthetic inputs that are already resident in HBM:
     (value = decode queries/s);
   * also reported: a prefill chunk of 4,096 queries at positions
     200,704..204,799 of one 204,800-token sequence (query-tokens/s), and an
-    IndexShare group of 4 decode layers (one selects, three reuse).
+    IndexShare group of 4 decode layers (one selects, three reuse), index_topk
+    4096/8192 on the same inputs, and both workloads with 64-token cache pages.
 Prints one JSON line.  Run `python bench.py --help` for options.
 """
 from __future__ import annotations
@@ -32,6 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 DECODE = "decode_b8_ctx204k"
 PREFILL = "prefill_chunk4096_ctx204k"
 TOPK = 2048
+PAGE = 64  # tokens per cache page for the paged-cache measurement
 
 
 def log(msg):
@@ -99,7 +101,30 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms
 
 
-def run_workload(name, steps, warmup, with_ops=True, extra_k=()):
+def paged_copy(inp, d, page_size, seed=4096):
+    """The workload's caches scattered over a device page pool (seeded page
+    permutation, 3 spare pages): every sequence length must be a multiple of
+    page_size.  Returns (block_table [B, pages] int32, k_idx pool, kv pool)."""
+    lens = list(inp.wl.seq_lens)
+    assert all(n % page_size == 0 for n in lens)
+    npg = sum(n // page_size for n in lens)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    perm = torch.randperm(npg + 3, generator=g, device="cuda")[:npg]
+    pools = []
+    for x, width in ((d["k_idx"], 128), (d["kv"], 576)):
+        pool = torch.zeros(((npg + 3) * page_size, width), dtype=x.dtype, device="cuda")
+        pool.view(npg + 3, page_size, width)[perm] = x.view(npg, page_size, width)
+        pools.append(pool)
+    table = torch.zeros((len(lens), max(lens) // page_size), dtype=torch.int32, device="cuda")
+    j = 0
+    for b, n in enumerate(lens):
+        table[b, : n // page_size] = perm[j: j + n // page_size].to(torch.int32)
+        j += n // page_size
+    return table, pools[0], pools[1]
+
+
+def run_workload(name, steps, warmup, with_ops=True, extra_k=(), page_size=0):
     log(f"[bench] {name}: generating inputs")
     t0 = time.time()
     inp = synth.make_inputs(synth.workload(name))
@@ -132,6 +157,19 @@ def run_workload(name, steps, warmup, with_ops=True, extra_k=()):
         by_k[k] = time_calls(step_k, steps, warmup)
         log(f"[bench] {name}: k={k} {by_k[k]:.3f} ms/step")
         del idx_k, ws_k
+    if page_size:
+        # paged caches: the same rows behind a block table
+        table, k_pool, kv_pool = paged_copy(inp, d, page_size)
+        pb = dsa.Batch(batch.q_seq, batch.q_pos, None, batch.max_ctx, block_table=table, page_size=page_size)
+
+        def step_p():
+            dsa.dsa_forward(pb, d["q_idx"], d["w"], k_pool, d["q_nope"], d["q_rope"], kv_pool, d["w_uk"],
+                            d["w_uv"], k=TOPK, out=out, idx=idx, ws=ws)
+
+        by_k["paged"] = time_calls(step_p, steps, warmup)
+        log(f"[bench] {name}: paged ({page_size}-token pages) {by_k['paged']:.3f} ms/step")
+        del table, k_pool, kv_pool
+        torch.cuda.empty_cache()
     if not with_ops:
         log(f"[bench] {name}: {ms:.3f} ms/step")
         return inp, ms, {}, by_k
@@ -264,7 +302,8 @@ def main():
         run_workload(PREFILL, args.steps, args.warmup, not args.no_ops, extra_k[-1:])
         return
 
-    inp, ms, ops, dec_k = run_workload(DECODE, args.steps, args.warmup, extra_k=extra_k)
+    inp, ms, ops, dec_k = run_workload(DECODE, args.steps, args.warmup, extra_k=extra_k, page_size=PAGE)
+    dec_paged = dec_k.pop("paged")
     alg = algorithmic(inp)
     T = len(inp.q_pos)
     scan_ms = ops["index_scores"]
@@ -293,6 +332,8 @@ def main():
         "ops_ms": ops,
         "index_topk_variants": {str(k): {"ms_per_step": v, "value": T / (v * 1e-3), "unit": "decode queries/s"}
                                 for k, v in dec_k.items()},
+        "paged": {"page_size": PAGE, "ms_per_step": dec_paged, "value": T / (dec_paged * 1e-3),
+                  "unit": "decode queries/s", "vs_contiguous": ms / dec_paged},
     }
     if not args.no_index_share:
         result["index_share"] = index_share_group(inp, args.steps, args.warmup)
@@ -302,7 +343,8 @@ def main():
     del inp
     if not args.no_prefill:
         pinp, pms, pops, pre_k = run_workload(PREFILL, max(3, args.steps // 5), min(args.warmup, 3),
-                                              extra_k=extra_k[-1:])
+                                              extra_k=extra_k[-1:], page_size=PAGE)
+        pre_paged = pre_k.pop("paged")
         palg = algorithmic(pinp)
         pach = palg["index_flops"] / (pops["index_scores"] * 1e-3) / 1e12
         result["prefill"] = {
@@ -310,6 +352,8 @@ def main():
             "ms_per_step": pms, "ops_ms": pops,
             "index_topk_variants": {str(k): {"ms_per_step": v, "value": len(pinp.q_pos) / (v * 1e-3),
                                              "unit": "query-tokens/s"} for k, v in pre_k.items()},
+            "paged": {"page_size": PAGE, "ms_per_step": pre_paged, "value": len(pinp.q_pos) / (pre_paged * 1e-3),
+                      "unit": "query-tokens/s", "vs_contiguous": pms / pre_paged},
             "mfma_frac_whole_step": palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "idx_gemm_kernel", "achieved": pach,
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pach / MFMA_BF16_PEAK_TFLOPS,

@@ -24,8 +24,14 @@
  *   - bf16 arrays are raw bit patterns (uint16_t).  bf16 arrays, the score
  *     matrix and the workspace must be 16-byte aligned (DSA_ERR_ALIGN).
  *   - Positions are sequence-local: query t belongs to sequence q_seq[t] and
- *     sits at position q_pos[t]; token s of sequence b is cache row
- *     seq_row0[b] + s.  A query sees positions 0..q_pos[t] (itself included).
+ *     sits at position q_pos[t].  A query sees positions 0..q_pos[t] (itself
+ *     included).  Token s of sequence b is cache row row(b, s) of both caches
+ *     (the indexer keys k_idx and the latent cache kv):
+ *       contiguous (page_size == 0): row(b, s) = seq_row0[b] + s;
+ *       paged (page_size > 0):       row(b, s) = block_table[b*max_pages + s/page_size]
+ *                                                * page_size + s % page_size
+ *     (page 3, "GLM-5 7440亿参数，202K长上下文突破极限", section 六: paged KV caches for
+ *     batched serving).  Paged rows must stay below 2^31.
  *   - Ownership: the caller owns every buffer.  The library allocates nothing,
  *     frees nothing and keeps no pointer after a call returns.  Work is
  *     enqueued on `stream` (a hipStream_t; NULL = default stream) and is not
@@ -35,8 +41,9 @@
  *     enqueued, and a failing call enqueues nothing.  DSA_ERR_LAUNCH reports a
  *     failed kernel launch (see dsa_last_hip_error).  Device-side
  *     preconditions (q_seq[t] < num_seqs, 0 <= q_pos[t] < rows of that
- *     sequence, every cache row inside its allocation, idx entries in
- *     {-1} U [0, q_pos[t]]) are not checked: violating them is undefined.
+ *     sequence, every cache row and block_table page inside its allocation,
+ *     idx entries in {-1} U [0, q_pos[t]]) are not checked: violating them is
+ *     undefined.
  *   - num_queries == 0 is a valid empty call: DSA_OK, nothing enqueued.
  *   - Calls are re-entrant; the only library state is a per-device cache of
  *     the device check and a thread-local last HIP error.
@@ -51,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 #define DSA_INDEX_HEADS 32
 #define DSA_INDEX_DIM 128
@@ -83,15 +90,23 @@ enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
 /* Operation ids for dsa_workspace_bytes. */
 enum { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
 
-/* Batch geometry.  The struct itself is HOST memory, read during the call. */
+/* Batch geometry and cache layout.  The struct itself is HOST memory, read
+ * during the call. */
 typedef struct dsa_batch {
   int32_t num_queries;       /* T >= 0 */
   int32_t num_seqs;          /* B >= 1 */
   int32_t max_ctx;           /* >= max_t(q_pos[t]) + 1, 1 .. 2^21: bounds grids and score rows */
-  int32_t reserved;          /* must be 0 */
+  int32_t page_size;         /* 0: contiguous caches (seq_row0); else tokens per cache page,
+                                a power of two, 16 .. 2^20 (block_table) */
   const int32_t* q_seq;      /* [T] device: sequence of each query */
   const int32_t* q_pos;      /* [T] device: position of each query (inclusive causal limit) */
-  const int64_t* seq_row0;   /* [B] device: first cache row of each sequence */
+  const int64_t* seq_row0;   /* contiguous: [B] device, first cache row of each sequence;
+                                ignored when paged */
+  const int32_t* block_table;/* paged: [B, max_pages] device, the page holding tokens
+                                [j*page_size, (j+1)*page_size) of sequence b at [b*max_pages + j];
+                                ignored when contiguous */
+  int32_t max_pages;         /* paged: >= ceil(max_ctx / page_size); ignored when contiguous */
+  int32_t reserved;          /* must be 0 */
 } dsa_batch;
 
 /*

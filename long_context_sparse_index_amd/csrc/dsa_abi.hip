@@ -44,12 +44,27 @@ dsa_status check_device() {
   return ok ? DSA_OK : DSA_ERR_DEVICE;
 }
 
+// log2 of a valid page size (16 .. 2^20, a power of two), else 0.
+int page_shift(int32_t page_size) {
+  for (int s = 4; s <= 20; ++s)
+    if (page_size == (1 << s)) return s;
+  return 0;
+}
+
 dsa_status check_batch(const dsa_batch* b) {
   if (!b) return DSA_ERR_NULL;
   if (b->num_queries < 0 || b->num_queries > kMaxQueries) return DSA_ERR_SHAPE;
   if (b->num_seqs < 1 || b->max_ctx < 1 || b->max_ctx > kMaxCtx || b->reserved != 0)
     return DSA_ERR_SHAPE;
-  if (b->num_queries > 0 && (!b->q_seq || !b->q_pos || !b->seq_row0)) return DSA_ERR_NULL;
+  if (b->page_size != 0) {
+    if (page_shift(b->page_size) == 0) return DSA_ERR_SHAPE;
+    if (b->max_pages < 1 || (int64_t)b->max_pages * b->page_size < b->max_ctx) return DSA_ERR_SHAPE;
+    if ((int64_t)b->num_seqs * b->max_pages > ((int64_t)1 << 31)) return DSA_ERR_SHAPE;
+  }
+  if (b->num_queries > 0) {
+    if (!b->q_seq || !b->q_pos) return DSA_ERR_NULL;
+    if (b->page_size == 0 ? !b->seq_row0 : !b->block_table) return DSA_ERR_NULL;
+  }
   return DSA_OK;
 }
 
@@ -72,7 +87,10 @@ dsa::LaunchBatch to_launch(const dsa_batch* b, int t0, int T) {
   lb.max_ctx = b->max_ctx;
   lb.q_seq = b->q_seq + t0;
   lb.q_pos = b->q_pos + t0;
-  lb.seq_row0 = b->seq_row0;
+  lb.rows.seq_row0 = b->page_size == 0 ? b->seq_row0 : nullptr;
+  lb.rows.table = b->page_size == 0 ? nullptr : b->block_table;
+  lb.rows.page_shift = b->page_size == 0 ? 0 : page_shift(b->page_size);
+  lb.rows.max_pages = b->page_size == 0 ? 0 : b->max_pages;
   return lb;
 }
 

@@ -7,12 +7,23 @@
 
 namespace dsa {
 
+// Where token s of sequence b sits in the caches: row seq_row0[b] + s
+// (contiguous, page_shift == 0), or row (table[b * max_pages + (s >> page_shift)]
+// << page_shift) | (s & (2^page_shift - 1)) (paged, page_shift 4 .. 20).
+struct CacheRows {
+  const int64_t* seq_row0;
+  const int32_t* table;
+  int page_shift;
+  int max_pages;
+};
+
 struct LaunchBatch {
   int T;                   // queries in this launch
   int max_ctx;             // host bound of q_pos + 1
   const int32_t* q_seq;    // [T] device
   const int32_t* q_pos;    // [T] device
-  const int64_t* seq_row0; // [B] device
+  CacheRows rows;
+  bool paged() const { return rows.page_shift != 0; }
 };
 
 // Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries;

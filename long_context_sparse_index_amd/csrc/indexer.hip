@@ -25,25 +25,34 @@ namespace dsa {
 // measured at about half the bandwidth of this coalesced form.
 // With `lists` set, the workgroup also counts the top digit of its scores in
 // LDS and writes the slice's sparse bin list for the split top-k.
+// PAGED: the cache is paged (pages of >= 16 tokens, so every 16-key granule of
+// a tile lies in one page); the pages of tile i + 2 are looked up while tile i
+// is computed and kept in a 3-slot LDS ring, so key loads never wait on them.
 constexpr int kScanLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
+constexpr int kGranule = 16;           // keys per page-table lookup (smallest page)
 
+template <bool PAGED>
 __global__ __launch_bounds__(256) void idx_scan_kernel(
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
-    const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    float* __restrict__ scores, int64_t ld, int slice_keys, char* __restrict__ lists,
-    SplitWs sw) {
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int slice_keys,
+    char* __restrict__ lists, SplitWs sw) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kScanTile * kScanLds];
   __shared__ uint32_t hist[kTkBins / 2];
   __shared__ int wave_tot[4];
+  __shared__ int s_pid[3][kScanTile / kGranule];
   const int t = blockIdx.x;
   const int pos = q_pos[t];
   const int k0 = blockIdx.y * slice_keys;
   if (k0 > pos) return;
   const int kend = min(k0 + slice_keys, pos + 1);
   const int ntiles = (kend - k0 + kScanTile - 1) / kScanTile;
-  const int64_t row0 = seq_row0[q_seq[t]];
+  const int seq = q_seq[t];
+  const int64_t row0 = PAGED ? 0 : cr.seq_row0[seq];
+  const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // page of granule tid (< 8) of a tile (keys past pos: the page of pos)
+  auto pid_load = [&](int tile) { return bt[min(k0 + tile * kScanTile + kGranule * tid, pos) >> cr.page_shift]; };
   const int g = lane >> 5, n = lane & 31;
   if (lists) {
 #pragma unroll
@@ -62,11 +71,16 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 
   u32x4 st[8];
   auto gload = [&](int tile) {
+    const int base = k0 + tile * kScanTile;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int lin = tid + 256 * c;  // 16-byte chunk of the 32 KB tile
-      const int key = min(k0 + tile * kScanTile + (lin >> 4), pos);  // rows past pos: never used
-      st[c] = ld16_nt(k_idx + (row0 + key) * kIdxDim + (lin & 15) * 8);
+      const int key = min(base + (lin >> 4), pos);  // rows past pos: never used
+      int64_t row = row0 + key;
+      if (PAGED)
+        row = ((int64_t)s_pid[tile % 3][(key - base) / kGranule] << cr.page_shift) |
+              (key & ((1 << cr.page_shift) - 1));
+      st[c] = ld16_nt(k_idx + row * kIdxDim + (lin & 15) * 8);
     }
   };
   auto lstore = [&](int buf) {
@@ -77,12 +91,23 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     }
   };
   float* srow = scores + (int64_t)t * ld;
+  if (PAGED) {
+    if (tid < kScanTile / kGranule) {
+      const int p0 = pid_load(0);
+      const int p1 = ntiles > 1 ? pid_load(1) : 0;
+      s_pid[0][tid] = p0;
+      s_pid[1][tid] = p1;
+    }
+    __syncthreads();
+  }
   gload(0);
   lstore(0);
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < ntiles) gload(tile + 1);
+    const bool pref = PAGED && tid < kScanTile / kGranule && tile + 2 < ntiles;
+    const int pnext = pref ? pid_load(tile + 2) : 0;
     const uint16_t* bp = &ks[buf][(wave * 32 + n) * kScanLds + 8 * g];
     f32x16 acc = {};
 #pragma unroll
@@ -98,6 +123,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       if (lists) hist16_add(hist, score_key(tot));
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
+    if (pref) s_pid[(tile + 2) % 3][tid] = pnext;  // slot of tile - 1, read two barriers ago
     __syncthreads();
   }
   if (lists)
@@ -121,13 +147,14 @@ constexpr int kGemmKT = 64;
 constexpr int kGemmSplit = 8192;
 constexpr int kKeyLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 
+template <bool PAGED>
 __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos,
-    const int64_t* __restrict__ seq_row0, const uint16_t* __restrict__ q_idx,
-    const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    float* __restrict__ scores, int64_t ld, int T) {
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int T) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kGemmKT * kKeyLds];
   __shared__ int s_seq[kGemmQB], s_pos[kGemmQB];
+  __shared__ int s_pid[3][kGemmKT / kGranule];  // pages of tiles i .. i+2 (as in the scan)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int t0 = blockIdx.x * kGemmQB;
@@ -168,18 +195,26 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int kbeg = split0;
     const int kend = min(split0 + kGemmSplit, hi + 1);
     if (kbeg >= kend) continue;
-    const int64_t row0 = seq_row0[sq];
+    const int64_t row0 = PAGED ? 0 : cr.seq_row0[sq];
+    const int32_t* bt = PAGED ? cr.table + (int64_t)sq * cr.max_pages : nullptr;
     const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
+    auto pid_load = [&](int tile) { return bt[min(kbeg + tile * kGemmKT + kGranule * tid, hi) >> cr.page_shift]; };
+    constexpr int kGran = kGemmKT / kGranule;
 
     // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 2 per thread.
     constexpr int kPer = kGemmKT * 16 / kGemmThreads;
     u32x4 stage[kPer];
     auto gload = [&](int tile) {
+      const int base = kbeg + tile * kGemmKT;
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
         const int lin = tid + kGemmThreads * c;
-        const int key = min(kbeg + tile * kGemmKT + (lin >> 4), hi);
-        stage[c] = ld16(k_idx + (row0 + key) * kIdxDim + (lin & 15) * 8);
+        const int key = min(base + (lin >> 4), hi);
+        int64_t row = row0 + key;
+        if (PAGED)
+          row = ((int64_t)s_pid[tile % 3][(key - base) / kGranule] << cr.page_shift) |
+                (key & ((1 << cr.page_shift) - 1));
+        stage[c] = ld16(k_idx + row * kIdxDim + (lin & 15) * 8);
       }
     };
     auto lstore = [&](int buf) {
@@ -189,12 +224,23 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
         st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
       }
     };
+    if (PAGED) {
+      if (tid < kGran) {
+        const int p0 = pid_load(0);
+        const int p1 = ntiles > 1 ? pid_load(1) : 0;
+        s_pid[0][tid] = p0;
+        s_pid[1][tid] = p1;
+      }
+      __syncthreads();
+    }
     gload(0);
     lstore(0);
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
       if (tile + 1 < ntiles) gload(tile + 1);
+      const bool pref = PAGED && tid < kGran && tile + 2 < ntiles;
+      const int pnext = pref ? pid_load(tile + 2) : 0;
       const int sbase = kbeg + tile * kGemmKT;
       bf16x8 bfr[2][8];
 #pragma unroll
@@ -223,6 +269,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
         }
       }
       if (tile + 1 < ntiles) lstore(buf ^ 1);
+      if (pref) s_pid[(tile + 2) % 3][tid] = pnext;
       __syncthreads();
     }
   }
@@ -234,13 +281,21 @@ hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, cons
                                void* topk_ws, hipStream_t st) {
   if (gemm) {
     dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (b.max_ctx + kGemmSplit - 1) / kGemmSplit);
-    idx_gemm_kernel<<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx,
-                                                   scores, ld, b.T);
+    if (b.paged())
+      idx_gemm_kernel<true><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                           scores, ld, b.T);
+    else
+      idx_gemm_kernel<false><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                            scores, ld, b.T);
   } else {
     const SplitWs sw = split_ws(b.T, b.max_ctx);
-    idx_scan_kernel<<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.seq_row0, q_idx, w, k_idx,
-                                                     scores, ld, sw.slice_keys,
-                                                     static_cast<char*>(topk_ws), sw);
+    char* lists = static_cast<char*>(topk_ws);
+    if (b.paged())
+      idx_scan_kernel<true><<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                             scores, ld, sw.slice_keys, lists, sw);
+    else
+      idx_scan_kernel<false><<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                              scores, ld, sw.slice_keys, lists, sw);
   }
   return hipGetLastError();
 }

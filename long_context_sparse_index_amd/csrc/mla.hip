@@ -75,8 +75,9 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
-    const int32_t* __restrict__ q_seq, const int64_t* __restrict__ seq_row0,
+    const int32_t* __restrict__ q_seq, CacheRows cr,
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int k, float scale_log2,
     int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
@@ -99,8 +100,13 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   const int hg = wave & 3, hf = wave >> 2;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
-  // rows of this query's sequence; positions < 2^21, so 32-bit offsets suffice
-  const uint16_t* const kv_seq = kv + seq_row0[q_seq[t]] * kRow;
+  // Contiguous: s_idx holds positions, rows of the query's sequence start at
+  // kv_seq, and positions < 2^21 keep 32-bit element offsets in range.  Paged:
+  // s_idx holds pool rows (< 2^31) and offsets are 64-bit.  Absent entries
+  // hold ~r for the row r of position 0 (finite data, masked later).
+  const int seq = q_seq[t];
+  const uint16_t* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kRow;
+  const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
   const int32_t* irow = idx + (int64_t)t * k;
   const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
 
@@ -129,6 +135,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
         const int j = b0 + tid + u * kCoreThreads;
         const int e = irow[min(j0 + j, k - 1)];  // in-row read, replaced past the split
         v[u] = j0 + j < j1 ? e : -1;
+      }
+      if (PAGED) {  // position -> pool row (all page loads, then the rows)
+        int pg[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) pg[u] = bt[max(v[u], 0) >> cr.page_shift];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int row = (pg[u] << cr.page_shift) | (max(v[u], 0) & ((1 << cr.page_shift) - 1));
+          v[u] = v[u] >= 0 ? row : ~row;
+        }
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
@@ -168,9 +184,11 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
-      // absent keys (and tiles past the end) fetch row 0 of the sequence: finite data, masked later
-      const uint32_t off = (uint32_t)(sidx[i] >= 0 ? sidx[i] : 0) * (uint32_t)kRow + g_col[i];
-      __builtin_amdgcn_global_load_lds(kv_seq + off, dstt + blk * 64 * 8, 16, 0, 0);
+      // absent keys (and tiles past the end) fetch the row of position 0: finite data, masked later
+      const int r = sidx[i] >= 0 ? sidx[i] : ~sidx[i];
+      const uint16_t* src = PAGED ? kv_seq + (int64_t)r * kRow + g_col[i]
+                                  : kv_seq + ((uint32_t)r * (uint32_t)kRow + g_col[i]);
+      __builtin_amdgcn_global_load_lds(src, dstt + blk * 64 * 8, 16, 0, 0);
     }
     if (tid < kKT) s_valid[buf][tid] = valid >= 0;
   };
@@ -604,9 +622,14 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     if (e != hipSuccess) return e;
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  mla_core_kernel<<<dim3(T, p.splits), kCoreThreads, 0, st>>>(b.q_seq, b.seq_row0, q_lat, q_rope, kv, idx,
-                                                     p.k, scale_log2, p.keys_per_split, p.splits,
-                                                     o_lat, o_part, ml_part);
+  if (b.paged())
+    mla_core_kernel<true><<<dim3(T, p.splits), kCoreThreads, 0, st>>>(
+        b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k, scale_log2, p.keys_per_split, p.splits, o_lat,
+        o_part, ml_part);
+  else
+    mla_core_kernel<false><<<dim3(T, p.splits), kCoreThreads, 0, st>>>(
+        b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k, scale_log2, p.keys_per_split, p.splits, o_lat,
+        o_part, ml_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {

@@ -39,10 +39,13 @@ class _CBatch(ctypes.Structure):
         ("num_queries", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32),
         ("max_ctx", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
         ("q_seq", ctypes.c_void_p),
         ("q_pos", ctypes.c_void_p),
         ("seq_row0", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -110,25 +113,41 @@ def _bf16(x: torch.Tensor, name: str, shape) -> torch.Tensor:
 
 
 class Batch:
-    """Batch geometry: q_seq [T] int32, q_pos [T] int32, seq_row0 [B] int64 on the device."""
+    """Batch geometry: q_seq [T] int32 and q_pos [T] int32 on the device, and the
+    cache layout: contiguous (seq_row0 [B] int64: first cache row of each
+    sequence) or paged (block_table [B, max_pages] int32 page ids and
+    page_size tokens per page; seq_row0 then None)."""
 
-    def __init__(self, q_seq: torch.Tensor, q_pos: torch.Tensor, seq_row0: torch.Tensor, max_ctx: int):
-        for name, x, dt in (("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
-                            ("seq_row0", seq_row0, torch.int64)):
+    def __init__(self, q_seq: torch.Tensor, q_pos: torch.Tensor, seq_row0: Optional[torch.Tensor], max_ctx: int,
+                 block_table: Optional[torch.Tensor] = None, page_size: int = 0):
+        for name, x, dt in (("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32)):
             if x.dtype != dt or not x.is_cuda or not x.is_contiguous() or x.dim() != 1:
                 raise ValueError(f"{name}: expected a contiguous 1-D {dt} device tensor")
         if q_seq.shape != q_pos.shape:
             raise ValueError("q_seq and q_pos differ in length")
+        if page_size:
+            if block_table is None or block_table.dtype != torch.int32 or not block_table.is_cuda \
+                    or not block_table.is_contiguous() or block_table.dim() != 2:
+                raise ValueError("block_table: expected a contiguous [B, max_pages] int32 device tensor")
+            self.B = int(block_table.shape[0])
+        else:
+            if seq_row0 is None or seq_row0.dtype != torch.int64 or not seq_row0.is_cuda \
+                    or not seq_row0.is_contiguous() or seq_row0.dim() != 1:
+                raise ValueError("seq_row0: expected a contiguous 1-D int64 device tensor")
+            self.B = int(seq_row0.shape[0])
         self.q_seq, self.q_pos, self.seq_row0 = q_seq, q_pos, seq_row0
+        self.block_table, self.page_size = block_table, int(page_size)
         self.max_ctx = int(max_ctx)
         self.T = int(q_seq.shape[0])
-        self.B = int(seq_row0.shape[0])
 
     def c(self) -> _CBatch:
-        return _CBatch(self.T, self.B, self.max_ctx, 0, _ptr(self.q_seq), _ptr(self.q_pos), _ptr(self.seq_row0))
+        mp = int(self.block_table.shape[1]) if self.page_size else 0
+        return _CBatch(self.T, self.B, self.max_ctx, self.page_size, _ptr(self.q_seq), _ptr(self.q_pos),
+                       _ptr(self.seq_row0), _ptr(self.block_table), mp, 0)
 
     def slice(self, t0: int, t1: int) -> "Batch":
-        return Batch(self.q_seq[t0:t1], self.q_pos[t0:t1], self.seq_row0, self.max_ctx)
+        return Batch(self.q_seq[t0:t1], self.q_pos[t0:t1], self.seq_row0, self.max_ctx, self.block_table,
+                     self.page_size)
 
 
 def score_ld(max_ctx: int) -> int:

@@ -183,6 +183,48 @@ def make_layer_stack(wl: Workload, num_layers: int) -> List[Inputs]:
     return [make_inputs(dataclasses.replace(wl, seed=wl.seed + 7919 * l)) for l in range(num_layers)]
 
 
+@dataclasses.dataclass
+class PagedCaches:
+    """The caches of an ``Inputs`` moved into a pool of pages: token s of
+    sequence b is pool row block_table[b, s // page_size] * page_size +
+    s % page_size.  Pool pages no sequence uses hold bf16 NaN."""
+
+    page_size: int
+    block_table: np.ndarray  # [B, max_pages] int32
+    k_idx: np.ndarray        # [pages * page_size, 128] bf16
+    kv: np.ndarray           # [pages * page_size, 576] bf16
+
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def to_paged(inp: Inputs, page_size: int, seed: int, spare_pages: int = 3) -> PagedCaches:
+    """Scatter each sequence's cache rows, one page at a time, to pool pages in
+    an order drawn from ``default_rng(seed)`` (a permutation of all pool
+    pages, ``spare_pages`` of them left unused).  Row layout only: the rows
+    themselves are copied unchanged."""
+    rng = np.random.default_rng(seed)
+    lens = list(inp.wl.seq_lens)
+    pages_of = [(n + page_size - 1) // page_size for n in lens]
+    max_pages = max(pages_of)
+    total = sum(pages_of) + spare_pages
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.zeros((len(lens), max_pages), dtype=np.int32)
+    k_pool = np.full((total * page_size, IDX_DIM), BF16_NAN, dtype=np.uint16)
+    kv_pool = np.full((total * page_size, D_KV), BF16_NAN, dtype=np.uint16)
+    nxt = 0
+    for b, n in enumerate(lens):
+        r0 = int(inp.seq_row0[b])
+        for j in range(pages_of[b]):
+            page = int(perm[nxt])
+            nxt += 1
+            table[b, j] = page
+            m = min(page_size, n - j * page_size)
+            k_pool[page * page_size: page * page_size + m] = inp.k_idx[r0 + j * page_size: r0 + j * page_size + m]
+            kv_pool[page * page_size: page * page_size + m] = inp.kv[r0 + j * page_size: r0 + j * page_size + m]
+    return PagedCaches(page_size, table, k_pool, kv_pool)
+
+
 def derive_layer(inp: Inputs, seed: int) -> Inputs:
     """Another layer over the same batch, cheap to draw at full size: fresh
     q_nope, q_rope, W_UK, W_UV (distributions as above, drawn in that order

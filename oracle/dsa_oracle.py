@@ -19,6 +19,8 @@ Sources (the pages have no code; every step below is restated from prose):
         IndexShare section (one indexer per 4 layers, the group figure, the
         21 full / 57 shared count) and the config fields listed at its end
         (index_topk_freq 4, num_hidden_layers 78, 3 dense + 75 sparse).
+  [G5]  page "GLM-5 7440亿参数，202K长上下文突破极限", section 六 (deployment advice:
+        paged KV caches for batched serving).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -32,6 +34,9 @@ design notes of the repository):
     the nearest earlier full layer (a forward pass cannot use a later one);
     the group figure, which pairs layers 3-5 with layer 6, is read with each
     full layer feeding the three layers after it.
+  * paged caches: token s of a sequence sits in page s // P of that
+    sequence's page list, at offset s % P (page-table indirection is storage
+    only; every computation above reads the same rows).
   * MLA over the kept rows with explicit per-head up-projection
     K_nope = c @ W_UK[h], V = c @ W_UV[h]; logits (q_nope.K_nope + q_rope.r)
     times softmax_scale (1/sqrt(192+64) = 1/16 by default); softmax in full.
@@ -267,3 +272,16 @@ def layer_stack_forward(layers, schedule, queries: Optional[Iterable[int]] = Non
         idx_all.append(sel)
         out_all.append(outs)
     return idx_all, out_all
+
+
+# ---------------------------------------------------------------- paged caches
+def paged_row(page_list, page_size: int, s: int) -> int:
+    """Pool row of token s of a sequence whose cache lives in pages.
+
+    [G5] section six recommends paged caches for batched serving; the pages do
+    not fix a layout.  Reading: the sequence's tokens fill fixed-size pages in
+    order, page j holding tokens j*P .. j*P+P-1, and ``page_list[j]`` names
+    the pool page (rows page*P .. page*P+P-1) that holds them.
+    """
+    page, offset = divmod(int(s), int(page_size))
+    return int(page_list[page]) * int(page_size) + offset

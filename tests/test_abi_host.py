@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dsa_abi_version() == 1
+    assert L.dsa_abi_version() == 2
     for s in range(8):
         assert L.dsa_status_string(s)
     assert L.dsa_status_string(99) == b"unknown status"
@@ -58,7 +58,7 @@ def test_index_scores_validation(L):
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
     bad = _batch(B=0)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
-    bad = dsa._CBatch(4, 1, 100, 7, FAKE, FAKE, FAKE)  # reserved != 0
+    bad = dsa._CBatch(4, 1, 100, 0, FAKE, FAKE, FAKE, None, 0, 3)  # reserved != 0
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
     bad = dsa._CBatch(4, 1, 100, 0, None, FAKE, FAKE)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 1
@@ -136,3 +136,31 @@ def test_index_share_schedule_matches_oracle(L):
     assert L.dsa_index_share_schedule(4, 5, 2, src) == 2
     assert L.dsa_index_share_schedule(4, 1, 0, src) == 2
     assert list(src) == [-7] * 4  # nothing written on error
+
+
+def test_paged_batch_validation(L):
+    """Paged layout: page size a power of two in 16 .. 2^20, a block table with
+    enough pages per sequence; seq_row0 may then be NULL."""
+    f = L.dsa_index_scores
+
+    def call(page_size, table, max_pages, seq_row0=None, reserved=0):
+        b = dsa._CBatch(4, 2, 100, page_size, FAKE, FAKE, seq_row0, table, max_pages, reserved)
+        return f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None)
+
+    if not _gpu():  # valid layouts pass every check; without a GPU the device check answers
+        assert call(16, FAKE, 7) == 7         # 7 * 16 >= 100
+        assert call(64, FAKE, 2) == 7
+    assert call(16, FAKE, 6) == 2             # 96 < 100 tokens
+    assert call(48, FAKE, 4) == 2             # not a power of two
+    assert call(8, FAKE, 16) == 2             # below 16
+    assert call(1 << 21, FAKE, 1) == 2        # above 2^20
+    assert call(-16, FAKE, 7) == 2
+    assert call(16, None, 7) == 1             # block table required
+    assert call(16, FAKE, 7, reserved=1) == 2
+    b = dsa._CBatch(4, 2, 100, 0, FAKE, FAKE, None, FAKE, 7, 0)  # contiguous needs seq_row0
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None) == 1
+
+
+def _gpu():
+    import torch
+    return torch.cuda.is_available()

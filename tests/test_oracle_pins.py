@@ -357,3 +357,23 @@ def test_layer_stack_shared_layer_reuses_source_selection():
         kept = idx[0][t][idx[0][t] >= 0].astype(np.int64)
         dense_sub = _sdpa_rows(inp, t, inp.kv[r0 + kept])
         np.testing.assert_allclose(out[1][t], dense_sub, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------ paged caches
+@pytest.mark.parametrize("page_size", [16, 64, 4096])
+def test_paged_rows_reproduce_the_contiguous_caches(page_size):
+    """Every token's pool row (the oracle's page arithmetic) holds exactly the
+    row the contiguous cache holds (synth scatters page by page); pool rows
+    that no token maps to are the NaN filler."""
+    inp = synth.custom([1000, 17, 4100], [(0, 999), (1, 16), (2, 4099)], seed=23)
+    pc = synth.to_paged(inp, page_size, seed=5)
+    used = np.zeros(pc.k_idx.shape[0], bool)
+    for b, n in enumerate(inp.wl.seq_lens):
+        r0 = int(inp.seq_row0[b])
+        rows = np.array([O.paged_row(pc.block_table[b], page_size, s) for s in range(n)])
+        assert len(set(rows.tolist())) == n
+        np.testing.assert_array_equal(pc.k_idx[rows], inp.k_idx[r0:r0 + n])
+        np.testing.assert_array_equal(pc.kv[rows], inp.kv[r0:r0 + n])
+        used[rows] = True
+    assert np.all(pc.k_idx[~used] == synth.BF16_NAN) and np.all(pc.kv[~used] == synth.BF16_NAN)
+    assert (~used).sum() >= 3 * page_size  # spare pages exist, so a wrong page reads NaN
