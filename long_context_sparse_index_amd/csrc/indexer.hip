@@ -26,8 +26,10 @@ namespace dsa {
 // With `lists` set, the workgroup also counts the top digit of its scores in
 // LDS and writes the slice's sparse bin list for the split top-k.
 // PAGED: the cache is paged (pages of >= 16 tokens, so every 16-key granule of
-// a tile lies in one page); the pages of tile i + 2 are looked up while tile i
-// is computed and kept in a 3-slot LDS ring, so key loads never wait on them.
+// a tile lies in one page).  Chunk c of every thread's tile load lies in
+// granule c; each thread loads the 8 page ids of tile i + 2 into registers
+// while tile i is computed (they complete with the key loads of tile i + 1),
+// so key loads never wait on a lookup.
 constexpr int kScanLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 constexpr int kGranule = 16;           // keys per page-table lookup (smallest page)
 
@@ -40,7 +42,6 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kScanTile * kScanLds];
   __shared__ uint32_t hist[kTkBins / 2];
   __shared__ int wave_tot[4];
-  __shared__ int s_pid[3][kScanTile / kGranule];
   const int t = blockIdx.x;
   const int pos = q_pos[t];
   const int k0 = blockIdx.y * slice_keys;
@@ -51,8 +52,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   const int64_t row0 = PAGED ? 0 : cr.seq_row0[seq];
   const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // page of granule tid (< 8) of a tile (keys past pos: the page of pos)
-  auto pid_load = [&](int tile) { return bt[min(k0 + tile * kScanTile + kGranule * tid, pos) >> cr.page_shift]; };
+  // pages of the 8 granules of a tile (granules past pos: the page of pos)
+  constexpr int kGr = kScanTile / kGranule;
+  auto pid_fetch = [&](int tile, int p[kGr]) {
+#pragma unroll
+    for (int c = 0; c < kGr; ++c) p[c] = bt[min(k0 + tile * kScanTile + kGranule * c, pos) >> cr.page_shift];
+  };
   const int g = lane >> 5, n = lane & 31;
   if (lists) {
 #pragma unroll
@@ -70,16 +75,16 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
   for (int r = 0; r < 16; ++r) wr[r] = bf16_to_f32(w[t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)]);
 
   u32x4 st[8];
-  auto gload = [&](int tile) {
+  // Chunk c covers keys base + 16c + (tid >> 4): granule c.  A key clamped to
+  // pos may be read from another row of granule c's page (never used).
+  auto gload = [&](int tile, const int p[kGr]) {
     const int base = k0 + tile * kScanTile;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int lin = tid + 256 * c;  // 16-byte chunk of the 32 KB tile
       const int key = min(base + (lin >> 4), pos);  // rows past pos: never used
       int64_t row = row0 + key;
-      if (PAGED)
-        row = ((int64_t)s_pid[tile % 3][(key - base) / kGranule] << cr.page_shift) |
-              (key & ((1 << cr.page_shift) - 1));
+      if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (key & ((1 << cr.page_shift) - 1));
       st[c] = ld16_nt(k_idx + row * kIdxDim + (lin & 15) * 8);
     }
   };
@@ -91,23 +96,18 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     }
   };
   float* srow = scores + (int64_t)t * ld;
+  int pa[kGr] = {}, pb[kGr] = {};  // pages of tiles tile + 1 and tile + 2 (PAGED)
   if (PAGED) {
-    if (tid < kScanTile / kGranule) {
-      const int p0 = pid_load(0);
-      const int p1 = ntiles > 1 ? pid_load(1) : 0;
-      s_pid[0][tid] = p0;
-      s_pid[1][tid] = p1;
-    }
-    __syncthreads();
+    pid_fetch(0, pb);
+    if (ntiles > 1) pid_fetch(1, pa);
   }
-  gload(0);
+  gload(0, pb);
   lstore(0);
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
-    if (tile + 1 < ntiles) gload(tile + 1);
-    const bool pref = PAGED && tid < kScanTile / kGranule && tile + 2 < ntiles;
-    const int pnext = pref ? pid_load(tile + 2) : 0;
+    if (tile + 1 < ntiles) gload(tile + 1, pa);
+    if (PAGED && tile + 2 < ntiles) pid_fetch(tile + 2, pb);
     const uint16_t* bp = &ks[buf][(wave * 32 + n) * kScanLds + 8 * g];
     f32x16 acc = {};
 #pragma unroll
@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
       if (lists) hist16_add(hist, score_key(tot));
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
-    if (pref) s_pid[(tile + 2) % 3][tid] = pnext;  // slot of tile - 1, read two barriers ago
+    if (PAGED) {
+#pragma unroll
+      for (int c = 0; c < kGr; ++c) pa[c] = pb[c];
+    }
     __syncthreads();
   }
   if (lists)
@@ -154,7 +157,6 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int T) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kGemmKT * kKeyLds];
   __shared__ int s_seq[kGemmQB], s_pos[kGemmQB];
-  __shared__ int s_pid[3][kGemmKT / kGranule];  // pages of tiles i .. i+2 (as in the scan)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int t0 = blockIdx.x * kGemmQB;
@@ -198,22 +200,24 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int64_t row0 = PAGED ? 0 : cr.seq_row0[sq];
     const int32_t* bt = PAGED ? cr.table + (int64_t)sq * cr.max_pages : nullptr;
     const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
-    auto pid_load = [&](int tile) { return bt[min(kbeg + tile * kGemmKT + kGranule * tid, hi) >> cr.page_shift]; };
-    constexpr int kGran = kGemmKT / kGranule;
-
     // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 2 per thread.
+    // Chunk c covers keys base + 32c + (tid >> 4): granule (tid >> 8) + 2c, whose
+    // page (PAGED) the thread loads two tiles ahead, as the scan does.
     constexpr int kPer = kGemmKT * 16 / kGemmThreads;
+    auto pid_fetch = [&](int tile, int p[kPer]) {
+#pragma unroll
+      for (int c = 0; c < kPer; ++c)
+        p[c] = bt[min(kbeg + tile * kGemmKT + kGranule * ((tid >> 8) + 2 * c), hi) >> cr.page_shift];
+    };
     u32x4 stage[kPer];
-    auto gload = [&](int tile) {
+    auto gload = [&](int tile, const int p[kPer]) {
       const int base = kbeg + tile * kGemmKT;
 #pragma unroll
       for (int c = 0; c < kPer; ++c) {
         const int lin = tid + kGemmThreads * c;
         const int key = min(base + (lin >> 4), hi);
         int64_t row = row0 + key;
-        if (PAGED)
-          row = ((int64_t)s_pid[tile % 3][(key - base) / kGranule] << cr.page_shift) |
-                (key & ((1 << cr.page_shift) - 1));
+        if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (key & ((1 << cr.page_shift) - 1));
         stage[c] = ld16(k_idx + row * kIdxDim + (lin & 15) * 8);
       }
     };
@@ -224,23 +228,18 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
         st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
       }
     };
+    int pa[kPer] = {}, pb[kPer] = {};  // pages of tiles tile + 1 and tile + 2 (PAGED)
     if (PAGED) {
-      if (tid < kGran) {
-        const int p0 = pid_load(0);
-        const int p1 = ntiles > 1 ? pid_load(1) : 0;
-        s_pid[0][tid] = p0;
-        s_pid[1][tid] = p1;
-      }
-      __syncthreads();
+      pid_fetch(0, pb);
+      if (ntiles > 1) pid_fetch(1, pa);
     }
-    gload(0);
+    gload(0, pb);
     lstore(0);
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
       const int buf = tile & 1;
-      if (tile + 1 < ntiles) gload(tile + 1);
-      const bool pref = PAGED && tid < kGran && tile + 2 < ntiles;
-      const int pnext = pref ? pid_load(tile + 2) : 0;
+      if (tile + 1 < ntiles) gload(tile + 1, pa);
+      if (PAGED && tile + 2 < ntiles) pid_fetch(tile + 2, pb);
       const int sbase = kbeg + tile * kGemmKT;
       bf16x8 bfr[2][8];
 #pragma unroll
@@ -269,7 +268,10 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
         }
       }
       if (tile + 1 < ntiles) lstore(buf ^ 1);
-      if (pref) s_pid[(tile + 2) % 3][tid] = pnext;
+      if (PAGED) {
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) pa[c] = pb[c];
+      }
       __syncthreads();
     }
   }
