@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 #define DSA_INDEX_HEADS 32
 #define DSA_INDEX_DIM 128
@@ -87,6 +87,17 @@ typedef enum dsa_status {
 /* Output element type of the attention output. */
 enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
 
+/* Latent-cache row formats (dsa_batch.kv_format).
+ *   DSA_KV_BF16: 576 bf16 (512 latent | 64 rope), 1152 bytes.
+ *   DSA_KV_INT4: 400 bytes (page 3, "GLM-5 7440亿参数，202K长上下文突破极限", section 六:
+ *     INT4 KV-cache quantisation): bytes 0..255 the 512 latent values as 4-bit
+ *     two's complement codes (element 2i in the low nibble of byte i); bytes
+ *     256..271 eight bf16 scales, scale g for elements 64g .. 64g+63; bytes
+ *     272..399 the 64 rope values in bf16.  Latent value = code * scale.
+ *     dsa_quantize_kv_int4 writes this format. */
+enum { DSA_KV_BF16 = 0, DSA_KV_INT4 = 1 };
+#define DSA_KV_INT4_ROW_BYTES 400
+
 /* Operation ids for dsa_workspace_bytes. */
 enum { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_FORWARD = 3 };
 
@@ -106,7 +117,7 @@ typedef struct dsa_batch {
                                 [j*page_size, (j+1)*page_size) of sequence b at [b*max_pages + j];
                                 ignored when contiguous */
   int32_t max_pages;         /* paged: >= ceil(max_ctx / page_size); ignored when contiguous */
-  int32_t reserved;          /* must be 0 */
+  int32_t kv_format;         /* DSA_KV_BF16 or DSA_KV_INT4: row format of kv (the indexer keys are bf16) */
 } dsa_batch;
 
 /*
@@ -153,14 +164,16 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  * Computed in weight-absorbed form: q_lat = W_UK[h] q_nope (rounded to bf16),
  * logits against the latent, online softmax in fp32, the latent-weighted sum
  * (rounded to bf16) up-projected by W_UV[h]; fp32 accumulation throughout.
- *   q_nope [T,64,192], q_rope [T,64,64], kv [rows,576], w_uk [64,512,192],
- *   w_uv [64,512,256]: bf16.  idx [T,k] int32 (-1 = absent; any order).
+ *   q_nope [T,64,192], q_rope [T,64,64], w_uk [64,512,192], w_uv [64,512,256]:
+ *   bf16.  kv: [rows,576] bf16, or [rows,400] bytes when batch->kv_format is
+ *   DSA_KV_INT4 (the latent is then dequantised, code * scale, and rounded to
+ *   bf16 as it is gathered).  idx [T,k] int32 (-1 = absent; any order).
  *   out [T,64,256]: bf16 (out_dtype DSA_OUT_BF16) or fp32 (DSA_OUT_F32).
  *   A query with no valid entry gets a zero output.
  *   ws: dsa_workspace_bytes(DSA_OP_SPARSE_MLA, T, max_ctx, k) bytes.
  */
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
-                               const dsa_bf16* q_rope, const dsa_bf16* kv,
+                               const dsa_bf16* q_rope, const void* kv,
                                const dsa_bf16* w_uk, const dsa_bf16* w_uv, const int32_t* idx,
                                int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                                void* ws, size_t ws_bytes, void* stream);
@@ -175,9 +188,21 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
  */
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
                        const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
-                       const dsa_bf16* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                       const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * INT4 latent cache (page 3, section 六; format at DSA_KV_INT4): quantises
+ * `rows` bf16 cache rows kv [rows,576] into kv_int4 [rows,400] bytes.  Per
+ * group of 64 latent values: scale = bf16(absmax / 7) and code =
+ * clamp(rint(x / scale), -7, 7), both divisions correctly rounded in fp32,
+ * ties to even (scale 0 gives code 0); rope copied.  Bit-exact.  Both arrays
+ * device, 16-byte aligned, not overlapping; rows 0 .. 2^40 (0: nothing
+ * enqueued).  Errors: DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_ALIGN, DSA_ERR_DEVICE,
+ * DSA_ERR_LAUNCH.
+ */
+dsa_status dsa_quantize_kv_int4(const dsa_bf16* kv, int64_t rows, uint8_t* kv_int4, void* stream);
 
 /*
  * IndexShare layer schedule (page 5, IndexShare section and the config fields

@@ -54,8 +54,8 @@ int page_shift(int32_t page_size) {
 dsa_status check_batch(const dsa_batch* b) {
   if (!b) return DSA_ERR_NULL;
   if (b->num_queries < 0 || b->num_queries > kMaxQueries) return DSA_ERR_SHAPE;
-  if (b->num_seqs < 1 || b->max_ctx < 1 || b->max_ctx > kMaxCtx || b->reserved != 0)
-    return DSA_ERR_SHAPE;
+  if (b->num_seqs < 1 || b->max_ctx < 1 || b->max_ctx > kMaxCtx) return DSA_ERR_SHAPE;
+  if (b->kv_format != DSA_KV_BF16 && b->kv_format != DSA_KV_INT4) return DSA_ERR_UNSUPPORTED;
   if (b->page_size != 0) {
     if (page_shift(b->page_size) == 0) return DSA_ERR_SHAPE;
     if (b->max_pages < 1 || (int64_t)b->max_pages * b->page_size < b->max_ctx) return DSA_ERR_SHAPE;
@@ -91,6 +91,7 @@ dsa::LaunchBatch to_launch(const dsa_batch* b, int t0, int T) {
   lb.rows.table = b->page_size == 0 ? nullptr : b->block_table;
   lb.rows.page_shift = b->page_size == 0 ? 0 : page_shift(b->page_size);
   lb.rows.max_pages = b->page_size == 0 ? 0 : b->max_pages;
+  lb.kv_int4 = b->kv_format == DSA_KV_INT4;
   return lb;
 }
 
@@ -157,6 +158,17 @@ size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int
   }
 }
 
+dsa_status dsa_quantize_kv_int4(const dsa_bf16* kv, int64_t rows, uint8_t* kv_int4, void* stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 40)) return DSA_ERR_SHAPE;
+  if (rows == 0) return DSA_OK;
+  if (!kv || !kv_int4) return DSA_ERR_NULL;
+  if (!aligned16(kv) || !aligned16(kv_int4)) return DSA_ERR_ALIGN;
+  dsa_status s = check_device();
+  if (s != DSA_OK) return s;
+  (void)hipGetLastError();
+  return launch_status(dsa::launch_quantize_kv_int4(kv, rows, kv_int4, (hipStream_t)stream));
+}
+
 dsa_status dsa_index_share_schedule(int32_t num_layers, int32_t num_dense, int32_t index_topk_freq,
                                     int32_t* source) {
   if (!source) return DSA_ERR_NULL;
@@ -212,7 +224,7 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
 }
 
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
-                               const dsa_bf16* q_rope, const dsa_bf16* kv,
+                               const dsa_bf16* q_rope, const void* kv,
                                const dsa_bf16* w_uk, const dsa_bf16* w_uv, const int32_t* idx,
                                int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                                void* ws, size_t ws_bytes, void* stream) {
@@ -240,7 +252,7 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
 
 dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
                        const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
-                       const dsa_bf16* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                       const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   dsa_status s = check_batch(batch);

@@ -15,6 +15,12 @@ constexpr int kQk = kNope + kRope;    // 256
 constexpr int kV = 256;
 constexpr int kLat = 512;
 constexpr int kRow = kLat + kRope;    // 576 bf16 per latent-cache row
+// INT4 latent-cache row: 256 B of codes (element 2i in the low nibble of byte
+// i, two's complement), 8 bf16 group scales (groups of 64), 64 bf16 rope.
+constexpr int kQ4Group = 64;
+constexpr int kQ4ScaleOff = kLat / 2;                       // 256
+constexpr int kQ4RopeOff = kQ4ScaleOff + 2 * kLat / kQ4Group;  // 272
+constexpr int kQ4Row = kQ4RopeOff + 2 * kRope;              // 400 bytes
 constexpr int kMaxTopk = 8192;    // largest index_topk accepted
 constexpr int kTopkSmall = 2048;  // index_topk of the configuration tables; kernels specialise up to it
 
@@ -39,6 +45,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two fp32 -> packed bf16 (lo in bits 0..15), one hardware conversion
+// (round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {

@@ -23,8 +23,12 @@ struct LaunchBatch {
   const int32_t* q_seq;    // [T] device
   const int32_t* q_pos;    // [T] device
   CacheRows rows;
+  bool kv_int4;            // latent cache rows are INT4 (400 B) instead of bf16 (1152 B)
   bool paged() const { return rows.page_shift != 0; }
 };
+
+// INT4 latent cache: quantise `rows` bf16 cache rows into 400-byte rows.
+hipError_t launch_quantize_kv_int4(const uint16_t* kv, int64_t rows, uint8_t* out, hipStream_t st);
 
 // Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries;
 // else the per-query key scan, which also writes the split top-k's slice bin
@@ -56,7 +60,7 @@ struct MlaPlan {
 };
 MlaPlan plan_mla(int T, int k);
 hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
-                             const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
+                             const uint16_t* q_rope, const void* kv, const uint16_t* w_uk,
                              const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
                              int out_f32, void* ws, bool q_lat_ready, hipStream_t st);
 

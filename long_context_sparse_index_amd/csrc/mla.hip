@@ -64,6 +64,40 @@ constexpr int kPartSlab = kHeads * kLat;  // floats of one split partial
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
 
+// INT4 cache (Q4): raw 400-byte rows of a tile are gathered into a 3-slot
+// ring (800 chunks of 16 B: 2 loads per wave per tile, the second of wave 4
+// half in the padding, waves 5-7 repeating their first) and expanded into one
+// of two bf16 tiles of the layout above before QK (one extra barrier per tile).
+constexpr int kQ4Chunks = kKT * kQ4Row / 16;        // 800
+constexpr int kQ4RawBytes = 13 * 64 * 16;           // 832 chunks: padding for wave 4's second load
+
+// Thread tid expands latent elements 32j .. 32j+31 of row r = tid / 16
+// (j = tid % 16) and, for tid < 256, rope slot tid % 8 of row tid / 8.
+__device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tb) {
+  const int tid = threadIdx.x;
+  const int r = tid >> 4, j = tid & 15;
+  const uint8_t* rb = raw + r * kQ4Row;
+  const u32x4 c = *reinterpret_cast<const u32x4*>(rb + 16 * j);
+  const float sc = bf16_to_f32(*reinterpret_cast<const uint16_t*>(rb + kQ4ScaleOff + 2 * (j >> 1)));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // dword w: elements 32j + 8w + e in nibble e
+    const uint32_t d = c[w];
+    u32x4 v;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float x0 = (float)((int32_t)(d << (28 - 8 * m)) >> 28) * sc;
+      const float x1 = (float)((int32_t)(d << (24 - 8 * m)) >> 28) * sc;
+      v[m] = cvt_pk_bf16(x0, x1);
+    }
+    *reinterpret_cast<u32x4*>(tb + swz(r, 4 * j + w) * 8) = v;
+  }
+  if (tid < kKT * 8) {
+    const int rr = tid >> 3, i = tid & 7;
+    *reinterpret_cast<u32x4*>(tb + swz(rr, kLat / 8 + i) * 8) =
+        *reinterpret_cast<const u32x4*>(raw + rr * kQ4Row + kQ4RopeOff + 16 * i);
+  }
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -75,18 +109,21 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool Q4>
 __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr,
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_rope,
-    const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int k, float scale_log2,
+    const void* __restrict__ kv_v, const int32_t* __restrict__ idx, int k, float scale_log2,
     int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
     float* __restrict__ ml_part) {
   // Three distinct arrays (not one indexed array): the compiler then waits
   // only for the direct-to-LDS loads that target the array being read.
   __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileSlots * 8];
   __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileSlots * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileSlots * 8];  // (not used by Q4)
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[kQ4RawBytes];       // (Q4 only)
+  __shared__ __attribute__((aligned(16))) uint8_t raw1[kQ4RawBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t raw2[kQ4RawBytes];
   __shared__ __attribute__((aligned(16))) uint16_t pT[kHeads * kPLds];
   __shared__ float s_max[2][kHeads];
   __shared__ float s_alpha[kHeads];
@@ -105,7 +142,11 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // s_idx holds pool rows (< 2^31) and offsets are 64-bit.  Absent entries
   // hold ~r for the row r of position 0 (finite data, masked later).
   const int seq = q_seq[t];
-  const uint16_t* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kRow;
+  // row stride in elements of the gather's unit: bf16 (576) or bytes (Q4: 400)
+  using Unit = typename std::conditional<Q4, uint8_t, uint16_t>::type;
+  constexpr int kStride = Q4 ? kQ4Row : kRow;
+  const Unit* const kv = static_cast<const Unit*>(kv_v);
+  const Unit* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kStride;
   const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
   const int32_t* irow = idx + (int64_t)t * k;
   const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
@@ -165,30 +206,45 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // logical column (pc & ~7) | ((pc ^ row) & 7) of its row (the swizzle is an
   // involution within groups of 8), so the lane fetches that chunk.  Row and
   // column of each lane's five chunks are the same for every tile.
-  int g_row[5];
-  uint32_t g_col[5];
+  // Q4: 2 loads per wave; instruction i of wave w covers chunks
+  // [(8i + w) * 64, +64) for i = 0 and for i = 1, w < 5 (chunks past 799, in
+  // the padding, fetch chunk 799); waves 5-7 repeat their first load.
+  constexpr int kNL = Q4 ? 2 : 5;  // gather loads per wave per tile
+  int g_row[kNL];
+  uint32_t g_col[kNL];
+  auto blk_of = [&](int i) {
+    if (Q4) return (i == 0 || wave >= 5) ? wave : 8 + wave;
+    return i < 4 ? 8 * i + wave : 32 + (wave & 3);
+  };
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
-    const int lin = blk * 64 + lane;  // physical slot, < 2304
-    const int r = lin / kSlots, pc = lin - r * kSlots;
-    g_row[i] = r;
-    g_col[i] = (uint32_t)((pc & ~7) | ((pc ^ r) & 7)) * 8u;
+  for (int i = 0; i < kNL; ++i) {
+    const int lin = blk_of(i) * 64 + lane;
+    if (Q4) {
+      const int c = min(lin, kQ4Chunks - 1);
+      g_row[i] = c / (kQ4Row / 16);
+      g_col[i] = (uint32_t)(c - g_row[i] * (kQ4Row / 16)) * 16u;  // bytes
+    } else {  // physical slot lin < 2304 holds logical column (pc & ~7) | ((pc ^ row) & 7)
+      const int r = lin / kSlots, pc = lin - r * kSlots;
+      g_row[i] = r;
+      g_col[i] = (uint32_t)((pc & ~7) | ((pc ^ r) & 7)) * 8u;
+    }
   }
-  auto gather_idx = [&](int tt, int sidx[5], int& valid) {
+  auto gather_idx = [&](int tt, int sidx[kNL], int& valid) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) sidx[i] = s_idx[tt * kKT + g_row[i]];
+    for (int i = 0; i < kNL; ++i) sidx[i] = s_idx[tt * kKT + g_row[i]];
     valid = tid < kKT ? s_idx[tt * kKT + tid] : -1;
   };
-  auto gather_issue = [&](const int sidx[5], int valid, uint16_t* dstt, int buf) {
+  auto gather_issue = [&](const int sidx[kNL], int valid, void* dstt, int buf) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int blk = i < 4 ? 8 * i + wave : 32 + (wave & 3);
+    for (int i = 0; i < kNL; ++i) {
       // absent keys (and tiles past the end) fetch the row of position 0: finite data, masked later
       const int r = sidx[i] >= 0 ? sidx[i] : ~sidx[i];
-      const uint16_t* src = PAGED ? kv_seq + (int64_t)r * kRow + g_col[i]
-                                  : kv_seq + ((uint32_t)r * (uint32_t)kRow + g_col[i]);
-      __builtin_amdgcn_global_load_lds(src, dstt + blk * 64 * 8, 16, 0, 0);
+      const Unit* src = PAGED ? kv_seq + (int64_t)r * kStride + g_col[i]
+                              : kv_seq + ((uint32_t)r * (uint32_t)kStride + g_col[i]);
+      // (named pointers: the host pass rejects cast expressions as this builtin's operands)
+      uint16_t* const dst = static_cast<uint16_t*>(dstt) + blk_of(i) * 64 * 8;
+      const uint16_t* const gsrc = reinterpret_cast<const uint16_t*>(src);
+      __builtin_amdgcn_global_load_lds(gsrc, dst, 16, 0, 0);
     }
     if (tid < kKT) s_valid[buf][tid] = valid >= 0;
   };
@@ -205,29 +261,37 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // its barrier, into the slot that step tt - 1 used: every wave has passed
   // that barrier, so no wave still reads the slot.  One tile (5 loads per wave)
   // is then in flight at each wait.
+  auto slot = [&](int b) -> void* {
+    if (Q4) return b == 0 ? (void*)raw0 : (b == 1 ? (void*)raw1 : (void*)raw2);
+    return b == 0 ? (void*)tile0 : (b == 1 ? (void*)tile1 : (void*)tile2);
+  };
   {
-    int sidx[5], valid;
+    int sidx[kNL], valid;
     gather_idx(0, sidx, valid);
-    gather_issue(sidx, valid, tile0, 0);
+    gather_issue(sidx, valid, slot(0), 0);
     gather_idx(1, sidx, valid);
-    gather_issue(sidx, valid, tile1, 1);
+    gather_issue(sidx, valid, slot(1), 1);
   }
-  // Vector loads complete in issue order: with the 10 gather loads of this
-  // wave the most recent, vmcnt <= 10 means the query operands are in place.
-  wait_vm<10>();
+  // Vector loads complete in issue order: with the 2 kNL gather loads of this
+  // wave the most recent, vmcnt <= 2 kNL means the query operands are in place.
+  wait_vm<2 * kNL>();
 
   auto step = [&](int tt, auto BUFC) {
     constexpr int buf = decltype(BUFC)::value;
     constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (used by step tt - 1)
-    uint16_t* const tbw = buf == 0 ? tile0 : (buf == 1 ? tile1 : tile2);
-    uint16_t* const nbw = nbuf == 0 ? tile0 : (nbuf == 1 ? tile1 : tile2);
-    int sidx[5], valid;
+    int sidx[kNL], valid;
     gather_idx(tt + 2, sidx, valid);  // positions are static: read ahead of the barrier
-    wait_vm<5>();
+    wait_vm<kNL>();
     lds_barrier();
-    gather_issue(sidx, valid, nbw, nbuf);
+    gather_issue(sidx, valid, slot(nbuf), nbuf);
     if (tt < ntiles) {
-    const uint16_t* tb = tbw;
+    // Q4: bf16 tile tt & 1 was last read in step tt - 2, before this step's barrier
+    uint16_t* const tbq = (tt & 1) ? tile1 : tile0;
+    if (Q4) {
+      dequant_tile(static_cast<const uint8_t*>(slot(buf)), tbq);
+      lds_barrier();
+    }
+    const uint16_t* tb = Q4 ? tbq : static_cast<const uint16_t*>(slot(buf));
     int vmask[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[buf][hf * 16 + 4 * g + jj];
@@ -604,7 +668,7 @@ MlaPlan plan_mla(int T, int k) {
 }
 
 hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint16_t* q_nope,
-                             const uint16_t* q_rope, const uint16_t* kv, const uint16_t* w_uk,
+                             const uint16_t* q_rope, const void* kv, const uint16_t* w_uk,
                              const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
                              int out_f32, void* ws, bool q_lat_ready, hipStream_t st) {
   char* base = static_cast<char*>(ws);
@@ -622,14 +686,20 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     if (e != hipSuccess) return e;
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  if (b.paged())
-    mla_core_kernel<true><<<dim3(T, p.splits), kCoreThreads, 0, st>>>(
-        b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k, scale_log2, p.keys_per_split, p.splits, o_lat,
-        o_part, ml_part);
+  const dim3 grid(T, p.splits);
+  const int kps = p.keys_per_split, S = p.splits;
+  if (b.paged() && b.kv_int4)
+    mla_core_kernel<true, true><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
+                                                               scale_log2, kps, S, o_lat, o_part, ml_part);
+  else if (b.paged())
+    mla_core_kernel<true, false><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
+                                                                scale_log2, kps, S, o_lat, o_part, ml_part);
+  else if (b.kv_int4)
+    mla_core_kernel<false, true><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
+                                                                scale_log2, kps, S, o_lat, o_part, ml_part);
   else
-    mla_core_kernel<false><<<dim3(T, p.splits), kCoreThreads, 0, st>>>(
-        b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k, scale_log2, p.keys_per_split, p.splits, o_lat,
-        o_part, ml_part);
+    mla_core_kernel<false, false><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
+                                                                 scale_log2, kps, S, o_lat, o_part, ml_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {

@@ -25,6 +25,8 @@ DEFAULT_SCALE = 1.0 / 16.0
 OP_INDEX_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_FORWARD = 0, 1, 2, 3
 NO_WORKSPACE = "no-workspace"  # dsa_topk(ws=NO_WORKSPACE): pass NULL (one workgroup per row)
 OUT_BF16, OUT_F32 = 0, 1
+KV_BF16, KV_INT4 = 0, 1
+KV_INT4_ROW_BYTES = 400
 
 
 class DsaError(RuntimeError):
@@ -45,7 +47,7 @@ class _CBatch(ctypes.Structure):
         ("seq_row0", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("max_pages", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -61,6 +63,7 @@ _SIGS = {
     "dsa_forward": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                      _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "dsa_index_share_schedule": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P], ctypes.c_int),
+    "dsa_quantize_kv_int4": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int),
     "dsa_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], ctypes.c_size_t),
     "dsa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "dsa_abi_version": ([], ctypes.c_int32),
@@ -116,10 +119,11 @@ class Batch:
     """Batch geometry: q_seq [T] int32 and q_pos [T] int32 on the device, and the
     cache layout: contiguous (seq_row0 [B] int64: first cache row of each
     sequence) or paged (block_table [B, max_pages] int32 page ids and
-    page_size tokens per page; seq_row0 then None)."""
+    page_size tokens per page; seq_row0 then None), and the latent cache's row
+    format (KV_BF16: [rows, 576] bf16; KV_INT4: [rows, 400] uint8)."""
 
     def __init__(self, q_seq: torch.Tensor, q_pos: torch.Tensor, seq_row0: Optional[torch.Tensor], max_ctx: int,
-                 block_table: Optional[torch.Tensor] = None, page_size: int = 0):
+                 block_table: Optional[torch.Tensor] = None, page_size: int = 0, kv_format: int = KV_BF16):
         for name, x, dt in (("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32)):
             if x.dtype != dt or not x.is_cuda or not x.is_contiguous() or x.dim() != 1:
                 raise ValueError(f"{name}: expected a contiguous 1-D {dt} device tensor")
@@ -137,17 +141,38 @@ class Batch:
             self.B = int(seq_row0.shape[0])
         self.q_seq, self.q_pos, self.seq_row0 = q_seq, q_pos, seq_row0
         self.block_table, self.page_size = block_table, int(page_size)
+        self.kv_format = int(kv_format)
         self.max_ctx = int(max_ctx)
         self.T = int(q_seq.shape[0])
 
     def c(self) -> _CBatch:
         mp = int(self.block_table.shape[1]) if self.page_size else 0
         return _CBatch(self.T, self.B, self.max_ctx, self.page_size, _ptr(self.q_seq), _ptr(self.q_pos),
-                       _ptr(self.seq_row0), _ptr(self.block_table), mp, 0)
+                       _ptr(self.seq_row0), _ptr(self.block_table), mp, self.kv_format)
 
     def slice(self, t0: int, t1: int) -> "Batch":
         return Batch(self.q_seq[t0:t1], self.q_pos[t0:t1], self.seq_row0, self.max_ctx, self.block_table,
-                     self.page_size)
+                     self.page_size, self.kv_format)
+
+
+def _kv(batch: "Batch", kv: torch.Tensor) -> torch.Tensor:
+    if batch.kv_format == KV_INT4:
+        if kv.dtype != torch.uint8 or not kv.is_cuda or not kv.is_contiguous() or kv.dim() != 2 \
+                or kv.shape[1] != KV_INT4_ROW_BYTES:
+            raise ValueError(f"kv: expected a contiguous [rows, {KV_INT4_ROW_BYTES}] uint8 device tensor (INT4 rows)")
+        return kv
+    return _bf16(kv, "kv", None)
+
+
+def dsa_quantize_kv_int4(kv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 latent-cache rows [rows, 576] -> INT4 rows [rows, 400] uint8."""
+    _bf16(kv, "kv", None)
+    if kv.dim() != 2 or kv.shape[1] != D_KV:
+        raise ValueError("kv: expected [rows, 576]")
+    if out is None:
+        out = torch.empty((kv.shape[0], KV_INT4_ROW_BYTES), dtype=torch.uint8, device=kv.device)
+    _check("dsa_quantize_kv_int4", lib().dsa_quantize_kv_int4(_ptr(kv), kv.shape[0], _ptr(out), _stream()))
+    return out
 
 
 def score_ld(max_ctx: int) -> int:
@@ -208,7 +233,7 @@ def dsa_sparse_mla_attn(batch: Batch, q_nope, q_rope, kv, w_uk, w_uv, idx: torch
     T = batch.T
     _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
     _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
-    _bf16(kv, "kv", None)
+    _kv(batch, kv)
     _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
     _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
     if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != T or not idx.is_contiguous():
@@ -238,7 +263,7 @@ def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k
     _bf16(k_idx, "k_idx", None)
     _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
     _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
-    _bf16(kv, "kv", None)
+    _kv(batch, kv)
     _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
     _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
     od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16

@@ -37,6 +37,13 @@ design notes of the repository):
   * paged caches: token s of a sequence sits in page s // P of that
     sequence's page list, at offset s % P (page-table indirection is storage
     only; every computation above reads the same rows).
+  * INT4 latent cache ([G5] section six recommends INT4 KV-cache quantisation
+    and a saving above 60%, no format): per cache row, the 512 latent values
+    in 8 groups of 64, each with scale s = bf16(absmax / 7) and codes
+    q = clamp(rint(x / s), -7, 7) (fp32 division, ties to even, both decided
+    in fp32 as the kernel does); the 64 rope values stay bf16.  400 bytes per
+    row: 256 bytes of codes (element 2i in the low nibble of byte i, two's
+    complement), 8 bf16 scales, 64 bf16 rope.  Dequantised latent = q * s.
   * MLA over the kept rows with explicit per-head up-projection
     K_nope = c @ W_UK[h], V = c @ W_UV[h]; logits (q_nope.K_nope + q_rope.r)
     times softmax_scale (1/sqrt(192+64) = 1/16 by default); softmax in full.
@@ -140,6 +147,23 @@ def mla_explicit(q_nope_t, q_rope_t, kv_rows, w_uk, w_uv,
         e = np.exp(z - z.max())
         p = e / e.sum()
         out[h] = p @ v
+    return out
+
+
+def mla_explicit_f64(q_nope_t, q_rope_t, rows, w_uk, w_uv, scale: float = DEFAULT_SCALE) -> np.ndarray:
+    """``mla_explicit`` over cache rows already given as float64 [n,576] (e.g.
+    dequantised INT4 rows); queries and weights are bf16 bit patterns."""
+    qn = bf16_bits_to_f64(q_nope_t)
+    qr = bf16_bits_to_f64(q_rope_t)
+    c = rows[:, :KV_LORA_RANK]
+    r = rows[:, KV_LORA_RANK:]
+    wuk = bf16_bits_to_f64(w_uk)
+    wuv = bf16_bits_to_f64(w_uv)
+    out = np.empty((NUM_HEADS, V_HEAD_DIM))
+    for h in range(NUM_HEADS):
+        z = (c @ wuk[h] @ qn[h] + r @ qr[h]) * scale
+        e = np.exp(z - z.max())
+        out[h] = (e / e.sum()) @ (c @ wuv[h])
     return out
 
 
@@ -285,3 +309,55 @@ def paged_row(page_list, page_size: int, s: int) -> int:
     """
     page, offset = divmod(int(s), int(page_size))
     return int(page_list[page]) * int(page_size) + offset
+
+
+# ---------------------------------------------------------------- INT4 latent cache
+INT4_GROUP = 64
+INT4_ROW_BYTES = KV_LORA_RANK // 2 + 2 * (KV_LORA_RANK // INT4_GROUP) + 2 * QK_ROPE_HEAD_DIM  # 400
+
+
+def _f32_to_bf16_bits(x):
+    """fp32 -> bf16 bits, round to nearest even (finite values)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def quantize_kv_int4(kv_rows) -> np.ndarray:
+    """bf16 cache rows [n,576] -> INT4 rows [n,400] uint8 (format above).
+
+    Per group of 64 latent values: absmax in fp32 (exact for bf16 inputs), the
+    scale is that divided by 7 in fp32 and rounded to bf16; each code is the
+    value divided by the (bf16) scale in fp32, rounded half to even and clamped
+    to [-7, 7]; a zero scale gives zero codes.
+    """
+    rows = np.asarray(kv_rows, dtype=np.uint16)
+    n = rows.shape[0]
+    x = bf16_bits_to_f64(rows[:, :KV_LORA_RANK]).astype(np.float32).reshape(n, -1, INT4_GROUP)
+    absmax = np.abs(x).max(axis=2)                                   # [n, 8] fp32
+    scale_bits = _f32_to_bf16_bits(absmax / np.float32(7.0))         # fp32 division, then bf16
+    scale = bf16_bits_to_f64(scale_bits).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(scale[:, :, None] > 0, np.rint(x / scale[:, :, None]), np.float32(0))
+    q = np.clip(q, -7, 7).astype(np.int8).reshape(n, KV_LORA_RANK)
+    nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    out = np.empty((n, INT4_ROW_BYTES), dtype=np.uint8)
+    out[:, : KV_LORA_RANK // 2] = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    out[:, KV_LORA_RANK // 2: KV_LORA_RANK // 2 + 16] = scale_bits.astype("<u2").view(np.uint8).reshape(n, 16)
+    out[:, KV_LORA_RANK // 2 + 16:] = rows[:, KV_LORA_RANK:].astype("<u2").view(np.uint8).reshape(n, 128)
+    return out
+
+
+def dequantize_kv_int4(q_rows) -> np.ndarray:
+    """INT4 rows [n,400] -> float64 [n,576]: latent q * scale (exact), rope as stored."""
+    b = np.asarray(q_rows, dtype=np.uint8)
+    n = b.shape[0]
+    codes = b[:, : KV_LORA_RANK // 2]
+    lo = (codes & 0xF).astype(np.int16)
+    hi = (codes >> 4).astype(np.int16)
+    q = np.empty((n, KV_LORA_RANK), dtype=np.int16)
+    q[:, 0::2] = np.where(lo > 7, lo - 16, lo)
+    q[:, 1::2] = np.where(hi > 7, hi - 16, hi)
+    scales = bf16_bits_to_f64(b[:, 256:272].copy().view("<u2").reshape(n, 8))
+    rope = bf16_bits_to_f64(b[:, 272:400].copy().view("<u2").reshape(n, 64))
+    lat = q.reshape(n, 8, INT4_GROUP).astype(np.float64) * scales[:, :, None]
+    return np.concatenate([lat.reshape(n, KV_LORA_RANK), rope], axis=1)

@@ -17,7 +17,7 @@ FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced here
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dsa_abi_version() == 2
+    assert L.dsa_abi_version() == 3
     for s in range(8):
         assert L.dsa_status_string(s)
     assert L.dsa_status_string(99) == b"unknown status"
@@ -58,8 +58,8 @@ def test_index_scores_validation(L):
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
     bad = _batch(B=0)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
-    bad = dsa._CBatch(4, 1, 100, 0, FAKE, FAKE, FAKE, None, 0, 3)  # reserved != 0
-    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 2
+    bad = dsa._CBatch(4, 1, 100, 0, FAKE, FAKE, FAKE, None, 0, 3)  # unknown kv_format
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 5
     bad = dsa._CBatch(4, 1, 100, 0, None, FAKE, FAKE)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 100, None) == 1
     empty = _batch(T=0)
@@ -143,8 +143,8 @@ def test_paged_batch_validation(L):
     enough pages per sequence; seq_row0 may then be NULL."""
     f = L.dsa_index_scores
 
-    def call(page_size, table, max_pages, seq_row0=None, reserved=0):
-        b = dsa._CBatch(4, 2, 100, page_size, FAKE, FAKE, seq_row0, table, max_pages, reserved)
+    def call(page_size, table, max_pages, seq_row0=None, kv_format=0):
+        b = dsa._CBatch(4, 2, 100, page_size, FAKE, FAKE, seq_row0, table, max_pages, kv_format)
         return f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None)
 
     if not _gpu():  # valid layouts pass every check; without a GPU the device check answers
@@ -156,7 +156,7 @@ def test_paged_batch_validation(L):
     assert call(1 << 21, FAKE, 1) == 2        # above 2^20
     assert call(-16, FAKE, 7) == 2
     assert call(16, None, 7) == 1             # block table required
-    assert call(16, FAKE, 7, reserved=1) == 2
+    assert call(16, FAKE, 7, kv_format=2) == 5
     b = dsa._CBatch(4, 2, 100, 0, FAKE, FAKE, None, FAKE, 7, 0)  # contiguous needs seq_row0
     assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 100, None) == 1
 
@@ -164,3 +164,14 @@ def test_paged_batch_validation(L):
 def _gpu():
     import torch
     return torch.cuda.is_available()
+
+
+def test_quantize_kv_int4_validation(L):
+    f = L.dsa_quantize_kv_int4
+    assert f(FAKE, 0, FAKE, None) == 0          # empty: nothing enqueued
+    assert f(FAKE, -1, FAKE, None) == 2
+    assert f(FAKE, (1 << 40) + 1, FAKE, None) == 2
+    assert f(None, 4, FAKE, None) == 1
+    assert f(FAKE, 4, None, None) == 1
+    assert f(FAKE + 8, 4, FAKE, None) == 3
+    assert f(FAKE, 4, FAKE + 4, None) == 3

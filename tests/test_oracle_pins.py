@@ -377,3 +377,48 @@ def test_paged_rows_reproduce_the_contiguous_caches(page_size):
         used[rows] = True
     assert np.all(pc.k_idx[~used] == synth.BF16_NAN) and np.all(pc.kv[~used] == synth.BF16_NAN)
     assert (~used).sum() >= 3 * page_size  # spare pages exist, so a wrong page reads NaN
+
+
+# ------------------------------------------------------------------ INT4 latent cache
+def test_int4_cache_hand_worked_row(golden_dir):
+    """Scales, codes (with ties to even and clamping), nibble order and the
+    400-byte layout against a row worked by hand."""
+    g = json.load(open(os.path.join(golden_dir, "int4_cache.json")))
+    lat = np.concatenate([np.asarray([float(v) for v in grp], np.float32) for grp in g["latent_groups"]])
+    rope = np.asarray([float(v) for v in g["rope"]], np.float32)
+    row = _bits(np.concatenate([lat, rope]))[None, :]
+    q = O.quantize_kv_int4(row)[0]
+    assert q.shape == (g["row_bytes"],)
+    scales = q[256:272].copy().view("<u2")
+    assert [f"0x{int(v):04X}" for v in scales] == g["expected_scale_bits"]
+    for off, hexs in g["expected_code_bytes_hex"].items():  # byte offsets of groups 0 and 2
+        o = int(off)
+        assert bytes(q[o: o + len(hexs) // 2]).hex().upper() == hexs
+    assert np.array_equal(q[272:400].copy().view("<u2"), row[0, 512:])   # rope verbatim
+    d = O.dequantize_kv_int4(q[None, :])[0]
+    sc = np.asarray([int(v, 16) for v in g["expected_scale_bits"]], np.uint16)
+    want = np.concatenate([np.asarray(c, np.float64) * O.bf16_bits_to_f64(s) for c, s in
+                           zip(g["expected_codes"], sc)])
+    np.testing.assert_array_equal(d[:512], want)
+    np.testing.assert_array_equal(d[512:], rope.astype(np.float64))
+    assert 1 - g["row_bytes"] / g["bf16_row_bytes"] > g["page_min_saving"]
+
+
+def test_int4_cache_error_bound_and_exact_grid():
+    """Random rows: |x - q s| <= s/2 plus the clamp slack of the rounded scale;
+    values already on a bf16 grid k*s (|k| <= 7, absmax 7s) come back exactly."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((40, 576)).astype(np.float32)
+    rows = _bits(x)
+    xs = O.bf16_bits_to_f64(rows)
+    q = O.quantize_kv_int4(rows)
+    d = O.dequantize_kv_int4(q)
+    sc = O.bf16_bits_to_f64(q[:, 256:272].copy().view("<u2")).repeat(64, axis=1)
+    err = np.abs(d[:, :512] - xs[:, :512])
+    assert np.all(err <= 0.5 * sc + np.abs(xs[:, :512]) * 2 ** -8 + 1e-12)
+    np.testing.assert_array_equal(d[:, 512:], xs[:, 512:])
+    k = rng.integers(-7, 8, size=(8, 512)).astype(np.float32)
+    k[:, ::64] = 7  # absmax 7 in every group -> scale 1, scaled by a power of two below
+    grid = _bits(np.concatenate([k * np.float32(0.25), np.zeros((8, 64), np.float32)], axis=1))
+    np.testing.assert_array_equal(O.dequantize_kv_int4(O.quantize_kv_int4(grid))[:, :512],
+                                  O.bf16_bits_to_f64(grid)[:, :512])
