@@ -64,21 +64,25 @@ constexpr int kPartSlab = kHeads * kLat;  // floats of one split partial
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
 
-// INT4 cache (Q4): raw 400-byte rows of a tile are gathered into a 3-slot
-// ring (800 chunks of 16 B: 2 loads per wave per tile, the second of wave 4
-// half in the padding, waves 5-7 repeating their first) and expanded into one
-// of two bf16 tiles of the layout above before QK (one extra barrier per tile).
-constexpr int kQ4Chunks = kKT * kQ4Row / 16;        // 800
-constexpr int kQ4RawBytes = 13 * 64 * 16;           // 832 chunks: padding for wave 4's second load
+// INT4 cache (Q4): wave w gathers the whole raw 400-byte rows 4w .. 4w+3 of a
+// tile (100 chunks of 16 B: 2 loads, the second's lanes 36-63 refetching
+// chunk 99 into padding) into its own 2 KB region of a 2-slot raw ring, and
+// expands those rows into the bf16 tile layout above at the end of the
+// previous step: no wave reads another wave's raw rows, and the next step's
+// barrier publishes the bf16 tile.
+constexpr int kQ4RowsPerWave = kKT / 8;                        // 4
+constexpr int kQ4WaveChunks = kQ4RowsPerWave * kQ4Row / 16;    // 100
+constexpr int kQ4WaveBytes = 128 * 16;                         // 2 loads x 64 lanes x 16 B
+constexpr int kQ4RawBytes = 8 * kQ4WaveBytes;                  // 16 KB per slot
 
-// Thread tid expands latent elements 32j .. 32j+31 of row r = tid / 16
-// (j = tid % 16) and, for tid < 256, rope slot tid % 8 of row tid / 8.
-__device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tb) {
-  const int tid = threadIdx.x;
-  const int r = tid >> 4, j = tid & 15;
-  const uint8_t* rb = raw + r * kQ4Row;
+// Lane l of wave w expands latent elements 32j .. 32j+31 (j = l % 16) of row
+// 4w + l / 16, and lanes < 32 rope slot l % 8 of row 4w + l / 8.
+__device__ __forceinline__ void dequant_rows(const uint8_t* region, uint16_t* tb, int wave, int lane) {
+  const int rl = lane >> 4, j = lane & 15;
+  const uint8_t* rb = region + rl * kQ4Row;
   const u32x4 c = *reinterpret_cast<const u32x4*>(rb + 16 * j);
   const float sc = bf16_to_f32(*reinterpret_cast<const uint16_t*>(rb + kQ4ScaleOff + 2 * (j >> 1)));
+  const int r = kQ4RowsPerWave * wave + rl;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {  // dword w: elements 32j + 8w + e in nibble e
     const uint32_t d = c[w];
@@ -91,10 +95,10 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tb) {
     }
     *reinterpret_cast<u32x4*>(tb + swz(r, 4 * j + w) * 8) = v;
   }
-  if (tid < kKT * 8) {
-    const int rr = tid >> 3, i = tid & 7;
-    *reinterpret_cast<u32x4*>(tb + swz(rr, kLat / 8 + i) * 8) =
-        *reinterpret_cast<const u32x4*>(raw + rr * kQ4Row + kQ4RopeOff + 16 * i);
+  if (lane < kQ4RowsPerWave * 8) {
+    const int rr = lane >> 3, i = lane & 7;
+    *reinterpret_cast<u32x4*>(tb + swz(kQ4RowsPerWave * wave + rr, kLat / 8 + i) * 8) =
+        *reinterpret_cast<const u32x4*>(region + rr * kQ4Row + kQ4RopeOff + 16 * i);
   }
 }
 
@@ -123,7 +127,6 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileSlots * 8];  // (not used by Q4)
   __shared__ __attribute__((aligned(16))) uint8_t raw0[kQ4RawBytes];       // (Q4 only)
   __shared__ __attribute__((aligned(16))) uint8_t raw1[kQ4RawBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t raw2[kQ4RawBytes];
   __shared__ __attribute__((aligned(16))) uint16_t pT[kHeads * kPLds];
   __shared__ float s_max[2][kHeads];
   __shared__ float s_alpha[kHeads];
@@ -206,24 +209,23 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // logical column (pc & ~7) | ((pc ^ row) & 7) of its row (the swizzle is an
   // involution within groups of 8), so the lane fetches that chunk.  Row and
   // column of each lane's five chunks are the same for every tile.
-  // Q4: 2 loads per wave; instruction i of wave w covers chunks
-  // [(8i + w) * 64, +64) for i = 0 and for i = 1, w < 5 (chunks past 799, in
-  // the padding, fetch chunk 799); waves 5-7 repeat their first load.
+  // Q4: 2 loads per wave; load i covers chunks [64i, 64i + 64) of the wave's
+  // rows (chunks past 99 refetch chunk 99 into the region's padding).
   constexpr int kNL = Q4 ? 2 : 5;  // gather loads per wave per tile
   int g_row[kNL];
   uint32_t g_col[kNL];
-  auto blk_of = [&](int i) {
-    if (Q4) return (i == 0 || wave >= 5) ? wave : 8 + wave;
+  auto blk_of = [&](int i) {  // bf16: 64-slot block of the tile written by load i
     return i < 4 ? 8 * i + wave : 32 + (wave & 3);
   };
 #pragma unroll
   for (int i = 0; i < kNL; ++i) {
-    const int lin = blk_of(i) * 64 + lane;
     if (Q4) {
-      const int c = min(lin, kQ4Chunks - 1);
-      g_row[i] = c / (kQ4Row / 16);
-      g_col[i] = (uint32_t)(c - g_row[i] * (kQ4Row / 16)) * 16u;  // bytes
+      const int c = min(64 * i + lane, kQ4WaveChunks - 1);
+      const int rl = c / (kQ4Row / 16);
+      g_row[i] = kQ4RowsPerWave * wave + rl;
+      g_col[i] = (uint32_t)(c - rl * (kQ4Row / 16)) * 16u;  // bytes
     } else {  // physical slot lin < 2304 holds logical column (pc & ~7) | ((pc ^ row) & 7)
+      const int lin = blk_of(i) * 64 + lane;
       const int r = lin / kSlots, pc = lin - r * kSlots;
       g_row[i] = r;
       g_col[i] = (uint32_t)((pc & ~7) | ((pc ^ r) & 7)) * 8u;
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       const Unit* src = PAGED ? kv_seq + (int64_t)r * kStride + g_col[i]
                               : kv_seq + ((uint32_t)r * (uint32_t)kStride + g_col[i]);
       // (named pointers: the host pass rejects cast expressions as this builtin's operands)
-      uint16_t* const dst = static_cast<uint16_t*>(dstt) + blk_of(i) * 64 * 8;
+      uint16_t* const dst = static_cast<uint16_t*>(dstt) +
+                            (Q4 ? (wave * kQ4WaveBytes + i * 64 * 16) / 2 : blk_of(i) * 64 * 8);
       const uint16_t* const gsrc = reinterpret_cast<const uint16_t*>(src);
       __builtin_amdgcn_global_load_lds(gsrc, dst, 16, 0, 0);
     }
@@ -257,44 +260,18 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     qb[16] = as_bf16x8(ld16(qr));
     qb[17] = as_bf16x8(ld16(qr + 32));
   }
-  // Step tt issues the gather of tile tt + 2 (past the end too) right after
-  // its barrier, into the slot that step tt - 1 used: every wave has passed
-  // that barrier, so no wave still reads the slot.  One tile (5 loads per wave)
-  // is then in flight at each wait.
+  // bf16 cache: step tt issues the gather of tile tt + 2 (past the end too)
+  // right after its barrier, into the slot that step tt - 1 used: every wave
+  // has passed that barrier, so no wave still reads the slot.  One tile (5
+  // loads per wave) is then in flight at each wait.
   auto slot = [&](int b) -> void* {
-    if (Q4) return b == 0 ? (void*)raw0 : (b == 1 ? (void*)raw1 : (void*)raw2);
     return b == 0 ? (void*)tile0 : (b == 1 ? (void*)tile1 : (void*)tile2);
   };
-  {
-    int sidx[kNL], valid;
-    gather_idx(0, sidx, valid);
-    gather_issue(sidx, valid, slot(0), 0);
-    gather_idx(1, sidx, valid);
-    gather_issue(sidx, valid, slot(1), 1);
-  }
-  // Vector loads complete in issue order: with the 2 kNL gather loads of this
-  // wave the most recent, vmcnt <= 2 kNL means the query operands are in place.
-  wait_vm<2 * kNL>();
-
-  auto step = [&](int tt, auto BUFC) {
-    constexpr int buf = decltype(BUFC)::value;
-    constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (used by step tt - 1)
-    int sidx[kNL], valid;
-    gather_idx(tt + 2, sidx, valid);  // positions are static: read ahead of the barrier
-    wait_vm<kNL>();
-    lds_barrier();
-    gather_issue(sidx, valid, slot(nbuf), nbuf);
-    if (tt < ntiles) {
-    // Q4: bf16 tile tt & 1 was last read in step tt - 2, before this step's barrier
-    uint16_t* const tbq = (tt & 1) ? tile1 : tile0;
-    if (Q4) {
-      dequant_tile(static_cast<const uint8_t*>(slot(buf)), tbq);
-      lds_barrier();
-    }
-    const uint16_t* tb = Q4 ? tbq : static_cast<const uint16_t*>(slot(buf));
+  // QK, softmax and PV of one tile: bf16 tile tb, validity flags s_valid[vs].
+  auto compute = [&](const uint16_t* tb, int vs) {
     int vmask[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[buf][hf * 16 + 4 * g + jj];
+    for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[vs][hf * 16 + 4 * g + jj];
     // ---- QK: keys hf*16 + 4g + jj of head hq
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
     {
@@ -372,12 +349,67 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
         for (int j = 0; j < 4; ++j) o[e][j] = mfma16(fa, pb[j], o[e][j]);
       }
     }
-    }
   };
-  for (int tt = 0; tt < ntiles; tt += kRing) {
-    step(tt, std::integral_constant<int, 0>{});
-    step(tt + 1, std::integral_constant<int, 1>{});
-    step(tt + 2, std::integral_constant<int, 2>{});
+  if constexpr (!Q4) {
+    {
+      int sidx[kNL], valid;
+      gather_idx(0, sidx, valid);
+      gather_issue(sidx, valid, slot(0), 0);
+      gather_idx(1, sidx, valid);
+      gather_issue(sidx, valid, slot(1), 1);
+    }
+    // Vector loads complete in issue order: with the 10 gather loads of this
+    // wave the most recent, vmcnt <= 10 means the query operands are in place.
+    wait_vm<2 * kNL>();
+    auto step = [&](int tt, auto BUFC) {
+      constexpr int buf = decltype(BUFC)::value;
+      constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (used by step tt - 1)
+      int sidx[kNL], valid;
+      gather_idx(tt + 2, sidx, valid);  // positions are static: read ahead of the barrier
+      wait_vm<kNL>();
+      lds_barrier();
+      gather_issue(sidx, valid, slot(nbuf), nbuf);
+      if (tt < ntiles) compute(static_cast<const uint16_t*>(slot(buf)), buf);
+    };
+    for (int tt = 0; tt < ntiles; tt += kRing) {
+      step(tt, std::integral_constant<int, 0>{});
+      step(tt + 1, std::integral_constant<int, 1>{});
+      step(tt + 2, std::integral_constant<int, 2>{});
+    }
+  } else {
+    // INT4: raw tile j sits in raw slot j % 2, its bf16 expansion in tile
+    // j % 2, its validity flags in s_valid[j % 3].  A wave expands its own
+    // rows of tile tt + 1 at the end of step tt (its loads of that tile are
+    // then the older of its two tiles in flight); step tt + 1's barrier
+    // publishes them.  Tile tt + 2 is gathered into the raw slot of tile tt,
+    // which this wave has already expanded.
+    uint8_t* const raw_w0 = raw0 + wave * kQ4WaveBytes;
+    uint8_t* const raw_w1 = raw1 + wave * kQ4WaveBytes;
+    {
+      int sidx[kNL], valid;
+      gather_idx(0, sidx, valid);
+      gather_issue(sidx, valid, raw0, 0);
+      gather_idx(1, sidx, valid);
+      gather_issue(sidx, valid, raw1, 1);
+    }
+    wait_vm<kNL>();  // query operands and this wave's rows of tile 0
+    if (ntiles > 0) dequant_rows(raw_w0, tile0, wave, lane);
+    auto step = [&](int tt, auto BUFC) {
+      constexpr int buf = decltype(BUFC)::value;  // tt % 2
+      int sidx[kNL], valid;
+      gather_idx(tt + 2, sidx, valid);
+      lds_barrier();
+      gather_issue(sidx, valid, buf == 0 ? (void*)raw0 : (void*)raw1, (tt + 2) % 3);
+      if (tt < ntiles) compute(buf == 0 ? tile0 : tile1, tt % 3);
+      if (tt + 1 < ntiles) {
+        wait_vm<kNL>();
+        dequant_rows(buf == 0 ? raw_w1 : raw_w0, buf == 0 ? tile1 : tile0, wave, lane);
+      }
+    };
+    for (int tt = 0; tt < ntiles; tt += 2) {
+      step(tt, std::integral_constant<int, 0>{});
+      step(tt + 1, std::integral_constant<int, 1>{});
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target this workgroup's LDS at exit
 
