@@ -146,7 +146,7 @@ constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kGemmQPW = 2;
 constexpr int kGemmQB = kGemmWaves * kGemmQPW;
-constexpr int kGemmKT = 64;
+constexpr int kGemmKT = 128;  // keys per LDS tile (one barrier), computed in halves of 64
 constexpr int kGemmSplit = 8192;
 constexpr int kKeyLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
 
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int64_t row0 = PAGED ? 0 : cr.seq_row0[sq];
     const int32_t* bt = PAGED ? cr.table + (int64_t)sq * cr.max_pages : nullptr;
     const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
-    // Global -> LDS staging: 64 keys x 256 B = 1024 chunks of 16 B, 2 per thread.
+    // Global -> LDS staging: 128 keys x 256 B = 2048 chunks of 16 B, 4 per thread.
     // Chunk c covers keys base + 32c + (tid >> 4): granule (tid >> 8) + 2c, whose
     // page (PAGED) the thread loads two tiles ahead, as the scan does.
     constexpr int kPer = kGemmKT * 16 / kGemmThreads;
@@ -228,6 +228,15 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
         st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
       }
     };
+    // per query of the wave: last key to store (-1: another sequence), score row
+    int lim[kGemmQPW];
+    float* srow[kGemmQPW];
+#pragma unroll
+    for (int qi = 0; qi < kGemmQPW; ++qi) {
+      const int local = wave * kGemmQPW + qi;
+      lim[qi] = s_seq[local] == sq ? s_pos[local] : -1;
+      srow[qi] = scores + (int64_t)(t0 + local) * ld;
+    }
     int pa[kPer] = {}, pb[kPer] = {};  // pages of tiles tile + 1 and tile + 2 (PAGED)
     if (PAGED) {
       pid_fetch(0, pb);
@@ -240,32 +249,45 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
       const int buf = tile & 1;
       if (tile + 1 < ntiles) gload(tile + 1, pa);
       if (PAGED && tile + 2 < ntiles) pid_fetch(tile + 2, pb);
-      const int sbase = kbeg + tile * kGemmKT;
-      bf16x8 bfr[2][8];
+      const int sbase0 = kbeg + tile * kGemmKT;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int h = 0; h < kGemmKT / 64; ++h) {  // halves of 64 keys
+        const int sbase = sbase0 + 64 * h;
+        bf16x8 bfr[2][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          bfr[nt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              &ks[buf][(nt * 32 + n) * kKeyLds + 16 * j + 8 * g]));
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int qi = 0; qi < kGemmQPW; ++qi) {
-        const int local = wave * kGemmQPW + qi;
-        const int pos = s_pos[local];
-        if (s_seq[local] != sq || sbase > pos) continue;
-        float* srow = scores + (int64_t)(t0 + local) * ld;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+          for (int j = 0; j < 8; ++j)
+            bfr[nt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                &ks[buf][(64 * h + nt * 32 + n) * kKeyLds + 16 * j + 8 * g]));
+        // Four accumulators c = 2 qi + nt (query qi of the wave, key block nt).
+        // The epilogue of c (VALU, waits for c's chain) is placed after the MFMA
+        // chain of c + 1 is issued, so it runs while that chain executes.  All
+        // four are computed; only the block's queries of sequence sq store, and
+        // only keys s <= their position.
+        auto chain = [&](int c) {
           f32x16 acc = {};
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc = mfma32(qa[qi][j], bfr[nt][j], acc);
+          for (int j = 0; j < 8; ++j) acc = mfma32(qa[c >> 1][j], bfr[c & 1][j], acc);
+          return acc;
+        };
+        auto epilogue = [&](int c, const f32x16& acc) {
           float part = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], relu(acc[r]), part);
+          for (int r = 0; r < 16; ++r) part = fmaf(wr[c >> 1][r], relu(acc[r]), part);
           const float tot = part + xor_lane(part, 32);
-          const int s = sbase + nt * 32 + n;
-          if (g == 0 && s <= pos) srow[s] = tot;
-        }
+          const int s = sbase + (c & 1) * 32 + n;
+          if (g == 0 && s <= lim[c >> 1]) srow[c >> 1][s] = tot;
+        };
+        static_assert(kGemmQPW == 2, "four accumulators per half tile");
+        const f32x16 a0 = chain(0);
+        const f32x16 a1 = chain(1);
+        epilogue(0, a0);
+        const f32x16 a2 = chain(2);
+        epilogue(1, a1);
+        const f32x16 a3 = chain(3);
+        epilogue(2, a2);
+        epilogue(3, a3);
       }
       if (tile + 1 < ntiles) lstore(buf ^ 1);
       if (PAGED) {

@@ -60,7 +60,7 @@ constexpr int kCoreThreads = 512;
 constexpr int kRing = 3;
 constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
-constexpr int kPartSlab = kHeads * kLat;  // floats of one split partial
+constexpr int kPartSlab = kHeads * kLat;  // fp16 values of one split partial
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
 
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr,
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_rope,
     const void* __restrict__ kv_v, const int32_t* __restrict__ idx, int k, float scale_log2,
-    int kps, int S, uint16_t* __restrict__ o_lat, float* __restrict__ o_part,
+    int kps, int S, uint16_t* __restrict__ o_lat, uint16_t* __restrict__ o_part,
     float* __restrict__ ml_part) {
   // Three distinct arrays (not one indexed array): the compiler then waits
   // only for the direct-to-LDS loads that target the array being read.
@@ -272,13 +272,17 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     int vmask[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[vs][hf * 16 + 4 * g + jj];
-    // ---- QK: keys hf*16 + 4g + jj of head hq
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // ---- QK: keys hf*16 + 4g + jj of head hq; three independent MFMA chains
+    // (one chain of 18 would serialise on its accumulator)
+    f32x4 sc;
     {
       const int r = hf * 16 + l16;
+      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks)
-        sc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(tb + swz(r, 4 * ks + g) * 8)), qb[ks], sc);
+        acc[ks % 3] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(tb + swz(r, 4 * ks + g) * 8)), qb[ks],
+                             acc[ks % 3]);
+      sc = acc[0] + acc[1] + acc[2];
     }
     float z[4];
     float tmax = -INFINITY;
@@ -435,12 +439,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
             u32x2{pack_bf16x2(o[0][j][jj] * inv, o[1][j][jj] * inv),
                   pack_bf16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
     } else {
-      // Partials keep the accumulator order (see mla_merge_kernel), so that each
-      // store instruction writes 1 KB of consecutive memory.
-      float* dst = o_part + ((int64_t)t * S + sp) * kPartSlab + ((wave * 4 + j) * 4) * 256 + lane * 4;
+      // Partials are normalised by the split's own sum (a convex combination of
+      // cache rows, so fp16 holds them to 2^-11) and keep the accumulator order
+      // (see mla_merge_kernel): each store instruction writes 512 B of
+      // consecutive memory.
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* dst = o_part + ((int64_t)t * S + sp) * kPartSlab + ((wave * 4 + j) * 4) * 256 + lane * 4;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<f32x4*>(dst + jj * 256) = f32x4{o[0][j][jj], o[1][j][jj], o[2][j][jj], o[3][j][jj]};
+        *reinterpret_cast<u32x2*>(dst + jj * 256) =
+            u32x2{pack_f16x2(o[0][j][jj] * inv, o[1][j][jj] * inv), pack_f16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
       if (wave == 0 && g == 0) {
         const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
         ml_part[base * 2] = s_m[h];
@@ -451,20 +459,21 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 }
 
 // ---------------------------------------------------------------- merge
-// Split partials of (query t, split s) form one slab of kHeads * kLat floats in
-// the core's accumulator order: element e of f32x4 number
-// ((w * 4 + j) * 4 + jj) * 64 + lane is latent dim 64w + 16(lane / 16) + 4jj + e
-// of head 16j + lane % 16.  ml_part[t][s][h] = (reference max m, sum l).
-// grid (T, 32): workgroup (t, 4w + j) combines latent dims 64w .. 64w+63 of
-// heads 16j .. 16j+15, one f32x4 of every split per thread.
-__global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ o_part,
+// Split partials of (query t, split s) form one slab of kHeads * kLat fp16
+// values, each normalised by its split's sum l, in the core's accumulator
+// order: element e of the 4-value group number ((w * 4 + j) * 4 + jj) * 64 +
+// lane is latent dim 64w + 16(lane / 16) + 4jj + e of head 16j + lane % 16.
+// ml_part[t][s][h] = (reference max m, sum l).  grid (T, 32): workgroup
+// (t, 4w + j) combines latent dims 64w .. 64w+63 of heads 16j .. 16j+15, one
+// group of every split per thread, weighting split s by 2^(m_s - max m) l_s.
+__global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restrict__ o_part,
                                                         const float* __restrict__ ml_part, int S,
                                                         uint16_t* __restrict__ o_lat) {
   const int t = blockIdx.x, w = blockIdx.y >> 2, j = blockIdx.y & 3, tid = threadIdx.x;
   const int lane = tid & 63, jj = tid >> 6;
   const int h = 16 * j + (lane & 15), g = lane >> 4;
   const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
-  const float* src = o_part + (int64_t)t * S * kPartSlab + (((w * 4 + j) * 4 + jj) * 64 + lane) * 4;
+  const uint16_t* src = o_part + (int64_t)t * S * kPartSlab + (((w * 4 + j) * 4 + jj) * 64 + lane) * 4;
   float mstar = -1e30f;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml[s * kHeads * 2]);
@@ -472,9 +481,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict_
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const float wgt = exp2f(ml[s * kHeads * 2] - mstar);
-    L += wgt * ml[s * kHeads * 2 + 1];
-    acc += wgt * *reinterpret_cast<const f32x4*>(src + (int64_t)s * kPartSlab);
+    const float wgt = exp2f(ml[s * kHeads * 2] - mstar) * ml[s * kHeads * 2 + 1];
+    L += wgt;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src + (int64_t)s * kPartSlab);
+    acc += wgt * f32x4{f16_lo(v.x), f16_hi(v.x), f16_lo(v.y), f16_hi(v.y)};
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 64 * w + 16 * g + 4 * jj) =
@@ -669,10 +679,10 @@ MlaPlan plan_mla(int T, int k) {
   p.T = T;
   p.k = k;
   // Small batches split each query's keys so that about 256 workgroups run,
-  // with at least 128 keys (4 tiles) per split.
+  // with at least 64 keys (2 tiles) per split.
   int s = 1;
   if (T > 0 && T < 256) s = (256 + T - 1) / T;
-  const int cap = k / 128 > 16 ? k / 128 : 16;
+  const int cap = k / 64 > 32 ? k / 64 : 32;
   s = s < cap ? s : cap;
   const int max_s = (k + kKT - 1) / kKT;
   s = s < max_s ? s : max_s;
@@ -687,7 +697,7 @@ MlaPlan plan_mla(int T, int k) {
   size_t end = p.o_lat_off + align_up(lat, 256);
   if (p.splits > 1) {
     p.part_off = end;
-    end += align_up((size_t)T * p.splits * kHeads * kLat * sizeof(float), 256);
+    end += align_up((size_t)T * p.splits * kHeads * kLat * sizeof(uint16_t), 256);
     p.ml_off = end;
     end += align_up((size_t)T * p.splits * kHeads * 2 * sizeof(float), 256);
   }
@@ -706,7 +716,7 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   char* base = static_cast<char*>(ws);
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(base + p.q_lat_off);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(base + p.o_lat_off);
-  float* o_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.part_off) : nullptr;
+  uint16_t* o_part = p.splits > 1 ? reinterpret_cast<uint16_t*>(base + p.part_off) : nullptr;
   float* ml_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
   const int T = b.T;
   const int ntb = (T + 31) / 32;

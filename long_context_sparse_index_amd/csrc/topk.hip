@@ -421,10 +421,9 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
   const uint32_t b_hi = (uint32_t)min(bs + ((float)r <= margin ? 1 : 0), kTkBins - 1);
   const uint32_t b_lo = (uint32_t)max(bs - ((float)(ins - r) < margin ? 1 : 0), 0);
   // ---- exact ordered pass: above the window -> A, inside -> candidates;
-  // the next step's scores are loaded while this step is compacted
+  // the scores of the next two steps are in flight while a step is compacted
   int nA = 0, nC = 0;
-  f32x4 nx[kPerThread / 4];
-  auto fetch = [&](int i) {
+  auto fetch = [&](int i, f32x4 nx[kPerThread / 4]) {
 #pragma unroll
     for (int q = 0; q < kPerThread / 4; ++q) {
       const int b = i + 4 * q;
@@ -436,8 +435,7 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
       nx[q] = v;
     }
   };
-  fetch(kPerThread * tid);
-  for (int base = 0; base < n; base += kStep) {
+  auto step = [&](int base, f32x4 nx[kPerThread / 4]) {
     const int i = base + kPerThread * tid;
     uint32_t key[kPerThread];
     bool ok[kPerThread];
@@ -448,7 +446,7 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
         ok[4 * q + e] = i + 4 * q + e < n;
         key[4 * q + e] = score_key(nx[q][e]);
       }
-    if (base + kStep < n) fetch(i + kStep);
+    if (base + 2 * kStep < n) fetch(i + 2 * kStep, nx);
     int ca = 0, cc = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -476,6 +474,13 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
     }
     nA += tot >> 16;
     nC += tot & 0xFFFF;
+  };
+  f32x4 nxa[kPerThread / 4], nxb[kPerThread / 4];
+  fetch(kPerThread * tid, nxa);
+  if (kStep < n) fetch(kStep + kPerThread * tid, nxb);
+  for (int base = 0; base < n; base += 2 * kStep) {
+    step(base, nxa);
+    if (base + kStep < n) step(base + kStep, nxb);
   }
   __syncthreads();
   if (!(nA < k && nA + nC >= k && nC <= kCandCap)) return false;  // uniform: every thread has the totals
