@@ -99,6 +99,17 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Float threshold of a key bound: for every non-NaN f, score_key(f) >= K
+// exactly when f >= key_floor(K) (float order, -0 == +0).  K above the key of
+// +inf gives NaN, which no compare satisfies.
+__device__ __forceinline__ float key_floor(uint32_t K) {
+  if (K & 0x80000000u) {
+    const uint32_t b = K & 0x7FFFFFFFu;
+    return b > 0x7F800000u ? __uint_as_float(0x7FC00000u) : __uint_as_float(b);
+  }
+  return K <= 0x007FFFFFu ? -INFINITY : __uint_as_float(~K);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP):
 // Hillis-Steele shifts of 1, 2, 4, 8 lanes inside each 16-lane row (sources
 // outside the row read 0), then row 0's total is added to row 1 and row 2's

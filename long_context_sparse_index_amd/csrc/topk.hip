@@ -421,13 +421,19 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
   const uint32_t b_hi = (uint32_t)min(bs + ((float)r <= margin ? 1 : 0), kTkBins - 1);
   const uint32_t b_lo = (uint32_t)max(bs - ((float)(ins - r) < margin ? 1 : 0), 0);
   // ---- exact ordered pass: above the window -> A, inside -> candidates;
-  // the scores of the next two steps are in flight while a step is compacted
+  // the scores of the next two steps are in flight while a step is compacted.
+  // The window's bin edges become float thresholds, so a score is classified
+  // by two compares into per-thread bit masks; keys are formed only for the
+  // few scores that are kept.  Scores past the row are NaN (no compare holds).
+  const float thr_hi = b_hi + 1 >= (uint32_t)kTkBins ? __uint_as_float(0x7FC00000u) : key_floor((b_hi + 1) << 20);
+  const float thr_lo = key_floor(b_lo << 20);
   int nA = 0, nC = 0;
   auto fetch = [&](int i, f32x4 nx[kPerThread / 4]) {
+    const float nan = __uint_as_float(0x7FC00000u);
 #pragma unroll
     for (int q = 0; q < kPerThread / 4; ++q) {
       const int b = i + 4 * q;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      f32x4 v = {nan, nan, nan, nan};
       if (b + 3 < n) v = *reinterpret_cast<const f32x4*>(row + b);
       else
         for (int e = 0; e < 4; ++e)
@@ -437,36 +443,32 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
   };
   auto step = [&](int base, f32x4 nx[kPerThread / 4]) {
     const int i = base + kPerThread * tid;
-    uint32_t key[kPerThread];
-    bool ok[kPerThread];
+    float f[kPerThread];
 #pragma unroll
     for (int q = 0; q < kPerThread / 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ok[4 * q + e] = i + 4 * q + e < n;
-        key[4 * q + e] = score_key(nx[q][e]);
-      }
+      for (int e = 0; e < 4; ++e) f[4 * q + e] = nx[q][e];
     if (base + 2 * kStep < n) fetch(i + 2 * kStep, nx);
-    int ca = 0, cc = 0;
+    uint32_t mA = 0, mW = 0;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      const uint32_t d = key[e] >> 20;
-      ca += ok[e] && d > b_hi;
-      cc += ok[e] && d >= b_lo && d <= b_hi;
+      mA |= (f[e] >= thr_hi ? 1u : 0u) << e;
+      mW |= (f[e] >= thr_lo ? 1u : 0u) << e;
     }
+    const uint32_t mC = mW & ~mA;
     int tot;
-    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);  // <= kStep each
+    const int ex = block_excl_scan<kTkWaves>((__builtin_popcount(mA) << 16) | __builtin_popcount(mC),
+                                             sh.wave_tot, tot);  // <= kStep each
     int oa = nA + (ex >> 16), oc = nC + (ex & 0xFFFF);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
-      if (!ok[e]) continue;
-      const uint32_t d = key[e] >> 20;
-      if (d > b_hi) {
+      if (!((mW >> e) & 1u)) continue;
+      if ((mA >> e) & 1u) {
         if (oa < KMAX) sh.list_a[oa] = i + e;
         ++oa;
-      } else if (d >= b_lo) {
+      } else {
         if (oc < kCandCap) {
-          sh.cand_key[oc] = key[e];
+          sh.cand_key[oc] = score_key(f[e]);
           sh.cand_pos[oc] = i + e;
         }
         ++oc;
