@@ -90,6 +90,26 @@ def _topk_rows(kind, n_list, seed):
             r[(np.arange(n) // 64) % 16 == 0] += shift
             rows.append(r)
         return rows
+    if kind == "negative":  # every score below zero: window thresholds on the negative side
+        return [-np.abs(synth.random_scores(rng, 1, n, "signed")[0]) - np.float32(0.5) for n in n_list]
+    if kind == "zeros_mix":  # 5% positive, 40% exact +-0, the rest negative: the k-th is a zero
+        rows = []
+        for n in n_list:
+            r = -np.abs(synth.random_scores(rng, 1, n, "signed")[0]) * np.float32(1e-3)
+            u = rng.random(n)
+            r[u < 0.05] = -r[u < 0.05]
+            z = (u >= 0.05) & (u < 0.45)
+            r[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+            rows.append(r.astype(np.float32))
+        return rows
+    if kind == "inf_mix":  # a few infinities of both signs among normal scores
+        rows = []
+        for n in n_list:
+            r = synth.random_scores(rng, 1, n, "normal")[0]
+            r[rng.choice(n, 300, replace=False)] = np.float32(np.inf)
+            r[rng.choice(n, 300, replace=False)] = np.float32(-np.inf)
+            rows.append(r)
+        return rows
     return [synth.random_scores(rng, 1, n, kind)[0] for n in n_list]
 
 
@@ -104,6 +124,11 @@ TOPK_CASES = {
     "long_small_k": ("normal", [70000, 200000], 7),
     "sample_low": ("sample_low", [100000, 204800], 2048),       # window too low -> full path
     "sample_high": ("sample_high", [100000, 204800], 2048),     # window too high -> full path
+    # long rows (sampled window) at the edges of the float-threshold classification
+    "long_negative": ("negative", [70000, 150001], 2048),
+    "long_zeros_mix": ("zeros_mix", [70000, 204800], 8192),
+    "long_inf_mix": ("inf_mix", [65536, 120000], 2048),
+    "long_inf_mix_k250": ("inf_mix", [90000], 250),
     # index_topk as a runtime parameter above 2048 (kernels with larger LDS lists)
     "k4096_ragged": ("normal", [1, 4095, 4096, 4097, 9000, 40000], 4096),
     "k3000_signed": ("signed", [3000, 3001, 70000], 3000),
