@@ -21,20 +21,24 @@
 namespace dsa {
 
 // ---------------------------------------------------------------- absorb
-// grid (64 heads, query groups of kAbsorbTilesPerWg 32-query tiles); 16 waves
-// cover the 512 latent columns (absorb_wave, 32 each), so the q_nope tile of
-// a step is fetched once per workgroup and shared by its waves through L1.
+// grid (64 heads, query groups of kAbsorbTilesPerWg 32-query tiles, 16 / NW
+// column groups); NW waves per workgroup cover 32 latent columns each
+// (absorb_wave), so the q_nope tile of a step is fetched once per workgroup
+// and shared by its waves through L1.  Many queries: NW = 16 (one workgroup
+// per head and query group); few queries: NW = 4, so that W_UK is read by
+// four times as many CUs.
 constexpr int kAbsorbTilesPerWg = 8;
 
-__global__ __launch_bounds__(1024) void absorb_kernel(const uint16_t* __restrict__ q_nope,
-                                                      const uint16_t* __restrict__ w_uk,
-                                                      uint16_t* __restrict__ q_lat, int T) {
-  __shared__ __attribute__((aligned(16))) uint16_t stage[16][kAbsorbStage];
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                         const uint16_t* __restrict__ w_uk,
+                                                         uint16_t* __restrict__ q_lat, int T) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[NW][kAbsorbStage];
   const int ntb = (T + 31) / 32;
   const int tb0 = blockIdx.y * kAbsorbTilesPerWg;
   const int wave = threadIdx.x >> 6;
-  absorb_wave(q_nope, w_uk, q_lat, T, blockIdx.x, wave * 32, tb0, min(ntb, tb0 + kAbsorbTilesPerWg),
-              stage[wave]);
+  absorb_wave(q_nope, w_uk, q_lat, T, blockIdx.x, (blockIdx.z * NW + wave) * 32, tb0,
+              min(ntb, tb0 + kAbsorbTilesPerWg), stage[wave]);
 }
 
 // ---------------------------------------------------------------- core
@@ -722,8 +726,11 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   const int ntb = (T + 31) / 32;
   hipError_t e;
   if (!q_lat_ready) {
-    absorb_kernel<<<dim3(kHeads, (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg), 1024, 0, st>>>(
-        q_nope, w_uk, q_lat, T);
+    const int nqg = (ntb + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg;
+    if (ntb <= 2)
+      absorb_kernel<4><<<dim3(kHeads, nqg, 4), 256, 0, st>>>(q_nope, w_uk, q_lat, T);
+    else
+      absorb_kernel<16><<<dim3(kHeads, nqg, 1), 1024, 0, st>>>(q_nope, w_uk, q_lat, T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
