@@ -750,6 +750,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
   if (c1 > kCandCapWs) return;  // heavy ties: the row's finish re-reads the row
   int offA = sh.offA, offC = sh.offC;
   // ---- ordered compaction of the slice, 16 consecutive scores per thread per step
+  const float thr_hi = b1 + 1 >= (uint32_t)kTkBins ? __uint_as_float(0x7FC00000u) : key_floor((b1 + 1) << 20);
+  const float thr_lo = key_floor(b1 << 20);
   int* list_a = reinterpret_cast<int*>(base + w.a_off);
   uint32_t* cand = reinterpret_cast<uint32_t*>(base + w.c_off);
   const int end = min(n, s0 + w.slice_keys);
@@ -762,27 +764,26 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
     } else {
       load16(i0, end, v);
     }
-    uint32_t key[kSelKeys];
-    int ca = 0, cc = 0;
+    // classify against the float edges of bin b1 (bit masks), keys only for
+    // the kept scores
+    uint32_t mA = 0, mW = 0;
 #pragma unroll
     for (int e = 0; e < kSelKeys; ++e) {
       const bool ok = i0 + e < end;
-      key[e] = ok ? score_key(v[e]) : 0u;  // unused when !ok
-      const uint32_t d = key[e] >> 20;
-      ca += ok && d > b1;
-      cc += ok && d == b1;
+      mA |= (ok && v[e] >= thr_hi ? 1u : 0u) << e;
+      mW |= (ok && v[e] >= thr_lo ? 1u : 0u) << e;
     }
     int tot;
-    const int exs = block_excl_scan<kSelWaves>((ca << 16) | cc, sh.wave_tot, tot);  // < 4096 each
+    const int exs = block_excl_scan<kSelWaves>((__builtin_popcount(mA) << 16) | __builtin_popcount(mW & ~mA),
+                                               sh.wave_tot, tot);  // < 4096 each
     int oa = offA + (exs >> 16), oc = offC + (exs & 0xFFFF);
 #pragma unroll
     for (int e = 0; e < kSelKeys; ++e) {
-      if (i0 + e >= end) continue;
-      const uint32_t d = key[e] >> 20;
-      if (d > b1) {
+      if (!((mW >> e) & 1u)) continue;
+      if ((mA >> e) & 1u) {
         list_a[oa++] = i0 + e;
-      } else if (d == b1) {
-        *reinterpret_cast<u32x2*>(cand + 2 * oc) = u32x2{key[e], (uint32_t)(i0 + e)};
+      } else {
+        *reinterpret_cast<u32x2*>(cand + 2 * oc) = u32x2{score_key(v[e]), (uint32_t)(i0 + e)};
         ++oc;
       }
     }
