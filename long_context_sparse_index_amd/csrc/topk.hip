@@ -181,20 +181,35 @@ __device__ void finish_from_candidates(TkShared<KMAX>& sh, uint32_t b1, int abov
   const uint32_t b3 = (uint32_t)sh.sel_bin;
   const int r = krem2 - sh.sel_above;  // ties at the threshold key to keep (lowest positions)
   const uint32_t kstar = (b1 << 20) | (b2 << 8) | b3;
+  // ordered compaction: thread tid takes candidates [kCE tid, kCE tid + kCE)
+  // of a round of kCE * kTkThreads (one round holds all of kCandCap)
+  constexpr int kCE = (kCandCap + kTkThreads - 1) / kTkThreads;
   int nG = 0, nE = 0;
-  for (int base = 0; base < c1; base += kTkThreads) {
-    const int j = base + tid;
-    int gt = 0, eq = 0;
-    if (j < c1) {
-      const uint32_t key = sh.cand_key[j];
-      gt = key > kstar;
-      eq = key == kstar;
+  for (int base = 0; base < c1; base += kCE * kTkThreads) {
+    const int j0 = base + kCE * tid;
+    uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+    for (int e = 0; e < kCE; ++e) {
+      if (j0 + e < c1) {
+        const uint32_t key = sh.cand_key[j0 + e];
+        gtm |= (key > kstar ? 1u : 0u) << e;
+        eqm |= (key == kstar ? 1u : 0u) << e;
+      }
     }
     int tot;
-    const int ex = block_excl_scan<kTkWaves>((gt << 16) | eq, sh.wave_tot, tot);
-    const int eg = nG + (ex >> 16), ee = nE + (ex & 0xFFFF);
-    if (gt) sh.list_c[eg + min(ee, r)] = sh.cand_pos[j];
-    else if (eq && ee < r) sh.list_c[eg + ee] = sh.cand_pos[j];
+    const int ex = block_excl_scan<kTkWaves>((__builtin_popcount(gtm) << 16) | __builtin_popcount(eqm),
+                                             sh.wave_tot, tot);
+    int eg = nG + (ex >> 16), ee = nE + (ex & 0xFFFF);
+#pragma unroll
+    for (int e = 0; e < kCE; ++e) {
+      if ((gtm >> e) & 1u) {
+        sh.list_c[eg + min(ee, r)] = sh.cand_pos[j0 + e];
+        ++eg;
+      } else if ((eqm >> e) & 1u) {
+        if (ee < r) sh.list_c[eg + ee] = sh.cand_pos[j0 + e];
+        ++ee;
+      }
+    }
     nG += tot >> 16;
     nE += tot & 0xFFFF;
   }
