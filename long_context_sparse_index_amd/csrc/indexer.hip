@@ -138,26 +138,48 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 
 // ---------------------------------------------------------------- prefill GEMM
 // One workgroup = kGemmQB consecutive queries x kGemmSplit keys.  Each of the
-// 8 waves keeps kGemmQPW queries (32 heads each) as resident A operands; key
-// tiles of kGemmKT keys are staged through LDS (double buffered) and shared by
-// the eight waves.  Queries of one block normally share a sequence; a block that mixes
-// sequences is processed once per distinct sequence.
+// kGemmWaves waves keeps kGemmQPW queries (32 heads each) as resident A
+// operands; key tiles of kGemmKT keys reach LDS by direct global->LDS loads
+// (no register staging), double buffered, and are shared by the waves (one
+// workgroup per CU; four waves per workgroup with two workgroups per CU
+// measured slower).  Queries of one block normally share a sequence; a block
+// that mixes sequences is processed once per distinct sequence.
+//
+// LDS holds a key row as 16 chunks of 16 B with chunk c of row r at slot
+// c ^ (r & 15), so the B-fragment reads (32 rows, one chunk each, per
+// instruction) spread over all banks without padding; a direct load writes
+// lane L of a wave instruction to slot L of a 1 KB block, so each lane fetches
+// the chunk that its slot holds.
+// A tile is computed in groups of 64 keys.  The fragments of key block 0 of
+// the next group are read as soon as the two MFMA chains that use block 0 of
+// the current group are issued (likewise block 1), and the last epilogue of a
+// group runs after the next group's first chain is issued (across the tile
+// barrier too), so LDS latency and epilogue VALU overlap MFMA work.
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kGemmQPW = 2;
 constexpr int kGemmQB = kGemmWaves * kGemmQPW;
-constexpr int kGemmKT = 128;  // keys per LDS tile (one barrier), computed in halves of 64
+constexpr int kGemmKT = 256;  // keys per LDS tile (one barrier)
+constexpr int kGemmGroups = kGemmKT / 64;
 constexpr int kGemmSplit = 8192;
-constexpr int kKeyLds = kIdxDim + 8;  // bf16 per LDS key row (16 B pad)
+constexpr int kGemmLoads = kGemmKT * kIdxDim * 2 / (kGemmThreads * 16);  // direct loads per thread per tile
+constexpr int kDlStride = 4 * kGemmWaves;  // key rows between a thread's successive direct loads
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9: 32-bit data, no swizzle)
+constexpr int kDropOffset = 0x40000000;   // a store offset past every resource's end
 
 template <bool PAGED>
 __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int T) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kGemmKT * kKeyLds];
+  // two buffers as two arrays: with distinct objects the compiler sees that
+  // direct loads into one do not alias reads of the other, and does not make
+  // those reads wait for the loads
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kGemmKT * kIdxDim];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kGemmKT * kIdxDim];
   __shared__ int s_seq[kGemmQB], s_pos[kGemmQB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addresses stay scalar
   const int g = lane >> 5, n = lane & 31;
   const int t0 = blockIdx.x * kGemmQB;
   if (tid < kGemmQB) {
@@ -184,6 +206,17 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     for (int r = 0; r < 16; ++r) wr[qi][r] = bf16_to_f32(w[tt * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)]);
   }
 
+  // Direct load i of this thread: 1 KB block kGemmWaves i + wave of the tile
+  // = rows kDlStride i + 4 wave .. +3; the lane's row and (swizzled) chunk.
+  static_assert(kDlStride % 16 == 0, "the swizzle of a load's row does not depend on i");
+  const int dl_row = 4 * wave + (lane >> 4);             // + kDlStride i
+  const int dl_chunk = (lane & 15) ^ (dl_row & 15);
+  // B-fragment read offsets (bf16 units) of key block nt of a group, step j:
+  // row 32 nt + n (+ 64 per group), logical chunk 2j + g.
+  int frag_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) frag_off[j] = n * kIdxDim + (((2 * j + g) ^ (n & 15)) << 3);
+
   for (int i = 0; i < kGemmQB; ++i) {
     const int sq = s_seq[i];
     if (sq < 0) continue;
@@ -200,102 +233,113 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int64_t row0 = PAGED ? 0 : cr.seq_row0[sq];
     const int32_t* bt = PAGED ? cr.table + (int64_t)sq * cr.max_pages : nullptr;
     const int ntiles = (kend - kbeg + kGemmKT - 1) / kGemmKT;
-    // Global -> LDS staging: 128 keys x 256 B = 2048 chunks of 16 B, 4 per thread.
-    // Chunk c covers keys base + 32c + (tid >> 4): granule (tid >> 8) + 2c, whose
-    // page (PAGED) the thread loads two tiles ahead, as the scan does.
-    constexpr int kPer = kGemmKT * 16 / kGemmThreads;
-    auto pid_fetch = [&](int tile, int p[kPer]) {
+    // PAGED: load i of a tile lies in granule (kGemmWaves i + wave) / 4 (16
+    // keys, one page); the page ids of tile + 2 are loaded (into pv) while
+    // tile is computed, and made scalar (pa, wave-uniform) once they have
+    // arrived.
+    auto pid_fetch = [&](int tile, int p[kGemmLoads]) {
 #pragma unroll
-      for (int c = 0; c < kPer; ++c)
-        p[c] = bt[min(kbeg + tile * kGemmKT + kGranule * ((tid >> 8) + 2 * c), hi) >> cr.page_shift];
+      for (int c = 0; c < kGemmLoads; ++c)
+        p[c] = bt[min(kbeg + tile * kGemmKT + kGranule * ((kGemmWaves * c + wave) >> 2), hi) >> cr.page_shift];
     };
-    u32x4 stage[kPer];
-    auto gload = [&](int tile, const int p[kPer]) {
+    auto dma = [&](int tile, const int p[kGemmLoads], uint16_t* buf) {
       const int base = kbeg + tile * kGemmKT;
 #pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const int lin = tid + kGemmThreads * c;
-        const int key = min(base + (lin >> 4), hi);
+      for (int c = 0; c < kGemmLoads; ++c) {
+        const int key = min(base + kDlStride * c + dl_row, hi);  // rows past hi: never stored
         int64_t row = row0 + key;
         if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (key & ((1 << cr.page_shift) - 1));
-        stage[c] = ld16(k_idx + row * kIdxDim + (lin & 15) * 8);
+        // (named pointers: the host pass rejects cast expressions as this builtin's operands)
+        const uint16_t* const gsrc = k_idx + row * kIdxDim + dl_chunk * 8;
+        uint16_t* const dst = buf + (kGemmWaves * c + wave) * 512;
+        __builtin_amdgcn_global_load_lds(gsrc, dst, 16, 0, 0);
       }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const int lin = tid + kGemmThreads * c;
-        st16(&ks[buf][(lin >> 4) * kKeyLds + (lin & 15) * 8], stage[c]);
-      }
-    };
-    // per query of the wave: last key to store (-1: another sequence), score row
-    int lim[kGemmQPW];
-    float* srow[kGemmQPW];
+    // per query of the wave: a buffer resource over the keys of this split
+    // that the query stores (s <= its position; none for another sequence).
+    // Stores past its end are dropped by the hardware, so the epilogue stores
+    // without a branch.
+    __amdgpu_buffer_rsrc_t rs[kGemmQPW];
 #pragma unroll
     for (int qi = 0; qi < kGemmQPW; ++qi) {
       const int local = wave * kGemmQPW + qi;
-      lim[qi] = s_seq[local] == sq ? s_pos[local] : -1;
-      srow[qi] = scores + (int64_t)(t0 + local) * ld;
+      const int lim = __builtin_amdgcn_readfirstlane(s_seq[local] == sq ? s_pos[local] : -1);
+      const int nrec = min(max(lim + 1 - kbeg, 0), kGemmSplit) * 4;
+      const uint64_t srow = reinterpret_cast<uint64_t>(scores + (int64_t)(t0 + local) * ld + kbeg);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)srow);
+      const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(srow >> 32));
+      float* const base = reinterpret_cast<float*>(((uint64_t)hi32 << 32) | lo);
+      rs[qi] = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(nrec), kBufferWord3);
     }
-    int pa[kPer] = {}, pb[kPer] = {};  // pages of tiles tile + 1 and tile + 2 (PAGED)
-    if (PAGED) {
-      pid_fetch(0, pb);
-      if (ntiles > 1) pid_fetch(1, pa);
+    auto chain = [&](int qi, const bf16x8 b[8]) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = mfma32(qa[qi][j], b[j], acc);
+      return acc;
+    };
+    // column n of the accumulator: key kbeg + koff of query qi (lanes n and
+    // n + 32 hold 16 head rows each; g == 0 stores the sum)
+    auto epilogue = [&](int qi, const f32x16& acc, int koff) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], relu(acc[r]), part);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // part(n) + part(n + 32)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[qi], g == 0 ? 4 * koff : kDropOffset, 0, 0);
+    };
+    auto frags = [&](const uint16_t* buf, int grp, int nt, bf16x8 b[8]) {
+      const uint16_t* base = buf + (64 * grp + 32 * nt) * kIdxDim;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + frag_off[j]));
+    };
+    int pa[kGemmLoads] = {}, pv[kGemmLoads] = {};  // pages of tiles tile + 1 and tile + 2 (PAGED)
+    if (PAGED) pid_fetch(0, pv);
+    dma(0, pv, ks0);
+    if (PAGED && ntiles > 1) {
+      pid_fetch(1, pv);
+#pragma unroll
+      for (int c = 0; c < kGemmLoads; ++c) pa[c] = __builtin_amdgcn_readfirstlane(pv[c]);
     }
-    gload(0, pb);
-    lstore(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
     __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile & 1;
-      if (tile + 1 < ntiles) gload(tile + 1, pa);
-      if (PAGED && tile + 2 < ntiles) pid_fetch(tile + 2, pb);
-      const int sbase0 = kbeg + tile * kGemmKT;
+    bf16x8 fa[8], fb[8];  // fragments of key blocks 0 and 1 of the current group
+    f32x16 pend = {};          // accumulator of (query 1, block 1) of the previous group
+    int pend_k = kGemmSplit;   // its key offset (kGemmSplit: none, the store is dropped)
+    // tile in cur, tile + 1 loaded into nxt meanwhile
+    auto tile_body = [&](const uint16_t* cur, uint16_t* nxt, int tile) {
+      if (tile + 1 < ntiles) dma(tile + 1, pa, nxt);
+      if (PAGED && tile + 2 < ntiles) pid_fetch(tile + 2, pv);
+      frags(cur, 0, 0, fa);
+      frags(cur, 0, 1, fb);
 #pragma unroll
-      for (int h = 0; h < kGemmKT / 64; ++h) {  // halves of 64 keys
-        const int sbase = sbase0 + 64 * h;
-        bf16x8 bfr[2][8];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            bfr[nt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                &ks[buf][(64 * h + nt * 32 + n) * kKeyLds + 16 * j + 8 * g]));
-        // Four accumulators c = 2 qi + nt (query qi of the wave, key block nt).
-        // The epilogue of c (VALU, waits for c's chain) is placed after the MFMA
-        // chain of c + 1 is issued, so it runs while that chain executes.  All
-        // four are computed; only the block's queries of sequence sq store, and
-        // only keys s <= their position.
-        auto chain = [&](int c) {
-          f32x16 acc = {};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc = mfma32(qa[c >> 1][j], bfr[c & 1][j], acc);
-          return acc;
-        };
-        auto epilogue = [&](int c, const f32x16& acc) {
-          float part = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part = fmaf(wr[c >> 1][r], relu(acc[r]), part);
-          const float tot = part + xor_lane(part, 32);
-          const int s = sbase + (c & 1) * 32 + n;
-          if (g == 0 && s <= lim[c >> 1]) srow[c >> 1][s] = tot;
-        };
-        static_assert(kGemmQPW == 2, "four accumulators per half tile");
-        const f32x16 a0 = chain(0);
-        const f32x16 a1 = chain(1);
-        epilogue(0, a0);
-        const f32x16 a2 = chain(2);
-        epilogue(1, a1);
-        const f32x16 a3 = chain(3);
-        epilogue(2, a2);
-        epilogue(3, a3);
+      for (int grp = 0; grp < kGemmGroups; ++grp) {
+        const int kb = tile * kGemmKT + 64 * grp + n;
+        // each epilogue follows the issue of the next chain, which runs meanwhile
+        const f32x16 a0 = chain(0, fa);
+        epilogue(1, pend, pend_k);
+        const f32x16 a1 = chain(1, fa);
+        if (grp + 1 < kGemmGroups) frags(cur, grp + 1, 0, fa);
+        epilogue(0, a0, kb);
+        const f32x16 a2 = chain(0, fb);
+        epilogue(1, a1, kb);
+        const f32x16 a3 = chain(1, fb);
+        if (grp + 1 < kGemmGroups) frags(cur, grp + 1, 1, fb);
+        epilogue(0, a2, kb + 32);
+        pend = a3;
+        pend_k = kb + 32;
       }
-      if (tile + 1 < ntiles) lstore(buf ^ 1);
-      if (PAGED) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile + 1 are in LDS
+      if (PAGED && tile + 2 < ntiles) {
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) pa[c] = pb[c];
+        for (int c = 0; c < kGemmLoads; ++c) pa[c] = __builtin_amdgcn_readfirstlane(pv[c]);
       }
-      __syncthreads();
+      __syncthreads();                      // ... and every wave's; every wave is done with cur
+    };
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      tile_body(ks0, ks1, tile);
+      if (tile + 1 < ntiles) tile_body(ks1, ks0, tile + 1);
     }
+    epilogue(1, pend, pend_k);
   }
 }
 

@@ -115,26 +115,31 @@ __device__ __forceinline__ void load_run(const float* row, int i, int n, uint32_
   }
 }
 
-__device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 // Writes the union of two ascending, disjoint position lists (in LDS) to out
-// in ascending order: each entry's slot is its index plus its rank in the
-// other list.
+// in ascending order.  Thread i produces the contiguous output run
+// [i * per, i * per + per): a binary search along the merge path finds how many
+// entries of la precede the run's start, then the run is merged sequentially.
 __device__ __forceinline__ void merge_lists(const int* la, int na, const int* lc, int nc, int32_t* out) {
-  for (int i = threadIdx.x; i < na; i += blockDim.x) {
-    const int a = la[i];
-    out[i + lower_bound(lc, nc, a)] = a;
+  const int total = na + nc;
+  const int per = (total + blockDim.x - 1) / blockDim.x;
+  const int d = min((int)threadIdx.x * per, total), dend = min(d + per, total);
+  int lo = max(0, d - nc), hi = min(d, na);
+  while (lo < hi) {  // first i with la[i] > lc[d - 1 - i]: i entries of la precede output d
+    const int mid = (lo + hi) >> 1;
+    if (la[mid] < lc[d - 1 - mid]) lo = mid + 1; else hi = mid;
   }
-  for (int j = threadIdx.x; j < nc; j += blockDim.x) {
-    const int c = lc[j];
-    out[j + lower_bound(la, na, c)] = c;
+  int i = lo, j = d - lo;
+  int a = i < na ? la[i] : INT_MAX, c = j < nc ? lc[j] : INT_MAX;
+  for (int o = d; o < dend; ++o) {
+    if (a < c) {
+      out[o] = a;
+      ++i;
+      a = i < na ? la[i] : INT_MAX;
+    } else {
+      out[o] = c;
+      ++j;
+      c = j < nc ? lc[j] : INT_MAX;
+    }
   }
 }
 
@@ -831,11 +836,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   const char* base = ws + (size_t)t * w.per_query;
   const int* list_a = reinterpret_cast<const int*>(base + w.a_off);
   const uint32_t* cand = reinterpret_cast<const uint32_t*>(base + w.c_off);
-  // List A (fewer than k <= KMAX entries) and the first kTopkSmall candidates
-  // are read together with the header; entries past the counts are stale and
-  // unused (the workspace holds kMaxTopk entries of A and kCandCapWs candidates).
+  // List A (fewer than k <= KMAX entries) and the first kCandCap candidates
+  // (all an LDS finish can hold) are read together with the header; entries
+  // past the counts are stale and unused (the workspace holds kMaxTopk entries
+  // of A and kCandCapWs candidates).
   constexpr int kSpecA = KMAX / kTkThreads;
-  constexpr int kSpecC = kTopkSmall / kTkThreads;
+  constexpr int kSpecC = (kCandCap + kTkThreads - 1) / kTkThreads;
+  static_assert(kSpecC * kTkThreads <= kCandCapWs, "speculative candidate reads stay in the workspace");
   int a_spec[kSpecA];
   u32x2 c_spec[kSpecC];
 #pragma unroll
@@ -875,11 +882,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
       sh.cand_key[i] = c_spec[u].x;
       sh.cand_pos[i] = (int)c_spec[u].y;
     }
-  }
-  for (int j = kTopkSmall + tid; j < c1; j += kTkThreads) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(cand + 2 * j);
-    sh.cand_key[j] = v.x;
-    sh.cand_pos[j] = (int)v.y;
   }
   __syncthreads();
   finish_from_candidates(sh, b1, above1, c1, krem, out);
