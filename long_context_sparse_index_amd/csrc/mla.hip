@@ -478,17 +478,38 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restri
   const int h = 16 * j + (lane & 15), g = lane >> 4;
   const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
   const uint16_t* src = o_part + (int64_t)t * S * kPartSlab + (((w * 4 + j) * 4 + jj) * 64 + lane) * 4;
-  float mstar = -1e30f;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) mstar = fmaxf(mstar, ml[s * kHeads * 2]);
-  float L = 0.f;
+  // Splits in chunks of kMergeChunk whose (m, l) pairs and partials are all
+  // requested before any is used (one memory latency per chunk).  Past S a
+  // slot repeats split S - 1 with weight 0.  A later chunk with a larger
+  // maximum rescales what is summed so far (with at most one chunk this is
+  // the plain two-pass sum).
+  constexpr int kMergeChunk = 32;
+  float mstar = -1e30f, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float wgt = exp2f(ml[s * kHeads * 2] - mstar) * ml[s * kHeads * 2 + 1];
-    L += wgt;
-    const u32x2 v = *reinterpret_cast<const u32x2*>(src + (int64_t)s * kPartSlab);
-    acc += wgt * f32x4{f16_lo(v.x), f16_hi(v.x), f16_lo(v.y), f16_hi(v.y)};
+  for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
+    f32x2 m_l[kMergeChunk];
+    u32x2 v[kMergeChunk];
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int s = min(s0 + u, S - 1);
+      m_l[u] = *reinterpret_cast<const f32x2*>(ml + (int64_t)s * kHeads * 2);
+      v[u] = *reinterpret_cast<const u32x2*>(src + (int64_t)s * kPartSlab);
+    }
+    float cm = mstar;
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) cm = s0 + u < S ? fmaxf(cm, m_l[u][0]) : cm;
+    if (cm > mstar) {
+      const float sc = exp2f(mstar - cm);
+      L *= sc;
+      acc *= sc;
+      mstar = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const float wgt = s0 + u < S ? exp2f(m_l[u][0] - mstar) * m_l[u][1] : 0.f;
+      L += wgt;
+      acc += wgt * f32x4{f16_lo(v[u].x), f16_hi(v[u].x), f16_lo(v[u].y), f16_hi(v[u].y)};
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 64 * w + 16 * g + 4 * jj) =
@@ -511,36 +532,57 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
   __shared__ float red[2][64 * 16];
   const int h = blockIdx.x, eb = blockIdx.y, mb = blockIdx.z;
   const int tid = threadIdx.x;
-  for (int u = tid; u < (kLat / 4) * (kUpEB / 8); u += 256) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int nt = wave & 1, kh = wave >> 1;
+  // All of the thread's W_UV pieces (4 units of 4 rows x 8 e) and the first
+  // tile's A operand are requested before any is used: the 64 KB slice of a
+  // workgroup is in flight at once rather than a unit at a time.
+  constexpr int kUnits = (kLat / 4) * (kUpEB / 8) / 256;
+  u32x4 rows[kUnits][4];
+#pragma unroll
+  for (int it = 0; it < kUnits; ++it) {
+    const int u = tid + 256 * it;
     const int q = u >> 3, r = u & 7;  // c = 4q..4q+3, e = 8r..8r+7
-    u32x4 rows[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rows[i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
+      rows[it][i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
+  }
+  auto a_load = [&](int mt, u32x4 a[16]) {
+    const int trow = min((mb * kUpMT + mt) * 32 + n, T - 1);
+    const uint16_t* ap = o_lat + ((int64_t)trow * kHeads + h) * kLat + kh * 256 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) a[ks] = ld16(ap + 16 * ks);
+  };
+  u32x4 a[16];
+  a_load(0, a);
+  // keep the first tile's A loads here, in flight with the W_UV loads (the
+  // compiler would otherwise sink them past the barrier, one latency each)
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+v"(a[ks]));
+#pragma unroll
+  for (int it = 0; it < kUnits; ++it) {
+    const int u = tid + 256 * it;
+    const int q = u >> 3, r = u & 7;
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
       const int dw = e8 >> 1;
-      const u32x2 v = {__builtin_amdgcn_perm(rows[1][dw], rows[0][dw], sel),
-                       __builtin_amdgcn_perm(rows[3][dw], rows[2][dw], sel)};
+      const u32x2 v = {__builtin_amdgcn_perm(rows[it][1][dw], rows[it][0][dw], sel),
+                       __builtin_amdgcn_perm(rows[it][3][dw], rows[it][2][dw], sel)};
       *reinterpret_cast<u32x2*>(&wt[(8 * r + e8) * kWvLds + 4 * q]) = v;
     }
   }
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, n = lane & 31;
-  const int nt = wave & 1, kh = wave >> 1;
   const uint16_t* bp = &wt[(nt * 32 + n) * kWvLds + kh * 256 + 8 * g];
   for (int mt = 0; mt < kUpMT; ++mt) {
     const int tbase = (mb * kUpMT + mt) * 32;
     if (tbase >= T) break;
-    const int trow = min(tbase + n, T - 1);
-    const uint16_t* ap = o_lat + ((int64_t)trow * kHeads + h) * kLat + kh * 256 + 8 * g;
+    if (mt > 0) a_load(mt, a);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
-      acc = mfma32(as_bf16x8(ld16(ap + 16 * ks)),
-                   as_bf16x8(*reinterpret_cast<const u32x4*>(bp + 16 * ks)), acc);
+      acc = mfma32(as_bf16x8(a[ks]), as_bf16x8(*reinterpret_cast<const u32x4*>(bp + 16 * ks)), acc);
     if (kh == 1) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) red[nt][lane * 16 + r] = acc[r];

@@ -655,24 +655,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
     const int j = wave + kSelWaves * u;
     word[u] = j < w.S ? reinterpret_cast<const uint32_t*>(lists + (size_t)j * w.list_stride)[lane] : 0u;
   }
-  auto load16 = [&](int i0, int lim, float v[kSelKeys]) {
+  // 16 scores from i0 on; groups of 4 past the row's stride (a multiple of 4)
+  // re-read its last group: every load is in bounds and unconditional, and
+  // scores at or past the slice's end are masked where they are used.
+  const int64_t last4 = ld - 4;
+  auto load16 = [&](int i0, float v[kSelKeys]) {
 #pragma unroll
     for (int q = 0; q < kSelKeys / 4; ++q) {
-      const int b = i0 + 4 * q;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (b + 3 < lim) x = *reinterpret_cast<const f32x4*>(row + b);
-      else
-        for (int e = 0; e < 4; ++e)
-          if (b + e < lim) x[e] = row[b + e];
+      const int64_t b = min((int64_t)i0 + 4 * q, last4);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(row + b);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
     }
   };
   float v0[kSelKeys];
-  {
-    const int lim = (int)min((int64_t)s0 + min(w.slice_keys, kSelStep), ld);
-    load16(s0 + kSelKeys * tid, lim, v0);
-  }
+  load16(s0 + kSelKeys * tid, v0);
   const int n = q_pos[t] + 1;
   if (n <= k) return;
   const int S = (n + w.slice_keys - 1) / w.slice_keys;  // slices holding keys (<= kMaxSlices)
@@ -782,7 +779,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
 #pragma unroll
       for (int e = 0; e < kSelKeys; ++e) v[e] = v0[e];
     } else {
-      load16(i0, end, v);
+      load16(i0, v);
     }
     // classify against the float edges of bin b1 (bit masks), keys only for
     // the kept scores
