@@ -396,8 +396,12 @@ constexpr int kSampleBlock = 64;    // scores per sampled block
 constexpr int kSampleStride = 16;   // one block in 16 is sampled
 
 template <int KMAX>
-__device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k, int32_t* out) {
+__device__ bool window_select(TkShared<KMAX>& sh, const float* row, int64_t ld, int n, int k, int32_t* out) {
   const int tid = threadIdx.x;
+  // Loads of 4 scores start at multiples of 4; those at or past the row's
+  // stride ld (a multiple of 4, >= n) re-read its last 4, so every load is in
+  // bounds and unconditional, and scores at or past n are masked where used.
+  const int64_t last4 = ld - 4;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
   // ---- sample: 16 threads x 4 scores per sampled block, 64 blocks per step;
@@ -413,10 +417,7 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
       const int m = m0 + u * kBlocksPerStep + tid / (kSampleBlock / 4);
       const int64_t i64 = (int64_t)m * kSampleStride * kSampleBlock + 4 * (tid % (kSampleBlock / 4));
       ii[u] = i64 < n ? (int)i64 : n;
-      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ii[u] + 3 < n) v[u] = *reinterpret_cast<const f32x4*>(row + ii[u]);
-      else
-        for (int e = 0; ii[u] + e < n && e < 4; ++e) v[u][e] = row[ii[u] + e];
+      v[u] = *reinterpret_cast<const f32x4*>(row + min(i64, last4));
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -444,23 +445,15 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
   // the scores of the next two steps are in flight while a step is compacted.
   // The window's bin edges become float thresholds, so a score is classified
   // by two compares into per-thread bit masks; keys are formed only for the
-  // few scores that are kept.  Scores past the row are NaN (no compare holds).
+  // few scores that are kept.  Masks drop the scores past the row.
   const float thr_hi = b_hi + 1 >= (uint32_t)kTkBins ? __uint_as_float(0x7FC00000u) : key_floor((b_hi + 1) << 20);
   const float thr_lo = key_floor(b_lo << 20);
   int nA = 0, nC = 0;
   auto fetch = [&](int i, f32x4 nx[kPerThread / 4]) {
-    const float nan = __uint_as_float(0x7FC00000u);
 #pragma unroll
-    for (int q = 0; q < kPerThread / 4; ++q) {
-      const int b = i + 4 * q;
-      f32x4 v = {nan, nan, nan, nan};
-      if (b + 3 < n) v = *reinterpret_cast<const f32x4*>(row + b);
-      else
-        for (int e = 0; e < 4; ++e)
-          if (b + e < n) v[e] = row[b + e];
-      nx[q] = v;
-    }
+    for (int q = 0; q < kPerThread / 4; ++q) nx[q] = *reinterpret_cast<const f32x4*>(row + min((int64_t)i + 4 * q, last4));
   };
+  static_assert(kPerThread <= 31, "valid-score mask");
   auto step = [&](int base, f32x4 nx[kPerThread / 4]) {
     const int i = base + kPerThread * tid;
     float f[kPerThread];
@@ -475,6 +468,10 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int n, int k
       mA |= (f[e] >= thr_hi ? 1u : 0u) << e;
       mW |= (f[e] >= thr_lo ? 1u : 0u) << e;
     }
+    const int rem = n - i;  // scores of this thread inside the row
+    const uint32_t valid = rem >= kPerThread ? (1u << kPerThread) - 1u : (rem > 0 ? (1u << rem) - 1u : 0u);
+    mA &= valid;
+    mW &= valid;
     const uint32_t mC = mW & ~mA;
     int tot;
     const int ex = block_excl_scan<kTkWaves>((__builtin_popcount(mA) << 16) | __builtin_popcount(mC),
@@ -525,7 +522,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __r
     return;
   }
   const float* row = scores + (int64_t)t * ld;
-  if (n >= kSampleMinRow && window_select(sh, row, n, k, out)) return;
+  if (n >= kSampleMinRow && window_select(sh, row, ld, n, k, out)) return;
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
   for (int base = 0; base < n; base += kStep) {
