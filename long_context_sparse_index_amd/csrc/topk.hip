@@ -405,49 +405,80 @@ __device__ bool window_select(TkShared<KMAX>& sh, const float* row, int64_t ld, 
   for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
   __syncthreads();
   // ---- sample: 16 threads x 4 scores per sampled block, 64 blocks per step;
-  // four steps' loads are issued before any is counted
-  int ns = 0;
-  constexpr int kBlocksPerStep = kTkThreads / (kSampleBlock / 4);
-  constexpr int kU = 4;
-  for (int m0 = 0; (int64_t)m0 * kSampleStride * kSampleBlock < n; m0 += kU * kBlocksPerStep) {
-    f32x4 v[kU];
-    int ii[kU];
+  // four steps' loads are issued before any is counted.  `act(key)` sees
+  // every sampled score of the row, in the same order on every pass.
+  auto sample_pass = [&](auto&& act) {
+    constexpr int kBlocksPerStep = kTkThreads / (kSampleBlock / 4);
+    constexpr int kU = 4;
+    for (int m0 = 0; (int64_t)m0 * kSampleStride * kSampleBlock < n; m0 += kU * kBlocksPerStep) {
+      f32x4 v[kU];
+      int ii[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int m = m0 + u * kBlocksPerStep + tid / (kSampleBlock / 4);
-      const int64_t i64 = (int64_t)m * kSampleStride * kSampleBlock + 4 * (tid % (kSampleBlock / 4));
-      ii[u] = i64 < n ? (int)i64 : n;
-      v[u] = *reinterpret_cast<const f32x4*>(row + min(i64, last4));
+      for (int u = 0; u < kU; ++u) {
+        const int m = m0 + u * kBlocksPerStep + tid / (kSampleBlock / 4);
+        const int64_t i64 = (int64_t)m * kSampleStride * kSampleBlock + 4 * (tid % (kSampleBlock / 4));
+        ii[u] = i64 < n ? (int)i64 : n;
+        v[u] = *reinterpret_cast<const f32x4*>(row + min(i64, last4));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ii[u] + e < n) act(score_key(v[u][e]));
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ii[u] + e < n) {
-          atomicAdd(&sh.hist[score_key(v[u][e]) >> 20], 1u);
-          ++ns;
-        }
-  }
+  };
+  int ns = 0;
+  sample_pass([&](uint32_t key) {
+    atomicAdd(&sh.hist[key >> 20], 1u);
+    ++ns;
+  });
   int ns_tot;
   (void)block_excl_scan<kTkWaves>(ns, sh.wave_tot, ns_tot);
+  // The k-th largest score of the row sits near rank ks of the ns_tot
+  // sampled scores (counted from the top); that rank varies by about
+  // sqrt(ks) between samples, so the window spans sample ranks ks -+ m with
+  // m ~ 3 deviations: its top edge lies above the k-th score and its bottom
+  // edge below it, except in rare rows (which take the full path).
   const int ks = max(1, (int)((int64_t)k * ns_tot / n));
-  find_bin<kTkBins>(sh, ks);
-  const int bs = sh.sel_bin;
-  // The sample's threshold sits at rank r of the ins sampled scores of bin bs,
-  // below `above` sampled scores of higher bins.  A neighbouring bin joins the
-  // window only when the threshold lies within ~3 sampling deviations of that
-  // edge (sampled counts of the row vary by about the square root).
-  const int above = sh.sel_above, ins = (int)sh.hist[bs], r = ks - above;
-  const float margin = 3.f * sqrtf((float)max(above, 1)) + 2.f;
-  const uint32_t b_hi = (uint32_t)min(bs + ((float)r <= margin ? 1 : 0), kTkBins - 1);
-  const uint32_t b_lo = (uint32_t)max(bs - ((float)(ins - r) < margin ? 1 : 0), 0);
+  const int m = (int)(3.f * sqrtf((float)ks)) + 2;
+  const int r_hi = max(ks - m, 1), r_lo = min(ks + m, ns_tot);
+  find_bin<kTkBins>(sh, r_hi);
+  const int bh = sh.sel_bin, ah = sh.sel_above;  // bin of rank r_hi, samples in higher bins
+  find_bin<kTkBins>(sh, r_lo);
+  const int bl = sh.sel_bin;                      // bin of rank r_lo
+  // Window edges as 32-bit keys [key_lo, key_hi): whole top-digit bins, or,
+  // when the window spans at most kSubBins / 256 bins, edges of sub-bins that
+  // add the next 8 key bits (a second pass over the same sample counts the
+  // sampled scores of those bins by sub-bin).
+  constexpr int kSubBins = 1024;
+  uint64_t key_hi = (uint64_t)(bh + 1) << 20;
+  uint32_t key_lo = (uint32_t)bl << 20;
+  if (bh - bl < kSubBins / 256) {
+    const int btop = min(bl + kSubBins / 256 - 1, kTkBins - 1);  // top bin of the sub-bin range
+    int a0 = ah;  // samples above the sub-bin range: above bh, less the bins bh+1..btop
+    for (int bb = bh + 1; bb <= btop; ++bb) a0 -= (int)sh.hist[bb];
+    __syncthreads();
+    for (int i = tid; i < kSubBins; i += kTkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    sample_pass([&](uint32_t key) {
+      const int bin = (int)(key >> 20);
+      if (bin >= bl && bin <= btop) atomicAdd(&sh.hist[((bin - bl) << 8) | ((key >> 12) & 0xFFu)], 1u);
+    });
+    __syncthreads();
+    find_bin<kSubBins>(sh, r_hi - a0);
+    const int sub_hi = sh.sel_bin;
+    find_bin<kSubBins>(sh, r_lo - a0);
+    const int sub_lo = sh.sel_bin;
+    key_hi = ((uint64_t)((uint32_t)bl << 8) + (uint32_t)sub_hi + 1u) << 12;
+    key_lo = (((uint32_t)bl << 8) + (uint32_t)sub_lo) << 12;
+  }
   // ---- exact ordered pass: above the window -> A, inside -> candidates;
   // the scores of the next two steps are in flight while a step is compacted.
-  // The window's bin edges become float thresholds, so a score is classified
+  // The window's edges become float thresholds, so a score is classified
   // by two compares into per-thread bit masks; keys are formed only for the
   // few scores that are kept.  Masks drop the scores past the row.
-  const float thr_hi = b_hi + 1 >= (uint32_t)kTkBins ? __uint_as_float(0x7FC00000u) : key_floor((b_hi + 1) << 20);
-  const float thr_lo = key_floor(b_lo << 20);
+  const float thr_hi = key_hi >= (1ull << 32) ? __uint_as_float(0x7FC00000u) : key_floor((uint32_t)key_hi);
+  const float thr_lo = key_floor(key_lo);
   int nA = 0, nC = 0;
   auto fetch = [&](int i, f32x4 nx[kPerThread / 4]) {
 #pragma unroll

@@ -102,6 +102,12 @@ def _topk_rows(kind, n_list, seed):
             r[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
             rows.append(r.astype(np.float32))
         return rows
+    if kind.startswith("log_"):
+        # Log-uniform scores: the sampled ranks around the threshold span
+        # several top-digit bins (log_mid: 2-4, refined by sub-bins) or many
+        # (log_wide: the window keeps whole bins).
+        span = np.float32(20.0 if kind == "log_mid" else 80.0)
+        return [np.exp(rng.uniform(-span, span, n).astype(np.float32)).astype(np.float32) for n in n_list]
     if kind == "inf_mix":  # a few infinities of both signs among normal scores
         rows = []
         for n in n_list:
@@ -129,6 +135,10 @@ TOPK_CASES = {
     "long_zeros_mix": ("zeros_mix", [70000, 204800], 8192),
     "long_inf_mix": ("inf_mix", [65536, 120000], 2048),
     "long_inf_mix_k250": ("inf_mix", [90000], 250),
+    # sampled window across several top-digit bins (sub-bin edges) and across many (whole bins)
+    "long_log_mid": ("log_mid", [70000, 204800], 2048),
+    "long_log_wide": ("log_wide", [70000, 204800], 2048),
+    "k8192_log_mid": ("log_mid", [204800], 8192),
     # index_topk as a runtime parameter above 2048 (kernels with larger LDS lists)
     "k4096_ragged": ("normal", [1, 4095, 4096, 4097, 9000, 40000], 4096),
     "k3000_signed": ("signed", [3000, 3001, 70000], 3000),
