@@ -21,12 +21,10 @@
 namespace dsa {
 
 // ---------------------------------------------------------------- absorb
-// grid (64 heads, query groups of kAbsorbTilesPerWg 32-query tiles, 16 / NW
-// column groups); NW waves per workgroup cover 32 latent columns each
-// (absorb_wave), so the q_nope tile of a step is fetched once per workgroup
-// and shared by its waves through L1.  Many queries: NW = 16 (one workgroup
-// per head and query group); few queries: NW = 4, so that W_UK is read by
-// four times as many CUs.
+// Few queries (up to 2 tiles of 32): grid (64 heads, query groups of
+// kAbsorbTilesPerWg 32-query tiles, 16 / NW column groups); NW waves per
+// workgroup cover 32 latent columns each (absorb_wave), so that W_UK is read
+// by many CUs.  More queries use head_gemm_kernel<192, 512> (below).
 constexpr int kAbsorbTilesPerWg = 8;
 
 template <int NW>
@@ -608,11 +606,8 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
 // ---------------------------------------------------------------- upproj, many queries
 // W_UV[h] is [c][e] with e contiguous, while MFMA operands take 8 consecutive
 // c per lane.  For large batches the weights are transposed once per call into
-// the workspace (W_UVt [64][256 e][512 c], 16.8 MB), and 8 waves per (head,
-// group of 32-query tiles) each keep the W_UVt fragments of 32 output dims
-// resident (32 K-steps) while the o_lat rows of a tile, read by all 8 waves,
-// come through L1.  Output blocks (32 queries x 32 dims) are staged in LDS and
-// written as whole 16-byte pieces of output rows.
+// the workspace (W_UVt [64][256 e][512 c], 16.8 MB) and the product runs as
+// head_gemm_kernel<512, 256> (below).
 constexpr int kUpTMin = 256;        // batches from this size use the transposed path
 constexpr int kUpTilesPerWg = 8;
 constexpr int kUpStageRow = 36;     // fp32 per staged row (32 + pad)
@@ -646,74 +641,116 @@ __global__ __launch_bounds__(256) void wuv_transpose_kernel(const uint16_t* __re
   st16(dst + 8, o1);
 }
 
-__global__ __launch_bounds__(512) void upproj_t_kernel(const uint16_t* __restrict__ o_lat,
-                                                       const uint16_t* __restrict__ w_uvt,
-                                                       void* __restrict__ out, int out_f32, int T) {
+// Head-batched product over 32-query tiles, for large batches:
+//   C[t, h, col] = sum_k A[(t*64 + h)*K + k] * B[(h*NCOL + col)*K + k]
+// (absorption: A = q_nope, B = W_UK, K = 192, NCOL = 512; up-projection:
+// A = o_lat, B = W_UVt, K = 512, NCOL = 256).  grid (64 heads, groups of
+// kUpTilesPerWg tiles); 8 waves, wave w owning columns [w*NCOL/8, +NCOL/8) with
+// their B fragments resident.  The A rows of a tile (32 x K bf16) are read
+// once per workgroup with coalesced 16-byte loads (consecutive threads,
+// consecutive pieces of a row) into a double-buffered, padded LDS tile while
+// the previous tile is computed; every wave takes its A fragments from LDS.
+// Output blocks (32 queries x 32 columns) are staged in LDS and written as
+// 16-byte pieces of output rows (bf16, round to nearest even, or fp32).
+template <int K, int NCOL>
+__global__ __launch_bounds__(512) void head_gemm_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B,
+                                                        void* __restrict__ C, int out_f32, int T) {
+  constexpr int kCW = NCOL / 8, kNB = kCW / 32, kKS = K / 16, kRowLds = K + 8;
+  constexpr int kChunks = 32 * K / 8;  // 16-byte pieces of an A tile
+  constexpr int kCPT = (kChunks + 511) / 512;
+  static_assert(kCW % 32 == 0 && K % 16 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t at[2][32 * kRowLds];
   __shared__ __attribute__((aligned(16))) float stage[8][32 * kUpStageRow];
-  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int e0 = wave * 32;
-  bf16x8 bw[kLat / 16];
-  const uint16_t* bp = w_uvt + ((int64_t)h * kV + e0 + n) * kLat + 8 * g;
-#pragma unroll
-  for (int j = 0; j < kLat / 16; ++j) bw[j] = as_bf16x8(ld16(bp + 16 * j));
   const int ntb = (T + 31) / 32;
   const int tb0 = blockIdx.y * kUpTilesPerWg, tb1 = min(ntb, tb0 + kUpTilesPerWg);
-  float* st = stage[wave];
-  // A operand in groups of 8 K-steps; the next group (of this tile or of the
-  // next tile) loads while the current group's MFMAs run
-  auto load_grp = [&](int tb, int j0, bf16x8* a) {
-    const int t = min(tb * 32 + n, T - 1);
-    const uint16_t* ap = o_lat + ((int64_t)t * kHeads + h) * kLat + 8 * g + 16 * j0;
+  if (tb0 >= tb1) return;
+  bf16x8 bw[kNB][kKS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = as_bf16x8(ld16(ap + 16 * j));
-  };
-  bf16x8 a[8], an[8];
-  if (tb0 < tb1) load_grp(tb0, 0, a);
-  for (int tb = tb0; tb < tb1; ++tb) {
-    f32x16 acc = {};
+  for (int nb = 0; nb < kNB; ++nb) {
+    const uint16_t* bp = B + ((int64_t)h * NCOL + wave * kCW + nb * 32 + n) * K + 8 * g;
 #pragma unroll
-    for (int j0 = 0; j0 < kLat / 16; j0 += 8) {
-      if (j0 + 8 < kLat / 16) load_grp(tb, j0 + 8, an);
-      else if (tb + 1 < tb1) load_grp(tb + 1, 0, an);
+    for (int j = 0; j < kKS; ++j) bw[nb][j] = as_bf16x8(ld16(bp + 16 * j));
+  }
+  u32x4 stg[kCPT];
+  auto gload = [&](int tb) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = mfma32(a[j], bw[j0 + j], acc);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = an[j];
-    }
-    // element r of lane (g, n): query row 8(r/4) + 4g + r%4 of the tile, output dim e0 + n
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st[(8 * (r >> 2) + 4 * g + (r & 3)) * kUpStageRow + n] = acc[r];
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int row = lane >> 1, half = lane & 1;  // lane writes 16 dims of one row
-    const int tr = tb * 32 + row;
-    const float* sp = st + row * kUpStageRow + 16 * half;
-    f32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(sp + 4 * i);
-    if (tr < T) {
-      const int64_t o = ((int64_t)tr * kHeads + h) * kV + e0 + 16 * half;
-      if (out_f32) {
-        float* dst = reinterpret_cast<float*>(out) + o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 4 * i) = v[i];
-      } else {
-        uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
-        u32x4 p0, p1;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          p0[2 * i] = pack_bf16x2(v[i][0], v[i][1]);
-          p0[2 * i + 1] = pack_bf16x2(v[i][2], v[i][3]);
-          p1[2 * i] = pack_bf16x2(v[2 + i][0], v[2 + i][1]);
-          p1[2 * i + 1] = pack_bf16x2(v[2 + i][2], v[2 + i][3]);
-        }
-        st16(dst, p0);
-        st16(dst + 8, p1);
+    for (int c = 0; c < kCPT; ++c) {
+      const int lin = tid + 512 * c;
+      if (kChunks % 512 == 0 || lin < kChunks) {
+        const int r = lin / (K / 8), q = lin - r * (K / 8);
+        const int t = min(tb * 32 + r, T - 1);
+        stg[c] = ld16(A + ((int64_t)t * kHeads + h) * K + 8 * q);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile's writes
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kCPT; ++c) {
+      const int lin = tid + 512 * c;
+      if (kChunks % 512 == 0 || lin < kChunks) {
+        const int r = lin / (K / 8), q = lin - r * (K / 8);
+        st16(&at[buf][r * kRowLds + 8 * q], stg[c]);
+      }
+    }
+  };
+  gload(tb0);
+  lstore(0);
+  __syncthreads();
+  float* st = stage[wave];
+  for (int tb = tb0; tb < tb1; ++tb) {
+    const int buf = (tb - tb0) & 1;
+    if (tb + 1 < tb1) gload(tb + 1);
+    f32x16 acc[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x16{};
+    const uint16_t* ap = &at[buf][n * kRowLds + 8 * g];
+#pragma unroll
+    for (int j = 0; j < kKS; ++j) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 16 * j));
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[nb] = mfma32(a, bw[nb][j], acc[nb]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      // element r of lane (g, n): query row 8(r/4) + 4g + r%4 of the tile, column n of block nb
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[(8 * (r >> 2) + 4 * g + (r & 3)) * kUpStageRow + n] = acc[nb][r];
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int row = lane >> 1, half = lane & 1;  // lane writes 16 columns of one row
+      const int tr = tb * 32 + row;
+      const float* sp = st + row * kUpStageRow + 16 * half;
+      f32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(sp + 4 * i);
+      if (tr < T) {
+        const int64_t o = ((int64_t)tr * kHeads + h) * NCOL + wave * kCW + nb * 32 + 16 * half;
+        if (out_f32) {
+          float* dst = reinterpret_cast<float*>(C) + o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 4 * i) = v[i];
+        } else {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(C) + o;
+          u32x4 p0, p1;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            p0[2 * i] = pack_bf16x2(v[i][0], v[i][1]);
+            p0[2 * i + 1] = pack_bf16x2(v[i][2], v[i][3]);
+            p1[2 * i] = pack_bf16x2(v[2 + i][0], v[2 + i][1]);
+            p1[2 * i + 1] = pack_bf16x2(v[2 + i][2], v[2 + i][3]);
+          }
+          st16(dst, p0);
+          st16(dst + 8, p1);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block's writes
+    }
+    if (tb + 1 < tb1) lstore(buf ^ 1);
+    __syncthreads();
   }
 }
 
@@ -772,7 +809,8 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     if (ntb <= 2)
       absorb_kernel<4><<<dim3(kHeads, nqg, 4), 256, 0, st>>>(q_nope, w_uk, q_lat, T);
     else
-      absorb_kernel<16><<<dim3(kHeads, nqg, 1), 1024, 0, st>>>(q_nope, w_uk, q_lat, T);
+      head_gemm_kernel<kNope, kLat><<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
+          q_nope, w_uk, q_lat, 0, T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -803,7 +841,7 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     wuv_transpose_kernel<<<dim3(kHeads, kLat / 64, kV / 64), 256, 0, st>>>(w_uv, w_uvt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    upproj_t_kernel<<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
+    head_gemm_kernel<kLat, kV><<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
         o_lat, w_uvt, out, out_f32, T);
     return hipGetLastError();
   }
