@@ -609,7 +609,9 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
 // the workspace (W_UVt [64][256 e][512 c], 16.8 MB) and the product runs as
 // head_gemm_kernel<512, 256> (below).
 constexpr int kUpTMin = 256;        // batches from this size use the transposed path
-constexpr int kUpTilesPerWg = 8;
+// 32-query tiles per head_gemm_kernel workgroup: at least 4 groups per head
+// (256 workgroups), at most 32 tiles
+inline int head_gemm_tiles(int ntb) { return ntb / 4 < 1 ? 1 : (ntb / 4 > 32 ? 32 : ntb / 4); }
 constexpr int kUpStageRow = 36;     // fp32 per staged row (32 + pad)
 
 __global__ __launch_bounds__(256) void wuv_transpose_kernel(const uint16_t* __restrict__ w_uv,
@@ -644,8 +646,9 @@ __global__ __launch_bounds__(256) void wuv_transpose_kernel(const uint16_t* __re
 // Head-batched product over 32-query tiles, for large batches:
 //   C[t, h, col] = sum_k A[(t*64 + h)*K + k] * B[(h*NCOL + col)*K + k]
 // (absorption: A = q_nope, B = W_UK, K = 192, NCOL = 512; up-projection:
-// A = o_lat, B = W_UVt, K = 512, NCOL = 256).  grid (64 heads, groups of
-// kUpTilesPerWg tiles); 8 waves, wave w owning columns [w*NCOL/8, +NCOL/8) with
+// A = o_lat, B = W_UVt, K = 512, NCOL = 256).  grid (64 heads, groups of tpw
+// tiles; head_gemm_tiles keeps >= 256 workgroups and amortises each
+// workgroup's B load over up to 32 tiles); 8 waves, wave w owning columns [w*NCOL/8, +NCOL/8) with
 // their B fragments resident.  The A rows of a tile (32 x K bf16) are read
 // once per workgroup with coalesced 16-byte loads (consecutive threads,
 // consecutive pieces of a row) into a double-buffered, padded LDS tile while
@@ -655,7 +658,7 @@ __global__ __launch_bounds__(256) void wuv_transpose_kernel(const uint16_t* __re
 template <int K, int NCOL>
 __global__ __launch_bounds__(512) void head_gemm_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
-                                                        void* __restrict__ C, int out_f32, int T) {
+                                                        void* __restrict__ C, int out_f32, int T, int tpw) {
   constexpr int kCW = NCOL / 8, kNB = kCW / 32, kKS = K / 16, kRowLds = K + 8;
   constexpr int kChunks = 32 * K / 8;  // 16-byte pieces of an A tile
   constexpr int kCPT = (kChunks + 511) / 512;
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(512) void head_gemm_kernel(const uint16_t* __restri
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int ntb = (T + 31) / 32;
-  const int tb0 = blockIdx.y * kUpTilesPerWg, tb1 = min(ntb, tb0 + kUpTilesPerWg);
+  const int tb0 = blockIdx.y * tpw, tb1 = min(ntb, tb0 + tpw);
   if (tb0 >= tb1) return;
   bf16x8 bw[kNB][kKS];
 #pragma unroll
@@ -809,8 +812,8 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     if (ntb <= 2)
       absorb_kernel<4><<<dim3(kHeads, nqg, 4), 256, 0, st>>>(q_nope, w_uk, q_lat, T);
     else
-      head_gemm_kernel<kNope, kLat><<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
-          q_nope, w_uk, q_lat, 0, T);
+      head_gemm_kernel<kNope, kLat><<<dim3(kHeads, (ntb + head_gemm_tiles(ntb) - 1) / head_gemm_tiles(ntb)), 512,
+                                        0, st>>>(q_nope, w_uk, q_lat, 0, T, head_gemm_tiles(ntb));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -841,8 +844,8 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
     wuv_transpose_kernel<<<dim3(kHeads, kLat / 64, kV / 64), 256, 0, st>>>(w_uv, w_uvt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    head_gemm_kernel<kLat, kV><<<dim3(kHeads, (ntb + kUpTilesPerWg - 1) / kUpTilesPerWg), 512, 0, st>>>(
-        o_lat, w_uvt, out, out_f32, T);
+    head_gemm_kernel<kLat, kV><<<dim3(kHeads, (ntb + head_gemm_tiles(ntb) - 1) / head_gemm_tiles(ntb)), 512, 0,
+                                 st>>>(o_lat, w_uvt, out, out_f32, T, head_gemm_tiles(ntb));
     return hipGetLastError();
   }
   upproj_kernel<<<dim3(kHeads, kV / kUpEB, (T + 32 * kUpMT - 1) / (32 * kUpMT)), 256, 0, st>>>(
