@@ -262,15 +262,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     qb[16] = as_bf16x8(ld16(qr));
     qb[17] = as_bf16x8(ld16(qr + 32));
   }
-  // bf16 cache: step tt issues the gather of tile tt + 2 (past the end too)
-  // right after its barrier, into the slot that step tt - 1 used: every wave
-  // has passed that barrier, so no wave still reads the slot.  One tile (5
-  // loads per wave) is then in flight at each wait.
+  // Ring slots of the bf16 tiles (three distinct arrays).
   auto slot = [&](int b) -> void* {
     return b == 0 ? (void*)tile0 : (b == 1 ? (void*)tile1 : (void*)tile2);
   };
   // QK, softmax and PV of one tile: bf16 tile tb, validity flags s_valid[vs].
-  auto compute = [&](const uint16_t* tb, int vs) {
+  // Two barriers: after QK (the tile maxima of both key halves meet), and
+  // before PV (P^T and the rescale factors are published).  `mid()` runs
+  // after the first (every wave is past the previous tile's PV), `pre_pv()`
+  // before the second.
+  auto compute = [&](const uint16_t* tb, int vs, auto&& mid, auto&& pre_pv) {
     int vmask[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[vs][hf * 16 + 4 * g + jj];
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     tmax = fmaxf(tmax, xor_lane(tmax, 32));
     if (g == 0) s_max[hf][hq] = tmax;
     lds_barrier();
+    mid();
     const float tile_max = fmaxf(s_max[0][hq], s_max[1][hq]);
     const float m_new = tile_max > m_ref + kRescaleLog2 ? tile_max : m_ref;
     const float alpha = exp2f(m_ref - m_new);
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     *reinterpret_cast<u32x2*>(&pT[hq * kPLds + hf * 16 + 4 * g]) =
         u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     if (hf == 0 && g == 0) s_alpha[hq] = alpha;
+    pre_pv();
     lds_barrier();
     // ---- PV
     {
@@ -364,23 +367,29 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       gather_idx(1, sidx, valid);
       gather_issue(sidx, valid, slot(1), 1);
     }
-    // Vector loads complete in issue order: with the 10 gather loads of this
-    // wave the most recent, vmcnt <= 10 means the query operands are in place.
-    wait_vm<2 * kNL>();
+    // Vector loads complete in issue order: vmcnt <= 5 means the query
+    // operands and this wave's loads of tile 0 are in place.
+    wait_vm<kNL>();
+    lds_barrier();
+    // Step tt issues the gather of tile tt + 2, right after its first barrier,
+    // into the slot of tile tt - 1 (every wave has finished that tile's PV),
+    // and before its second barrier waits for this wave's loads of tile
+    // tt + 1, which that barrier then publishes for step tt + 1.
     auto step = [&](int tt, auto BUFC) {
       constexpr int buf = decltype(BUFC)::value;
-      constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (used by step tt - 1)
-      int sidx[kNL], valid;
-      gather_idx(tt + 2, sidx, valid);  // positions are static: read ahead of the barrier
-      wait_vm<kNL>();
-      lds_barrier();
-      gather_issue(sidx, valid, slot(nbuf), nbuf);
-      if (tt < ntiles) compute(static_cast<const uint16_t*>(slot(buf)), buf);
+      constexpr int nbuf = (buf + 2) % kRing;  // slot of tile tt + 2 (that of tile tt - 1)
+      compute(static_cast<const uint16_t*>(slot(buf)), buf,
+              [&]() {
+                int sidx[kNL], valid;
+                gather_idx(tt + 2, sidx, valid);
+                gather_issue(sidx, valid, slot(nbuf), nbuf);
+              },
+              [&]() { wait_vm<kNL>(); });
     };
     for (int tt = 0; tt < ntiles; tt += kRing) {
       step(tt, std::integral_constant<int, 0>{});
-      step(tt + 1, std::integral_constant<int, 1>{});
-      step(tt + 2, std::integral_constant<int, 2>{});
+      if (tt + 1 < ntiles) step(tt + 1, std::integral_constant<int, 1>{});
+      if (tt + 2 < ntiles) step(tt + 2, std::integral_constant<int, 2>{});
     }
   } else {
     // INT4: raw tile j sits in raw slot j % 2, its bf16 expansion in tile
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       gather_idx(tt + 2, sidx, valid);
       lds_barrier();
       gather_issue(sidx, valid, buf == 0 ? (void*)raw0 : (void*)raw1, (tt + 2) % 3);
-      if (tt < ntiles) compute(buf == 0 ? tile0 : tile1, tt % 3);
+      if (tt < ntiles) compute(buf == 0 ? tile0 : tile1, tt % 3, [] {}, [] {});
       if (tt + 1 < ntiles) {
         wait_vm<kNL>();
         dequant_rows(buf == 0 ? raw_w1 : raw_w0, buf == 0 ? tile1 : tile0, wave, lane);
