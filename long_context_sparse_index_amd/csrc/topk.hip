@@ -64,16 +64,22 @@ __device__ void find_bin(const uint32_t* hist, int krem, int* wave_tot, int* sel
   constexpr int kBpt = NBINS >= NT ? NBINS / NT : 1;
   const int tid = threadIdx.x;
   const int top = NBINS - 1 - tid * kBpt;
-  uint32_t c[kBpt];
+  // The block's total is read in a lane-rotated order (step b reads bin
+  // (b + lane / 4) % kBpt of the block), which spreads the lanes of a read over
+  // the LDS banks (blocks of consecutive lanes are kBpt words apart); only
+  // the thread whose block holds the krem-th element reads it in order.
   int local = 0;
 #pragma unroll
   for (int b = 0; b < kBpt; ++b) {
-    c[b] = top - b >= 0 ? hist[top - b] : 0u;
-    local += (int)c[b];
+    const int e = (b + ((tid & 63) >> 2)) % kBpt;
+    local += top - e >= 0 ? (int)hist[top - e] : 0;
   }
   int total;
   const int above = block_excl_scan<NT / 64>(local, wave_tot, total);
   if (local > 0 && above < krem && krem <= above + local) {
+    uint32_t c[kBpt];
+#pragma unroll
+    for (int b = 0; b < kBpt; ++b) c[b] = top - b >= 0 ? hist[top - b] : 0u;
     int acc = above;
 #pragma unroll
     for (int b = 0; b < kBpt; ++b) {
@@ -737,24 +743,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
   // counts in descending bin order; thread i owns bins 4095-16i-15 .. 4095-16i
   {
     const int lo_bin = kTkBins - kSelBinsPT * (tid + 1);
-    uint32_t ca[kSelBinsPT], cp[kSelBinsPT];
-#pragma unroll
-    for (int q = 0; q < kSelBinsPT / 4; ++q) {
-      const u32x4 a4 = reinterpret_cast<const u32x4*>(sh.all + lo_bin)[q];
-      const u32x4 p4 = reinterpret_cast<const u32x4*>(sh.pre + lo_bin)[q];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ca[4 * q + e] = a4[e];
-        cp[4 * q + e] = p4[e];
-      }
-    }
-    // both counts stay below 2^21, so the two scans are plain 32-bit scans
+    // The thread's totals come from 16-byte reads in a lane-rotated order
+    // (step q reads quarter (q + lane / 2) % 4 of the thread's bins), which
+    // spreads a read over the LDS banks (consecutive lanes' bins are 64 bytes
+    // apart); only the thread that holds the threshold bin reads them in order.
     uint32_t mine_all = 0, mine_pre = 0;
 #pragma unroll
-    for (int e = 0; e < kSelBinsPT; ++e) {
-      mine_all += ca[e];
-      mine_pre += cp[e];
+    for (int q = 0; q < kSelBinsPT / 4; ++q) {
+      const int qq = (q + (lane >> 1)) & (kSelBinsPT / 4 - 1);
+      const u32x4 a4 = reinterpret_cast<const u32x4*>(sh.all + lo_bin)[qq];
+      const u32x4 p4 = reinterpret_cast<const u32x4*>(sh.pre + lo_bin)[qq];
+      mine_all += a4[0] + a4[1] + a4[2] + a4[3];
+      mine_pre += p4[0] + p4[1] + p4[2] + p4[3];
     }
+    // both counts stay below 2^21, so the two scans are plain 32-bit scans
     const int inc_all = wave_inclusive_scan((int)mine_all), inc_pre = wave_inclusive_scan((int)mine_pre);
     if (lane == 63) {
       sh.wave_tot[wave] = inc_all;
@@ -768,6 +770,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
       pre_above += i < wave ? (uint32_t)sh.wave_tot2[i] : 0u;
     }
     if (above < (uint32_t)k && (uint32_t)k <= above + mine_all) {
+      uint32_t ca[kSelBinsPT], cp[kSelBinsPT];
+#pragma unroll
+      for (int e = 0; e < kSelBinsPT; ++e) {
+        ca[e] = sh.all[lo_bin + e];
+        cp[e] = sh.pre[lo_bin + e];
+      }
 #pragma unroll
       for (int e = kSelBinsPT - 1; e >= 0; --e) {
         if (above + ca[e] >= (uint32_t)k) {
