@@ -201,6 +201,9 @@ MLA_CASES = {
     "tiny_ref_4k": (None, 2048),
     "decode_splits": (([3000, 2100, 5000], [(0, 2999), (1, 2099), (2, 100)]), 2048),   # T=3 -> key splits
     "many_queries_no_split": (([2600], [(0, 2300 + i) for i in range(300)]), 2048),      # T=300 -> one split
+    # T=100: head-batched absorption (more than 2 query tiles, ragged last tile) with the
+    # small-batch up-projection
+    "mid_queries": (([3000], [(0, 2880 + i) for i in range(100)]), 2048),
     # k = 8192: 64 splits of 128 keys for few queries; one split of 8192 keys for many
     "decode_splits_k8192": (([9000, 12000, 3000], [(0, 8999), (1, 11999), (2, 2999)]), 8192),
     "many_queries_k8192": (([9000], [(0, 8740 + i) for i in range(260)]), 8192),
