@@ -177,7 +177,6 @@ inline int gemm_split_keys(int T, int max_ctx) {
 }
 constexpr int kGemmLoads = kGemmKT * kIdxDim * 2 / (kGemmThreads * 16);  // direct loads per thread per tile
 constexpr int kDlStride = 4 * kGemmWaves;  // key rows between a thread's successive direct loads
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9: 32-bit data, no swizzle)
 constexpr int kDropOffset = 0x40000000;   // a store offset past every resource's end
 
 template <bool PAGED>

@@ -50,8 +50,11 @@ __global__ __launch_bounds__(NW * 64) void absorb_kernel(const uint16_t* __restr
 //        moves when a tile exceeds it by 2^8 (so P <= 256 and the running
 //        output is rescaled rarely); P^T goes to LDS as bf16;
 //   PV   wave w accumulates o^T[64 latent dims of slice w][64 heads] =
-//        c_tile^T . P^T; the latent operand is read transposed from LDS as
-//        4 consecutive dims x 8 keys and repacked with v_perm.
+//        c_tile^T . P^T; the latent operand (8 consecutive keys of one dim per
+//        lane) comes from the row-major tile by gfx950's transposing LDS read
+//        (ds_read_b64_tr_b16: within 16 lanes, source lane s reads 4
+//        consecutive dims of one key, and lane i receives element i % 4 of
+//        source lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4).
 // LDS tile layout: row r (one gathered key) = 72 slots of 16 bytes; logical
 // slot c of row r sits at r*72 + ((c & ~7) | ((c ^ r) & 7)), which keeps the
 // row reads of QK and the column reads of PV free of bank conflicts.
@@ -63,6 +66,7 @@ constexpr int kRing = 3;
 constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
 constexpr int kPartSlab = kHeads * kLat;  // fp16 values of one split partial
+constexpr int kAbsent = 1 << 30;          // flag of an absent position in the contiguous core's index list
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
 
@@ -137,15 +141,18 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __shared__ int s_valid[kRing][kKT];
   __shared__ int s_idx[kMaxTopk + 4 * kKT];  // the split's positions (<= k), -1 padded
   const int t = blockIdx.x, sp = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS bases of the loads stay in SGPRs
   const int l16 = lane & 15, g = lane >> 4;
   const int hg = wave & 3, hf = wave >> 2;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
   // Contiguous: s_idx holds positions, rows of the query's sequence start at
-  // kv_seq, and positions < 2^21 keep 32-bit element offsets in range.  Paged:
-  // s_idx holds pool rows (< 2^31) and offsets are 64-bit.  Absent entries
-  // hold ~r for the row r of position 0 (finite data, masked later).
+  // kv_seq, and positions < 2^21 keep 32-bit byte offsets in range; an absent
+  // entry is position 0 with bit 30 set (kAbsent), which the gather's 24-bit
+  // offset multiply ignores.  Paged: s_idx holds pool rows (< 2^31) and
+  // offsets are 64-bit; an absent entry holds ~r for the row r of position 0.
+  // Either way an absent entry gathers finite data that is masked later.
   const int seq = q_seq[t];
   // row stride in elements of the gather's unit: bf16 (576) or bytes (Q4: 400)
   using Unit = typename std::conditional<Q4, uint8_t, uint16_t>::type;
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   const int32_t* irow = idx + (int64_t)t * k;
   const int hq = hg * 16 + l16;  // head of this lane in QK / softmax
 
-  // o[e][j]: latent dim 64*wave + 16g + 4jj + e, head 16j + l16 (element jj)
+  // o[e][j]: latent dim 64*wave + 16e + 4g + jj, head 16j + l16 (element jj)
   f32x4 o[4][4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -181,6 +188,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
         const int j = b0 + tid + u * kCoreThreads;
         const int e = irow[min(j0 + j, k - 1)];  // in-row read, replaced past the split
         v[u] = j0 + j < j1 ? e : -1;
+        if (!PAGED) v[u] = v[u] >= 0 ? v[u] : kAbsent;
       }
       if (PAGED) {  // position -> pool row (all page loads, then the rows)
         int pg[kPer];
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   // rows (chunks past 99 refetch chunk 99 into the region's padding).
   constexpr int kNL = Q4 ? 2 : 5;  // gather loads per wave per tile
   int g_row[kNL];
-  uint32_t g_col[kNL];
+  uint32_t g_col[kNL], g_colb[kNL];
   auto blk_of = [&](int i) {  // bf16: 64-slot block of the tile written by load i
     return i < 4 ? 8 * i + wave : 32 + (wave & 3);
   };
@@ -232,7 +240,15 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       g_row[i] = r;
       g_col[i] = (uint32_t)((pc & ~7) | ((pc ^ r) & 7)) * 8u;
     }
+    g_colb[i] = g_col[i] * (uint32_t)sizeof(Unit);
   }
+  // Contiguous caches: a raw buffer resource over the sequence's rows (byte
+  // offsets below 2^32), made wave-uniform so that it stays in SGPRs.
+  const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
+  const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
+  const uint32_t kv_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kv_a >> 32));
+  const __amdgpu_buffer_rsrc_t kv_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)kv_hi << 32) | kv_lo), (short)0, (int)0xFFFFFFFF, kBufferWord3);
   auto gather_idx = [&](int tt, int sidx[kNL], int& valid) {
 #pragma unroll
     for (int i = 0; i < kNL; ++i) sidx[i] = s_idx[tt * kKT + g_row[i]];
@@ -241,17 +257,21 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   auto gather_issue = [&](const int sidx[kNL], int valid, void* dstt, int buf) {
 #pragma unroll
     for (int i = 0; i < kNL; ++i) {
-      // absent keys (and tiles past the end) fetch the row of position 0: finite data, masked later
-      const int r = sidx[i] >= 0 ? sidx[i] : ~sidx[i];
-      const Unit* src = PAGED ? kv_seq + (int64_t)r * kStride + g_col[i]
-                              : kv_seq + ((uint32_t)r * (uint32_t)kStride + g_col[i]);
       // (named pointers: the host pass rejects cast expressions as this builtin's operands)
       uint16_t* const dst = static_cast<uint16_t*>(dstt) +
                             (Q4 ? (wave * kQ4WaveBytes + i * 64 * 16) / 2 : blk_of(i) * 64 * 8);
-      const uint16_t* const gsrc = reinterpret_cast<const uint16_t*>(src);
-      __builtin_amdgcn_global_load_lds(gsrc, dst, 16, 0, 0);
+      if (PAGED) {
+        // absent keys (and tiles past the end) fetch the row of position 0: finite data, masked later
+        const int r = sidx[i] >= 0 ? sidx[i] : ~sidx[i];
+        const uint16_t* const gsrc = reinterpret_cast<const uint16_t*>(kv_seq + (int64_t)r * kStride + g_col[i]);
+        __builtin_amdgcn_global_load_lds(gsrc, dst, 16, 0, 0);
+      } else {
+        // one 24-bit multiply-add per load (bit 30 of an absent entry drops out)
+        const uint32_t off = (uint32_t)(sidx[i] & 0xFFFFFF) * (uint32_t)(kStride * sizeof(Unit)) + g_colb[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dst, 16, off, 0, 0, 0);
+      }
     }
-    if (tid < kKT) s_valid[buf][tid] = valid >= 0;
+    if (tid < kKT) s_valid[buf][tid] = PAGED ? valid >= 0 : (valid & kAbsent) == 0;
   };
   bf16x8 qb[18];
   {
@@ -302,18 +322,20 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     mid();
     const float tile_max = fmaxf(s_max[0][hq], s_max[1][hq]);
     const float m_new = tile_max > m_ref + kRescaleLog2 ? tile_max : m_ref;
-    const float alpha = exp2f(m_ref - m_new);
+    // v_exp_f32 directly: results below 2^-126 flush to zero (weights that
+    // small vanish against the reference maximum's weight 1 anyway)
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
     m_ref = m_new;
     float p[4];
     float ps = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      p[jj] = exp2f(z[jj] - m_new);
+      p[jj] = __builtin_amdgcn_exp2f(z[jj] - m_new);
       ps += p[jj];
     }
     l_part = l_part * alpha + ps;
     *reinterpret_cast<u32x2*>(&pT[hq * kPLds + hf * 16 + 4 * g]) =
-        u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        u32x2{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
     if (hf == 0 && g == 0) s_alpha[hq] = alpha;
     pre_pv();
     lds_barrier();
@@ -332,28 +354,21 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[e][j] *= al[j];
       }
-      // dims 64*wave + 4*l16 .. +3 live in logical slot 8*wave + l16/2, half l16&1
-      u32x2 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * g + i;
-        v[i] = *reinterpret_cast<const u32x2*>(tb + swz(r, 8 * wave + (l16 >> 1)) * 8 + 4 * (l16 & 1));
-      }
       bf16x8 pb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         pb[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pT[(16 * j + l16) * kPLds + 8 * g]));
+      // A of MFMA e: keys 8g .. 8g+7 of dim 64*wave + 16e + l16.  Read h of a
+      // lane (source s = l16) covers key 8g + 4h + s/4, dims 16e + 4(s%4) ..+3
+      // of the wave's slice: logical slot 8*wave + 2e + (s%4)/2, half (s%4)&1.
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t x0 = (e < 2) ? v[2 * d].x : v[2 * d].y;
-          const uint32_t x1 = (e < 2) ? v[2 * d + 1].x : v[2 * d + 1].y;
-          f[d] = __builtin_amdgcn_perm(x1, x0, sel);
-        }
-        const bf16x8 fa = as_bf16x8(f);
+        const int c = 8 * wave + 2 * e + ((l16 & 3) >> 1);
+        const uint16_t* const a0 = tb + swz(8 * g + (l16 >> 2), c) * 8 + 4 * (l16 & 1);
+        const uint16_t* const a1 = tb + swz(8 * g + 4 + (l16 >> 2), c) * 8 + 4 * (l16 & 1);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a1));
+        const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[e][j] = mfma16(fa, pb[j], o[e][j]);
       }
@@ -436,7 +451,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     if (hf == 0) s_m[hq] = m_ref;
   }
   __syncthreads();
-  const int dim0 = 64 * wave + 16 * g;
+  const int dim0 = 64 * wave + 4 * g;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 16 * j + l16;
@@ -445,10 +460,10 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = o_lat + ((int64_t)t * kHeads + h) * kLat + dim0;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<u32x2*>(dst + 4 * jj) =
-            u32x2{pack_bf16x2(o[0][j][jj] * inv, o[1][j][jj] * inv),
-                  pack_bf16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<u32x2*>(dst + 16 * e) =
+            u32x2{pack_bf16x2(o[e][j][0] * inv, o[e][j][1] * inv),
+                  pack_bf16x2(o[e][j][2] * inv, o[e][j][3] * inv)};
     } else {
       // Partials are normalised by the split's own sum (a convex combination of
       // cache rows, so fp16 holds them to 2^-11) and keep the accumulator order
@@ -457,9 +472,9 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = o_part + ((int64_t)t * S + sp) * kPartSlab + ((wave * 4 + j) * 4) * 256 + lane * 4;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<u32x2*>(dst + jj * 256) =
-            u32x2{pack_f16x2(o[0][j][jj] * inv, o[1][j][jj] * inv), pack_f16x2(o[2][j][jj] * inv, o[3][j][jj] * inv)};
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<u32x2*>(dst + e * 256) =
+            u32x2{pack_f16x2(o[e][j][0] * inv, o[e][j][1] * inv), pack_f16x2(o[e][j][2] * inv, o[e][j][3] * inv)};
       if (wave == 0 && g == 0) {
         const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
         ml_part[base * 2] = s_m[h];
@@ -472,8 +487,8 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 // ---------------------------------------------------------------- merge
 // Split partials of (query t, split s) form one slab of kHeads * kLat fp16
 // values, each normalised by its split's sum l, in the core's accumulator
-// order: element e of the 4-value group number ((w * 4 + j) * 4 + jj) * 64 +
-// lane is latent dim 64w + 16(lane / 16) + 4jj + e of head 16j + lane % 16.
+// order: element i of the 4-value group number ((w * 4 + j) * 4 + e) * 64 +
+// lane is latent dim 64w + 16e + 4(lane / 16) + i of head 16j + lane % 16.
 // ml_part[t][s][h] = (reference max m, sum l).  grid (T, 32): workgroup
 // (t, 4w + j) combines latent dims 64w .. 64w+63 of heads 16j .. 16j+15, one
 // group of every split per thread, weighting split s by 2^(m_s - max m) l_s.
@@ -519,7 +534,7 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restri
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 64 * w + 16 * g + 4 * jj) =
+  *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + h) * kLat + 64 * w + 16 * jj + 4 * g) =
       u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
 }
 
