@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __shared__ float s_alpha[kHeads];
   __shared__ float s_l[2][kHeads];
   __shared__ float s_m[kHeads];
-  __shared__ int s_valid[kRing][kKT];
+  __shared__ float s_bias[kRing][kKT];  // 0 for a present key, -inf for an absent one
   __shared__ int s_idx[kMaxTopk + 4 * kKT];  // the split's positions (<= k), -1 padded
   const int t = blockIdx.x, sp = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dst, 16, off, 0, 0, 0);
       }
     }
-    if (tid < kKT) s_valid[buf][tid] = PAGED ? valid >= 0 : (valid & kAbsent) == 0;
+    if (tid < kKT) s_bias[buf][tid] = (PAGED ? valid >= 0 : (valid & kAbsent) == 0) ? 0.f : -INFINITY;
   };
   bf16x8 qb[18];
   {
@@ -286,15 +286,15 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   auto slot = [&](int b) -> void* {
     return b == 0 ? (void*)tile0 : (b == 1 ? (void*)tile1 : (void*)tile2);
   };
-  // QK, softmax and PV of one tile: bf16 tile tb, validity flags s_valid[vs].
+  // QK, softmax and PV of one tile: bf16 tile tb, key biases s_bias[vs].
   // Two barriers: after QK (the tile maxima of both key halves meet), and
   // before PV (P^T and the rescale factors are published).  `mid()` runs
   // after the first (every wave is past the previous tile's PV), `pre_pv()`
   // before the second.
   auto compute = [&](const uint16_t* tb, int vs, auto&& mid, auto&& pre_pv) {
-    int vmask[4];
+    float bias[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vmask[jj] = s_valid[vs][hf * 16 + 4 * g + jj];
+    for (int jj = 0; jj < 4; ++jj) bias[jj] = s_bias[vs][hf * 16 + 4 * g + jj];
     // ---- QK: keys hf*16 + 4g + jj of head hq; three independent MFMA chains
     // (one chain of 18 would serialise on its accumulator)
     f32x4 sc;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     float tmax = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float v = vmask[jj] ? sc[jj] * scale_log2 : -INFINITY;
+      const float v = fmaf(sc[jj], scale_log2, bias[jj]);  // (rounds like the plain product)
       z[jj] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     }
   } else {
     // INT4: raw tile j sits in raw slot j % 2, its bf16 expansion in tile
-    // j % 2, its validity flags in s_valid[j % 3].  A wave expands its own
+    // j % 2, its key biases in s_bias[j % 3].  A wave expands its own
     // rows of tile tt + 1 at the end of step tt (its loads of that tile are
     // then the older of its two tiles in flight); step tt + 1's barrier
     // publishes them.  Tile tt + 2 is gathered into the raw slot of tile tt,
