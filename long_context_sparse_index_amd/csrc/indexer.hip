@@ -152,9 +152,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
 // the chunk that its slot holds.
 // A tile is computed in groups of 64 keys.  The fragments of key block 0 of
 // the next group are read as soon as the two MFMA chains that use block 0 of
-// the current group are issued (likewise block 1), and the last epilogue of a
-// group runs after the next group's first chain is issued (across the tile
-// barrier too), so LDS latency and epilogue VALU overlap MFMA work.
+// the current group are issued (likewise block 1); each chain's fold of its
+// head rows follows the issue of the next chain, and the two chains of a
+// query (keys 0-31 and 32-63 of a group) are summed and stored together
+// through one lane-half swap (the last pair of a group after the next group's
+// first chain, across the tile barrier too), so LDS latency and epilogue VALU
+// overlap MFMA work.
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kGemmQPW = 2;
@@ -164,8 +167,8 @@ constexpr int kGemmGroups = kGemmKT / 64;
 // Keys per workgroup: the whole context when the query blocks alone fill the
 // chip (fewest workgroup prologues and no uneven last round: 5.59 ms against
 // 5.96 ms with 8,192-key splits at 4,096 queries x 204,800 keys), else the
-// context split so that about 256 workgroups run; at most 2^24 keys (buffer
-// offsets of a split stay below kDropOffset).
+// context split so that about 256 workgroups run; at most 2^24 keys (store
+// offsets of a split stay far below 2^32).
 constexpr int kGemmMinWgs = 256;
 constexpr int kGemmMaxSplit = 1 << 24;
 inline int gemm_split_keys(int T, int max_ctx) {
@@ -177,7 +180,6 @@ inline int gemm_split_keys(int T, int max_ctx) {
 }
 constexpr int kGemmLoads = kGemmKT * kIdxDim * 2 / (kGemmThreads * 16);  // direct loads per thread per tile
 constexpr int kDlStride = 4 * kGemmWaves;  // key rows between a thread's successive direct loads
-constexpr int kDropOffset = 0x40000000;   // a store offset past every resource's end
 
 template <bool PAGED>
 __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
@@ -289,15 +291,22 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
       for (int j = 0; j < 8; ++j) acc = mfma32(qa[qi][j], b[j], acc);
       return acc;
     };
-    // column n of the accumulator: key kbeg + koff of query qi (lanes n and
-    // n + 32 hold 16 head rows each; g == 0 stores the sum)
-    auto epilogue = [&](int qi, const f32x16& acc, int koff) {
+    // Column n of a chain's accumulator is one key of query qi; lanes n and
+    // n + 32 hold 16 of its 32 head rows each.  reduce() folds a lane's rows;
+    // store_pair() takes the folds of the two chains of one query over keys
+    // kb .. kb + 31 (a) and kb + 32 .. kb + 63 (b): one lane-half swap
+    // (a's upper half for b's lower half) and one add leave the score of key
+    // kb + l in lane l, and all 64 lanes store (offsets from kbeg).
+    auto reduce = [&](int qi, const f32x16& acc) {
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) part = fmaf(wr[qi][r], relu(acc[r]), part);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // part(n) + part(n + 32)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[qi], g == 0 ? 4 * koff : kDropOffset, 0, 0);
+      return part;
+    };
+    auto store_pair = [&](int qi, float pa, float pb, int kb) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // a(l) + a(l + 32) | b(l - 32) + b(l)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[qi], 4 * (kb + lane), 0, 0);
     };
     auto frags = [&](const uint16_t* buf, int grp, int nt, bf16x8 b[8]) {
       const uint16_t* base = buf + (64 * grp + 32 * nt) * kIdxDim;
@@ -316,7 +325,8 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     __syncthreads();
     bf16x8 fa[8], fb[8];  // fragments of key blocks 0 and 1 of the current group
     f32x16 pend = {};          // accumulator of (query 1, block 1) of the previous group
-    int pend_k = split_keys;   // its key offset (split_keys: none, the store is dropped)
+    float pend_p = 0.f;        // fold of (query 1, block 0) of the previous group
+    int pend_k = split_keys;   // their first key (split_keys: none, the stores are dropped)
     // tile in cur, tile + 1 loaded into nxt meanwhile
     auto tile_body = [&](const uint16_t* cur, uint16_t* nxt, int tile) {
       if (tile + 1 < ntiles) dma(tile + 1, pa, nxt);
@@ -325,20 +335,21 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
       frags(cur, 0, 1, fb);
 #pragma unroll
       for (int grp = 0; grp < kGemmGroups; ++grp) {
-        const int kb = tile * kGemmKT + 64 * grp + n;
-        // each epilogue follows the issue of the next chain, which runs meanwhile
+        const int kb = tile * kGemmKT + 64 * grp;
+        // each fold follows the issue of the next chain, which runs meanwhile
         const f32x16 a0 = chain(0, fa);
-        epilogue(1, pend, pend_k);
+        store_pair(1, pend_p, reduce(1, pend), pend_k);
         const f32x16 a1 = chain(1, fa);
         if (grp + 1 < kGemmGroups) frags(cur, grp + 1, 0, fa);
-        epilogue(0, a0, kb);
+        const float p0 = reduce(0, a0);
         const f32x16 a2 = chain(0, fb);
-        epilogue(1, a1, kb);
+        const float p1 = reduce(1, a1);
         const f32x16 a3 = chain(1, fb);
         if (grp + 1 < kGemmGroups) frags(cur, grp + 1, 1, fb);
-        epilogue(0, a2, kb + 32);
+        store_pair(0, p0, reduce(0, a2), kb);
         pend = a3;
-        pend_k = kb + 32;
+        pend_p = p1;
+        pend_k = kb;
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile + 1 are in LDS
       if (PAGED && tile + 2 < ntiles) {
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
       tile_body(ks0, ks1, tile);
       if (tile + 1 < ntiles) tile_body(ks1, ks0, tile + 1);
     }
-    epilogue(1, pend, pend_k);
+    store_pair(1, pend_p, reduce(1, pend), pend_k);
   }
 }
 
