@@ -40,8 +40,9 @@ design notes of the repository):
   * INT4 latent cache ([G5] section six recommends INT4 KV-cache quantisation
     and a saving above 60%, no format): per cache row, the 512 latent values
     in 8 groups of 64, each with scale s = bf16(absmax / 7) and codes
-    q = clamp(rint(x / s), -7, 7) (fp32 division, ties to even, both decided
-    in fp32 as the kernel does); the 64 rope values stay bf16.  400 bytes per
+    q = clamp(rint(x / s), -7, 7) (each division correctly rounded in fp32,
+    rint ties to even: the format fixes its arithmetic in fp32, so a code is a
+    well-defined integer); the 64 rope values stay bf16.  400 bytes per
     row: 256 bytes of codes (element 2i in the low nibble of byte i, two's
     complement), 8 bf16 scales, 64 bf16 rope.  Dequantised latent = q * s.
   * MLA over the kept rows with explicit per-head up-projection
@@ -152,7 +153,11 @@ def mla_explicit(q_nope_t, q_rope_t, kv_rows, w_uk, w_uv,
 
 def mla_explicit_f64(q_nope_t, q_rope_t, rows, w_uk, w_uv, scale: float = DEFAULT_SCALE) -> np.ndarray:
     """``mla_explicit`` over cache rows already given as float64 [n,576] (e.g.
-    dequantised INT4 rows); queries and weights are bf16 bit patterns."""
+    dequantised INT4 rows); queries and weights are bf16 bit patterns.
+
+    Pinned on its own: equal to ``mla_explicit`` on rows that are bf16 values,
+    equal to torch's SDPA in fp64 (K/V up-projected explicitly) on dequantised
+    INT4 rows, and the zero-query / single-row softmax special cases."""
     qn = bf16_bits_to_f64(q_nope_t)
     qr = bf16_bits_to_f64(q_rope_t)
     c = rows[:, :KV_LORA_RANK]

@@ -254,6 +254,63 @@ def test_rope_term_and_scale_enter_logits():
     np.testing.assert_allclose(np.log(p[0] / p[1]), (qr @ (ra - rb)) / 16.0, rtol=1e-10)
 
 
+def _sdpa_rows_f64(inp, t, rows):
+    """torch SDPA (fp64) of query t over cache rows given as float64 [n,576]
+    (latent | rope), K/V up-projected explicitly; batched products take
+    contiguous operands."""
+    rows = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.float64))
+    c, r = rows[:, :512].contiguous(), rows[:, 512:].contiguous()
+    wuk = torch.from_numpy(synth.bf16_to_f32(inp.w_uk).astype(np.float64))
+    wuv = torch.from_numpy(synth.bf16_to_f32(inp.w_uv).astype(np.float64))
+    qn = torch.from_numpy(synth.bf16_to_f32(inp.q_nope[t]).astype(np.float64))
+    qr = torch.from_numpy(synth.bf16_to_f32(inp.q_rope[t]).astype(np.float64))
+    kn = torch.matmul(c.unsqueeze(0).expand(64, -1, -1).contiguous(), wuk)   # [64,n,192]
+    kk = torch.cat([kn, r.unsqueeze(0).expand(64, -1, -1)], -1)             # [64,n,256]
+    vv = torch.matmul(c.unsqueeze(0).expand(64, -1, -1).contiguous(), wuv)   # [64,n,256]
+    qq = torch.cat([qn, qr], -1).unsqueeze(1)                               # [64,1,256]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)        # scale 1/sqrt(256)
+    return o[:, 0, :].numpy()
+
+
+def test_mla_over_f64_rows_equals_bf16_form_on_exact_rows():
+    """mla_explicit_f64 (cache rows given as float64, e.g. dequantised INT4 rows)
+    computes the same attention as mla_explicit when the rows are bf16 values."""
+    inp = synth.custom([90], [(0, 89)], seed=31)
+    sel = np.array([0, 7, 8, 30, 31, 64, 88, 89])
+    a = O.mla_explicit(inp.q_nope[0], inp.q_rope[0], inp.kv[sel], inp.w_uk, inp.w_uv)
+    b = O.mla_explicit_f64(inp.q_nope[0], inp.q_rope[0], O.bf16_bits_to_f64(inp.kv[sel]),
+                           inp.w_uk, inp.w_uv)
+    np.testing.assert_allclose(b, a, rtol=1e-15, atol=1e-15)
+
+
+def test_mla_over_dequantised_int4_rows_equals_sdpa():
+    """Over dequantised INT4 rows (values that are not bf16 numbers in general:
+    code x bf16 scale) mla_explicit_f64 equals torch SDPA in fp64 with the K/V
+    up-projected explicitly.  A swapped latent/rope slice, a wrong head of W_UK
+    or W_UV, a dropped rope term or a wrong scale each fails this."""
+    inp = synth.custom([200], [(0, 199), (0, 120)], seed=32)
+    rows = O.dequantize_kv_int4(O.quantize_kv_int4(inp.kv[:200]))
+    for t, sel in ((0, np.arange(0, 200, 3)), (1, np.array([5, 6, 7, 100, 120]))):
+        got = O.mla_explicit_f64(inp.q_nope[t], inp.q_rope[t], rows[sel], inp.w_uk, inp.w_uv)
+        np.testing.assert_allclose(got, _sdpa_rows_f64(inp, t, rows[sel]), rtol=1e-12, atol=1e-13)
+
+
+def test_mla_over_f64_rows_softmax_special_cases():
+    """Zero query: uniform weights, so the output is the mean of the rows'
+    values (pins the rows used, independently of QK); one row: its value."""
+    inp = synth.custom([40], [(0, 39)], seed=33)
+    rows = O.dequantize_kv_int4(O.quantize_kv_int4(inp.kv[:40]))
+    sel = np.array([1, 2, 19, 33])
+    zn, zr = np.zeros_like(inp.q_nope[0]), np.zeros_like(inp.q_rope[0])
+    out = O.mla_explicit_f64(zn, zr, rows[sel], inp.w_uk, inp.w_uv)
+    wuv = synth.bf16_to_f32(inp.w_uv).astype(np.float64)
+    mean_c = rows[sel, :512].mean(0)
+    one = O.mla_explicit_f64(inp.q_nope[0], inp.q_rope[0], rows[[17]], inp.w_uk, inp.w_uv)
+    for h in range(64):
+        np.testing.assert_allclose(out[h], mean_c @ wuv[h], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(one[h], rows[17, :512] @ wuv[h], rtol=1e-14, atol=1e-15)
+
+
 # ------------------------------------------------------------------ whole path
 def test_selection_only_coupling():
     """P7: the indexer only ranks.  Scaling w by a power of two scales every score
