@@ -38,8 +38,11 @@
  *     waited for: buffers must stay valid until the stream has passed it.
  *     Input caches and weights are never written.
  *   - Errors: every host-checkable precondition is checked before anything is
- *     enqueued, and a failing call enqueues nothing.  DSA_ERR_LAUNCH reports a
- *     failed kernel launch (see dsa_last_hip_error).  Device-side
+ *     enqueued, and a call that fails such a check enqueues nothing.
+ *     DSA_ERR_LAUNCH reports a failed kernel launch (see dsa_last_hip_error);
+ *     the kernels of the same call enqueued before the failing one (a call
+ *     launches several, and dsa_forward one set per query chunk) stay
+ *     enqueued, and the call's outputs are then unspecified.  Device-side
  *     preconditions (q_seq[t] < num_seqs, 0 <= q_pos[t] < rows of that
  *     sequence, every cache row and block_table page inside its allocation,
  *     idx entries in {-1} U [0, q_pos[t]]) are not checked: violating them is
@@ -199,7 +202,7 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
  * clamp(rint(x / scale), -7, 7), both divisions correctly rounded in fp32,
  * ties to even (scale 0 gives code 0); rope copied.  Bit-exact.  Both arrays
  * device, 16-byte aligned, not overlapping; rows 0 .. 2^40 (0: nothing
- * enqueued).  Errors: DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_ALIGN, DSA_ERR_DEVICE,
+ * enqueued; any count runs, the kernel strides over the rows).  Errors: DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_ALIGN, DSA_ERR_DEVICE,
  * DSA_ERR_LAUNCH.
  */
 dsa_status dsa_quantize_kv_int4(const dsa_bf16* kv, int64_t rows, uint8_t* kv_int4, void* stream);

@@ -14,11 +14,11 @@
 namespace dsa {
 
 // One wave per row: lane l holds latent elements 8l .. 8l+7 (group l / 8).
-__global__ __launch_bounds__(256) void quantize_kv_int4_kernel(const uint16_t* __restrict__ kv, int64_t rows,
-                                                               uint8_t* __restrict__ out) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
+// Grid-stride over rows (a grid of at most kQuantMaxWgs workgroups of 4 waves).
+constexpr int64_t kQuantMaxWgs = 1 << 20;
+
+__device__ __forceinline__ void quantize_row(const uint16_t* __restrict__ kv, int64_t row,
+                                             uint8_t* __restrict__ out, int lane) {
   const uint16_t* src = kv + row * kRow;
   uint8_t* dst = out + row * kQ4Row;
   const u32x4 v = ld16(src + 8 * lane);
@@ -48,8 +48,17 @@ __global__ __launch_bounds__(256) void quantize_kv_int4_kernel(const uint16_t* _
   if (lane < 8) *reinterpret_cast<u32x4*>(dst + kQ4RopeOff + 16 * lane) = ld16(src + kLat + 8 * lane);
 }
 
+__global__ __launch_bounds__(256) void quantize_kv_int4_kernel(const uint16_t* __restrict__ kv, int64_t rows,
+                                                               uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += stride)
+    quantize_row(kv, row, out, lane);
+}
+
 hipError_t launch_quantize_kv_int4(const uint16_t* kv, int64_t rows, uint8_t* out, hipStream_t st) {
-  quantize_kv_int4_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(kv, rows, out);
+  const int64_t wgs = (rows + 3) / 4 < kQuantMaxWgs ? (rows + 3) / 4 : kQuantMaxWgs;
+  quantize_kv_int4_kernel<<<(unsigned)wgs, 256, 0, st>>>(kv, rows, out);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@
 // to the lower positions and the output needs no sort.
 //
 // Two launch shapes compute the same result:
-//   * one 1024-thread workgroup per row (many rows, e.g. a prefill chunk);
+//   * one 512-thread workgroup per row (many rows, e.g. a prefill chunk);
 //   * for few rows (decode), steps 1 and 2 are split over slices of the row:
 //     each slice's sparse top-digit list (written by the key scan itself, or by
 //     a histogram pass); then per slice the row histogram and the slice's output

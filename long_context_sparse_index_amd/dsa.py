@@ -1,8 +1,10 @@
 """Thin Python binding of libdsa.so (the C ABI in include/dsa.h).
 
-Argument marshalling only: tensors are checked for dtype, shape, device and
-contiguity, and their device pointers are handed to the library together with
-torch's current HIP stream.  Every step of the computation runs in the HIP
+Argument marshalling only: every tensor, inputs and caller-supplied outputs and
+workspaces alike, is checked for dtype, shape (outputs exactly, workspaces for
+their byte size), device and contiguity before the library is called, and the
+device pointers are handed to the library together with torch's current HIP
+stream.  Every step of the computation runs in the HIP
 kernels; there is no fallback.  If the library is missing, calls raise.
 """
 from __future__ import annotations
@@ -106,13 +108,69 @@ def _stream() -> int:
 
 
 def _bf16(x: torch.Tensor, name: str, shape) -> torch.Tensor:
+    """bf16 bits (bfloat16, int16 or uint16), contiguous, on the device; `shape`
+    a full shape, or (None, n) for [rows, n] with any number of rows."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor, got {type(x).__name__}")
     if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{name}: expected bf16 bits, got {x.dtype}")
+    if shape is not None:
+        ok = x.dim() == len(shape) and all(s is None or int(a) == s for a, s in zip(x.shape, shape))
+        if not ok:
+            raise ValueError(f"{name}: shape {tuple(x.shape)} does not match {tuple(shape)}")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError(f"{name}: must be a contiguous device tensor")
-    if shape is not None and tuple(x.shape) != tuple(shape):
-        raise ValueError(f"{name}: shape {tuple(x.shape)} != {tuple(shape)}")
     return x
+
+
+def _int32_out(x: torch.Tensor, name: str, shape) -> torch.Tensor:
+    """A caller-supplied int32 output array of exactly `shape`, contiguous, on the device."""
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.int32:
+        raise ValueError(f"{name}: expected an int32 tensor")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(x.shape)} != {tuple(shape)}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous device tensor")
+    return x
+
+
+def _out_tensor(out: torch.Tensor, T: int, od: int) -> torch.Tensor:
+    """A caller-supplied attention output: [T, 64, 256] of the requested element type."""
+    want = torch.float32 if od == OUT_F32 else torch.bfloat16
+    if not isinstance(out, torch.Tensor) or out.dtype != want:
+        raise ValueError(f"out: expected a {want} tensor (out_dtype), got "
+                         f"{getattr(out, 'dtype', type(out).__name__)}")
+    if tuple(out.shape) != (T, HEADS, D_V):
+        raise ValueError(f"out: shape {tuple(out.shape)} != {(T, HEADS, D_V)}")
+    if not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out: must be a contiguous device tensor")
+    return out
+
+
+def _scores_tensor(scores: torch.Tensor, T: int, max_ctx: int) -> torch.Tensor:
+    """A score matrix: row-major fp32 on the device with at least T rows of max_ctx."""
+    if not isinstance(scores, torch.Tensor) or scores.dtype != torch.float32 or scores.dim() != 2 \
+            or scores.stride(1) != 1:
+        raise ValueError("scores: expected a row-major 2-D fp32 tensor")
+    if scores.shape[0] < T or scores.shape[1] < max_ctx:
+        raise ValueError(f"scores: shape {tuple(scores.shape)} is smaller than ({T}, {max_ctx})")
+    if not scores.is_cuda:
+        raise ValueError("scores: must be a device tensor")
+    return scores
+
+
+def _workspace(ws: torch.Tensor, need: int) -> torch.Tensor:
+    """A caller-supplied workspace: a contiguous device tensor of at least `need` bytes
+    (any element type; its size is passed in bytes)."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("ws: must be a contiguous device tensor")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"ws: {ws.numel() * ws.element_size()} bytes < the {need} bytes needed")
+    return ws
+
+
+def _nbytes(ws: Optional[torch.Tensor]) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
 
 
 class Batch:
@@ -161,18 +219,27 @@ def _kv(batch: "Batch", kv: torch.Tensor) -> torch.Tensor:
                 or kv.shape[1] != KV_INT4_ROW_BYTES:
             raise ValueError(f"kv: expected a contiguous [rows, {KV_INT4_ROW_BYTES}] uint8 device tensor (INT4 rows)")
         return kv
-    return _bf16(kv, "kv", None)
+    return _bf16(kv, "kv", (None, D_KV))
 
 
 def dsa_quantize_kv_int4(kv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 latent-cache rows [rows, 576] -> INT4 rows [rows, 400] uint8."""
-    _bf16(kv, "kv", None)
-    if kv.dim() != 2 or kv.shape[1] != D_KV:
-        raise ValueError("kv: expected [rows, 576]")
+    _bf16(kv, "kv", (None, D_KV))
     if out is None:
         out = torch.empty((kv.shape[0], KV_INT4_ROW_BYTES), dtype=torch.uint8, device=kv.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (kv.shape[0], KV_INT4_ROW_BYTES) \
+            or not out.is_cuda or not out.is_contiguous():
+        raise ValueError(f"out: expected a contiguous [{kv.shape[0]}, {KV_INT4_ROW_BYTES}] uint8 device tensor")
     _check("dsa_quantize_kv_int4", lib().dsa_quantize_kv_int4(_ptr(kv), kv.shape[0], _ptr(out), _stream()))
     return out
+
+
+def _out_dtype(out_dtype) -> int:
+    if out_dtype == torch.float32:
+        return OUT_F32
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    raise ValueError(f"out_dtype: expected torch.bfloat16 or torch.float32, got {out_dtype}")
 
 
 def score_ld(max_ctx: int) -> int:
@@ -197,11 +264,10 @@ def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tenso
     T = batch.T
     _bf16(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM))
     _bf16(w, "w", (T, IDX_HEADS))
-    _bf16(k_idx, "k_idx", None)
+    _bf16(k_idx, "k_idx", (None, IDX_DIM))
     if scores is None:
         scores = torch.empty((T, score_ld(batch.max_ctx)), dtype=torch.float32, device=q_idx.device)
-    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
-        raise ValueError("scores: expected a row-major 2-D fp32 tensor")
+    _scores_tensor(scores, T, batch.max_ctx)
     cb = batch.c()
     _check("dsa_index_scores", lib().dsa_index_scores(ctypes.byref(cb), _ptr(q_idx), _ptr(w), _ptr(k_idx),
                                                       _ptr(scores), scores.stride(0), _stream()))
@@ -211,18 +277,22 @@ def dsa_index_scores(batch: Batch, q_idx, w, k_idx, scores: Optional[torch.Tenso
 def dsa_topk(batch: Batch, scores: torch.Tensor, k: int = INDEX_TOPK,
              idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Top-k positions [T, k] int32, ascending, -1 padded."""
-    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
-        raise ValueError("scores: expected a row-major 2-D fp32 tensor")
+    _scores_tensor(scores, batch.T, batch.max_ctx)
+    if not 1 <= k <= MAX_TOPK:
+        raise ValueError(f"k: {k} outside 1..{MAX_TOPK}")
     if idx is None:
         idx = torch.empty((batch.T, k), dtype=torch.int32, device=scores.device)
+    _int32_out(idx, "idx", (batch.T, k))
+    need = dsa_workspace_bytes(OP_TOPK, batch.T, batch.max_ctx, k)
     if isinstance(ws, str) and ws == NO_WORKSPACE:
         ws = None
     elif ws is None:
-        need = dsa_workspace_bytes(OP_TOPK, batch.T, batch.max_ctx, k)
         ws = torch.empty(need, dtype=torch.uint8, device=scores.device) if need else None
+    else:
+        _workspace(ws, need)
     cb = batch.c()
     _check("dsa_topk", lib().dsa_topk(ctypes.byref(cb), _ptr(scores), scores.stride(0), k, _ptr(idx),
-                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+                                      _ptr(ws), _nbytes(ws), _stream()))
     return idx
 
 
@@ -236,19 +306,23 @@ def dsa_sparse_mla_attn(batch: Batch, q_nope, q_rope, kv, w_uk, w_uv, idx: torch
     _kv(batch, kv)
     _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
     _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
-    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != T or not idx.is_contiguous():
-        raise ValueError("idx: expected a contiguous [T, k] int32 tensor")
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 2 or not 1 <= int(idx.shape[1]) <= MAX_TOPK:
+        raise ValueError(f"idx: expected a [T, k] int32 tensor with 1 <= k <= {MAX_TOPK}")
     k = int(idx.shape[1])
-    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    _int32_out(idx, "idx", (T, k))
+    od = _out_dtype(out_dtype)
     if out is None:
         out = torch.empty((T, HEADS, D_V), dtype=torch.float32 if od else torch.bfloat16, device=kv.device)
+    _out_tensor(out, T, od)
     need = dsa_workspace_bytes(OP_SPARSE_MLA, T, batch.max_ctx, k)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=kv.device)
+    else:
+        _workspace(ws, need)
     cb = batch.c()
     _check("dsa_sparse_mla_attn",
            lib().dsa_sparse_mla_attn(ctypes.byref(cb), _ptr(q_nope), _ptr(q_rope), _ptr(kv), _ptr(w_uk), _ptr(w_uv),
-                                     _ptr(idx), k, softmax_scale, _ptr(out), od, _ptr(ws), ws.numel(), _stream()))
+                                     _ptr(idx), k, softmax_scale, _ptr(out), od, _ptr(ws), _nbytes(ws), _stream()))
     return out
 
 
@@ -260,23 +334,30 @@ def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k
     T = batch.T
     _bf16(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM))
     _bf16(w, "w", (T, IDX_HEADS))
-    _bf16(k_idx, "k_idx", None)
+    _bf16(k_idx, "k_idx", (None, IDX_DIM))
     _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
     _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
     _kv(batch, kv)
     _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
     _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
-    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if not 1 <= k <= MAX_TOPK:
+        raise ValueError(f"k: {k} outside 1..{MAX_TOPK}")
+    od = _out_dtype(out_dtype)
     if out is None:
         out = torch.empty((T, HEADS, D_V), dtype=torch.float32 if od else torch.bfloat16, device=kv.device)
-    if return_idx and idx is None:
-        idx = torch.empty((T, k), dtype=torch.int32, device=kv.device)
+    _out_tensor(out, T, od)
+    if return_idx:
+        if idx is None:
+            idx = torch.empty((T, k), dtype=torch.int32, device=kv.device)
+        _int32_out(idx, "idx", (T, k))
     if ws is None:
         need = dsa_workspace_bytes(OP_FORWARD, T, batch.max_ctx, k)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=kv.device)
+    else:  # a smaller workspace runs the queries in chunks; one query must fit
+        _workspace(ws, dsa_workspace_bytes(OP_FORWARD, min(T, 1), batch.max_ctx, k))
     cb = batch.c()
     _check("dsa_forward",
            lib().dsa_forward(ctypes.byref(cb), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q_nope), _ptr(q_rope),
                              _ptr(kv), _ptr(w_uk), _ptr(w_uv), k, softmax_scale, _ptr(out), od,
-                             _ptr(idx) if return_idx else None, _ptr(ws), ws.numel(), _stream()))
+                             _ptr(idx) if return_idx else None, _ptr(ws), _nbytes(ws), _stream()))
     return out, (idx if return_idx else None)

@@ -41,8 +41,9 @@ SCORE_MAX_ABS = 1e-4
 
 
 def check_selection(got_idx: np.ndarray, oracle_scores: np.ndarray, oracle_idx: np.ndarray, k: int,
-                    tol: float = 1e-4):
-    """The GPU selection may differ from the oracle's only at near-ties of the k-th score.
+                    tol: float = 1e-4, atol: float = None):
+    """The GPU selection may differ from the oracle's only at near-ties of the k-th score:
+    within tol * max(1, |theta|) of it, or within atol when that is given.
 
     Returns the number of differing positions; asserts validity of the rest."""
     n = oracle_scores.shape[0]
@@ -58,6 +59,34 @@ def check_selection(got_idx: np.ndarray, oracle_scores: np.ndarray, oracle_idx: 
     theta = np.sort(oracle_scores.astype(np.float64))[::-1][k - 1]
     sym = np.setxor1d(g, o)
     if len(sym):
-        assert np.all(np.abs(oracle_scores[sym].astype(np.float64) - theta) <= tol * max(1.0, abs(theta))), \
+        lim = atol if atol is not None else tol * max(1.0, abs(theta))
+        assert np.all(np.abs(oracle_scores[sym].astype(np.float64) - theta) <= lim), \
             f"selection differs away from the threshold: {sym[:10]}"
     return len(sym)
+
+
+def check_selection_vs_scores(got_idx: np.ndarray, gpu_scores: np.ndarray, oracle_scores: np.ndarray,
+                              oracle_idx: np.ndarray, k: int):
+    """End-to-end selection of one query, checked exactly.
+
+    * the GPU's scores of the query's row agree with the oracle's within SCORE_MAX_ABS;
+    * the GPU's selection is bit-exactly the oracle's top-k rule applied to the GPU's
+      own scores (so the selector adds no error of its own);
+    * where it differs from the oracle's selection, the oracle score of every
+      differing position lies within 2*eps of the oracle's k-th score, eps being the
+      row's largest score error: scores moved by at most eps can only swap such
+      positions (the k-th largest value moves by at most eps too).
+
+    Returns (number of differing positions, eps)."""
+    n = oracle_scores.shape[0]
+    g = np.asarray(gpu_scores[:n], dtype=np.float32)
+    eps = float(np.abs(g.astype(np.float64) - oracle_scores.astype(np.float64)).max())
+    assert eps <= SCORE_MAX_ABS, f"score error {eps:.3e}"
+    assert np.array_equal(got_idx, oracle_topk_of(g, k)), "selection is not the top-k of the GPU's own scores"
+    nd = check_selection(got_idx, oracle_scores, oracle_idx, k, atol=2.0 * eps + 1e-12)
+    return nd, eps
+
+
+def oracle_topk_of(scores_f32: np.ndarray, k: int) -> np.ndarray:
+    from oracle import dsa_oracle as O
+    return O.topk_select(scores_f32, k)
