@@ -196,6 +196,31 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same path and results, with no workspace argument.  Its workspace is a
+ * static device array of DSA_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held
+ * from the first call on that device until the process ends; batches whose
+ * workspace (dsa_workspace_bytes(DSA_OP_FORWARD, T, max_ctx, k)) exceeds it run
+ * in query chunks that fit, as dsa_forward does with a small workspace.  The
+ * call allocates and frees nothing.
+ *   Every call on one device shares that device's array: calls that overlap on
+ *   one device (several host threads, or several streams with work in flight at
+ *   once) race and give undefined results; serialise them (one stream, or
+ *   stream order).  Nothing in the array needs clearing between calls (every
+ *   byte a call reads it has written first).
+ *   Errors: as dsa_forward; DSA_ERR_WORKSPACE if one query's workspace exceeds
+ *   the array (not reached for any valid max_ctx and k); DSA_ERR_DEVICE if the
+ *   array's device address cannot be obtained.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_forward_noalloc(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                               const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                               const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                               int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                               int32_t* idx_out, void* stream);
+
+/*
  * INT4 latent cache (page 3, section 六; format at DSA_KV_INT4): quantises
  * `rows` bf16 cache rows kv [rows,576] into kv_int4 [rows,400] bytes.  Per
  * group of 64 latent values: scale = bf16(absmax / 7) and code =

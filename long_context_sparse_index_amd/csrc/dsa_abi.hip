@@ -3,6 +3,7 @@
 // host synchronisation, nothing enqueued when a check fails.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "dsa.h"
 #include "dsa_common.h"
@@ -119,6 +120,53 @@ FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
   f.mla = dsa::plan_mla(T, k);
   f.total = end + f.mla.total;
   return f;
+}
+
+// The whole path over one workspace: query chunks sized to ws_bytes.
+dsa_status forward_impl(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                        const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                        const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+}  // namespace
+
+// Scratch of dsa_forward_noalloc: the workspace of callers that cannot
+// allocate, one copy per device for the life of the process.  Host code never
+// uses this name as an address: the device address of each device's copy comes
+// from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kNoAllocScratchBytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the current device's scratch (resolved once per device,
+// with that device current).
+dsa_status scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorInvalidDevice);
+    return DSA_ERR_DEVICE;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) {
+        g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        return DSA_ERR_DEVICE;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return DSA_OK;
 }
 
 }  // namespace
@@ -255,6 +303,38 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
                        const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k, softmax_scale, out,
+                      out_dtype, idx_out, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_forward_noalloc(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                               const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                               const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                               int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                               int32_t* idx_out, void* stream) {
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (batch->num_queries == 0) return DSA_OK;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  // One query must fit the scratch (the workspace of larger batches is chunked).
+  if (plan_forward(1, batch->max_ctx, k, idx_out == nullptr).total > kNoAllocScratchBytes)
+    return DSA_ERR_WORKSPACE;
+  if ((s = check_device()) != DSA_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != DSA_OK) return s;
+  return forward_impl(batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k, softmax_scale, out,
+                      out_dtype, idx_out, ws, kNoAllocScratchBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+dsa_status forward_impl(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_bf16* w,
+                        const dsa_bf16* k_idx, const dsa_bf16* q_nope, const dsa_bf16* q_rope,
+                        const void* kv, const dsa_bf16* w_uk, const dsa_bf16* w_uv,
+                        int32_t k, float softmax_scale, void* out, int32_t out_dtype,
+                        int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   dsa_status s = check_batch(batch);
   if (s != DSA_OK) return s;
   if (batch->num_queries == 0) return DSA_OK;
@@ -319,4 +399,4 @@ dsa_status dsa_forward(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa_
   return DSA_OK;
 }
 
-}  // extern "C"
+}  // namespace

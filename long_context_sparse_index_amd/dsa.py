@@ -64,6 +64,8 @@ _SIGS = {
                              _P, ctypes.c_int32, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "dsa_forward": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                      _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "dsa_forward_noalloc": ([ctypes.POINTER(_CBatch), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                             ctypes.c_float, _P, ctypes.c_int32, _P, _P], ctypes.c_int),
     "dsa_index_share_schedule": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P], ctypes.c_int),
     "dsa_quantize_kv_int4": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int),
     "dsa_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], ctypes.c_size_t),
@@ -361,3 +363,35 @@ def dsa_forward(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, k
                              _ptr(kv), _ptr(w_uk), _ptr(w_uv), k, softmax_scale, _ptr(out), od,
                              _ptr(idx) if return_idx else None, _ptr(ws), _nbytes(ws), _stream()))
     return out, (idx if return_idx else None)
+
+
+def dsa_forward_noalloc(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk, w_uv, out: torch.Tensor,
+                        idx: Optional[torch.Tensor] = None, k: int = INDEX_TOPK,
+                        softmax_scale: float = DEFAULT_SCALE) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dsa_forward over the library's static per-device scratch (no workspace; the
+    library allocates nothing).  The caller supplies `out` [T, 64, 256] (bf16 or
+    fp32, which selects the output type) and optionally `idx` [T, k] int32; this
+    wrapper allocates nothing either.  Calls overlapping on one device race."""
+    T = batch.T
+    _bf16(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM))
+    _bf16(w, "w", (T, IDX_HEADS))
+    _bf16(k_idx, "k_idx", (None, IDX_DIM))
+    _bf16(q_nope, "q_nope", (T, HEADS, D_NOPE))
+    _bf16(q_rope, "q_rope", (T, HEADS, D_ROPE))
+    _kv(batch, kv)
+    _bf16(w_uk, "w_uk", (HEADS, D_LAT, D_NOPE))
+    _bf16(w_uv, "w_uv", (HEADS, D_LAT, D_V))
+    if not 1 <= k <= MAX_TOPK:
+        raise ValueError(f"k: {k} outside 1..{MAX_TOPK}")
+    if not isinstance(out, torch.Tensor):
+        raise ValueError("out: the caller supplies the output tensor")
+    od = _out_dtype(out.dtype)
+    _out_tensor(out, T, od)
+    if idx is not None:
+        _int32_out(idx, "idx", (T, k))
+    cb = batch.c()
+    _check("dsa_forward_noalloc",
+           lib().dsa_forward_noalloc(ctypes.byref(cb), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q_nope),
+                                     _ptr(q_rope), _ptr(kv), _ptr(w_uk), _ptr(w_uv), k, softmax_scale,
+                                     _ptr(out), od, _ptr(idx), _stream()))
+    return out, idx

@@ -175,3 +175,19 @@ def test_quantize_kv_int4_validation(L):
     assert f(FAKE, 4, None, None) == 1
     assert f(FAKE + 8, 4, FAKE, None) == 3
     assert f(FAKE, 4, FAKE + 4, None) == 3
+
+
+def test_forward_noalloc_validation(L):
+    """The no-allocation forward checks its arguments like dsa_forward (no workspace
+    argument: its workspace is the library's static per-device scratch)."""
+    b = _batch()
+    f = L.dsa_forward_noalloc
+    args = [FAKE] * 8
+    assert f(None, *args, 2048, 0.0625, FAKE, 0, None, None) == 1
+    assert f(ctypes.byref(b), *args, 0, 0.0625, FAKE, 0, None, None) == 2
+    assert f(ctypes.byref(b), *args, 8193, 0.0625, FAKE, 0, None, None) == 2
+    assert f(ctypes.byref(_batch(T=0)), *args, 2048, 0.0625, FAKE, 0, None, None) == 0
+    # the largest single-query workspace fits the 64 MiB scratch
+    assert L.dsa_workspace_bytes(dsa.OP_FORWARD, 1, 1 << 21, 8192) <= 64 << 20
+    if not _gpu():
+        assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, None, None) == 7
