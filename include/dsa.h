@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 #define DSA_INDEX_HEADS 32
 #define DSA_INDEX_DIM 128
@@ -84,8 +84,19 @@ typedef enum dsa_status {
   DSA_ERR_WORKSPACE = 4,    /* workspace too small (see dsa_workspace_bytes) */
   DSA_ERR_UNSUPPORTED = 5,  /* an option value this build does not implement */
   DSA_ERR_LAUNCH = 6,       /* a kernel launch failed (dsa_last_hip_error) */
-  DSA_ERR_DEVICE = 7        /* the current HIP device is missing or is not gfx950 */
+  DSA_ERR_DEVICE = 7,       /* the current HIP device is missing or is not gfx950 */
+  DSA_ERR_DEVICE_ARGS = 8   /* DSA_CHECK_DEVICE_ARGS=1 found a device-side precondition violated
+                               (see dsa_last_device_arg_flags); nothing of the op was enqueued */
 } dsa_status;
+
+/* Bits of a device-side argument check (dsa_check_device_args,
+ * dsa_last_device_arg_flags). */
+#define DSA_ARG_Q_SEQ 1u       /* some q_seq[t] outside [0, num_seqs) */
+#define DSA_ARG_Q_POS 2u       /* some q_pos[t] outside [0, max_ctx) */
+#define DSA_ARG_CACHE_ROW 4u   /* a visible position maps outside the caches: seq_row0[b] < 0 or
+                                  seq_row0[b] + q_pos[t] >= cache_rows (contiguous), or a block_table
+                                  entry of pages 0 .. q_pos[t]/page_size outside the pool (paged) */
+#define DSA_ARG_IDX 8u         /* an idx entry that is neither -1 nor in [0, q_pos[t]] */
 
 /* Output element type of the attention output. */
 enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 };
@@ -254,6 +265,32 @@ dsa_status dsa_quantize_kv_int4(const dsa_bf16* kv, int64_t rows, uint8_t* kv_in
  */
 dsa_status dsa_index_share_schedule(int32_t num_layers, int32_t num_dense, int32_t index_topk_freq,
                                     int32_t* source);
+
+/*
+ * Device-side argument check (the device-only preconditions listed at the top:
+ * the selector keeps positions of the query's own history, page 4 §2.2).
+ * Enqueues kernels on `stream` that set *flags (a device word, 4-byte aligned;
+ * cleared first) to the DSA_ARG_* bits of every violated precondition, 0 when
+ * all hold.  Reads only q_seq, q_pos, seq_row0 / block_table and idx, never the
+ * caches.  idx [T,k] may be NULL (not checked; k is then ignored);
+ * cache_rows > 0 bounds the rows of the caches (k_idx and kv; in pages of
+ * page_size rows when paged), 0 leaves the upper row bound unchecked.
+ * Errors: DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_ALIGN, DSA_ERR_DEVICE,
+ * DSA_ERR_LAUNCH (host checks as for the ops).
+ *
+ * Debug mode: with the environment variable DSA_CHECK_DEVICE_ARGS=1 at the
+ * time of a call, dsa_index_scores, dsa_topk, dsa_sparse_mla_attn, dsa_forward
+ * and dsa_forward_noalloc first run this check (idx for dsa_sparse_mla_attn;
+ * cache rows unchecked) into a word of the library, wait for `stream`, and return
+ * DSA_ERR_DEVICE_ARGS, with nothing of the op enqueued, when any bit is set.
+ * The wait makes such calls blocking (not usable under graph capture).
+ */
+dsa_status dsa_check_device_args(const dsa_batch* batch, const int32_t* idx, int32_t k, int64_t cache_rows,
+                                 uint32_t* flags, void* stream);
+
+/* DSA_ARG_* bits found by the debug-mode check of the last call on this thread
+ * that returned DSA_ERR_DEVICE_ARGS (0 = none). */
+uint32_t dsa_last_device_arg_flags(void);
 
 /* Workspace bytes an op needs for num_queries queries (host only; 0 = none).
  * Returns 0 as well for invalid arguments (then the op itself reports them). */

@@ -2,6 +2,7 @@
 // chunking and kernel launches on the caller's stream.  No allocation, no
 // host synchronisation, nothing enqueued when a check fails.
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -171,9 +172,73 @@ dsa_status scratch_address(void** ptr) {
 
 }  // namespace
 
+// Result word of the debug-mode device-argument check (DSA_CHECK_DEVICE_ARGS=1),
+// one per device; its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint32_t argcheck_word[64];
+
+namespace {
+
+thread_local uint32_t g_last_arg_flags = 0;
+std::mutex g_argcheck_mu;  // the word is shared by all calls on a device
+std::atomic<void*> g_argword_ptr[kMaxDevices];
+
+bool debug_device_args() {
+  const char* e = std::getenv("DSA_CHECK_DEVICE_ARGS");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+// Debug mode: check the device-side preconditions of a call, wait for the
+// result, and report DSA_ERR_DEVICE_ARGS before anything of the op is enqueued.
+dsa_status debug_check(const dsa_batch* b, const int32_t* idx, int32_t k, hipStream_t st) {
+  if (!debug_device_args()) return DSA_OK;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorInvalidDevice);
+    return DSA_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_argcheck_mu);
+  void* w = g_argword_ptr[dev].load(std::memory_order_relaxed);
+  if (w == nullptr) {
+    e = hipGetSymbolAddress(&w, HIP_SYMBOL(argcheck_word));
+    if (e != hipSuccess || w == nullptr) {
+      g_last_hip_error = (int32_t)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return DSA_ERR_DEVICE;
+    }
+    g_argword_ptr[dev].store(w, std::memory_order_relaxed);
+  }
+  (void)hipGetLastError();
+  e = dsa::launch_argcheck(to_launch(b, 0, b->num_queries), b->num_seqs, 0, idx, k, static_cast<uint32_t*>(w), st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  uint32_t flags = 0;
+  if (e == hipSuccess) e = hipMemcpy(&flags, w, sizeof(flags), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return launch_status(e);
+  if (flags == 0) return DSA_OK;
+  g_last_arg_flags = flags;
+  return DSA_ERR_DEVICE_ARGS;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+uint32_t dsa_last_device_arg_flags(void) { return g_last_arg_flags; }
+
+dsa_status dsa_check_device_args(const dsa_batch* batch, const int32_t* idx, int32_t k, int64_t cache_rows,
+                                 uint32_t* flags, void* stream) {
+  dsa_status s = check_batch(batch);
+  if (s != DSA_OK) return s;
+  if (!flags) return DSA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) != 0) return DSA_ERR_ALIGN;
+  if (idx != nullptr && (k < 1 || k > DSA_MAX_TOPK)) return DSA_ERR_SHAPE;
+  if (cache_rows < 0) return DSA_ERR_SHAPE;
+  if ((s = check_device()) != DSA_OK) return s;
+  (void)hipGetLastError();
+  return launch_status(dsa::launch_argcheck(to_launch(batch, 0, batch->num_queries), batch->num_seqs, cache_rows,
+                                            idx, idx ? k : 0, flags, (hipStream_t)stream));
+}
 
 int32_t dsa_last_hip_error(void) { return g_last_hip_error; }
 
@@ -187,6 +252,7 @@ const char* dsa_status_string(int32_t s) {
     case DSA_ERR_UNSUPPORTED: return "unsupported option";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
     case DSA_ERR_DEVICE: return "no gfx950 HIP device is current";
+    case DSA_ERR_DEVICE_ARGS: return "a device-side argument violates its precondition (DSA_CHECK_DEVICE_ARGS)";
     default: return "unknown status";
   }
 }
@@ -245,6 +311,7 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const dsa_bf16* q_idx, const
   if ((s = check_scores(batch, scores, ld_scores)) != DSA_OK) return s;
   if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx)) return DSA_ERR_ALIGN;
   if ((s = check_device()) != DSA_OK) return s;
+  if ((s = debug_check(batch, nullptr, 0, (hipStream_t)stream)) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_index_scores(to_launch(batch, 0, batch->num_queries), q_idx, w,
                                                 k_idx, scores, ld_scores, use_gemm(batch), nullptr,
@@ -265,6 +332,7 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
       return DSA_ERR_WORKSPACE;
   }
   if ((s = check_device()) != DSA_OK) return s;
+  if ((s = debug_check(batch, nullptr, 0, (hipStream_t)stream)) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_topk(to_launch(batch, 0, batch->num_queries), scores,
                                         ld_scores, k, idx, ws, false, nullptr,
@@ -291,6 +359,7 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const dsa_bf16* q_nope,
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   if (ws_bytes < plan.total) return DSA_ERR_WORKSPACE;
   if ((s = check_device()) != DSA_OK) return s;
+  if ((s = debug_check(batch, idx, k, (hipStream_t)stream)) != DSA_OK) return s;
   (void)hipGetLastError();
   return launch_status(dsa::launch_sparse_mla(to_launch(batch, 0, batch->num_queries), plan,
                                               q_nope, q_rope, kv, w_uk, w_uv, idx, softmax_scale,
@@ -362,6 +431,7 @@ dsa_status forward_impl(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa
   while (tc > 1 && !fits(tc)) tc = (tc + 1) / 2;
   if (!fits(tc)) return DSA_ERR_WORKSPACE;
   if ((s = check_device()) != DSA_OK) return s;
+  if ((s = debug_check(batch, nullptr, 0, (hipStream_t)stream)) != DSA_OK) return s;
   (void)hipGetLastError();
   hipStream_t st = (hipStream_t)stream;
   const int64_t ld = score_ld(batch->max_ctx);

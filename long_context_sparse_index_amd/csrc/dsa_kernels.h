@@ -30,6 +30,10 @@ struct LaunchBatch {
 // INT4 latent cache: quantise `rows` bf16 cache rows into 400-byte rows.
 hipError_t launch_quantize_kv_int4(const uint16_t* kv, int64_t rows, uint8_t* out, hipStream_t st);
 
+// Device-side argument check (DSA_ARG_* bits into *flags, cleared first).
+hipError_t launch_argcheck(const LaunchBatch& b, int num_seqs, int64_t cache_rows, const int32_t* idx, int k,
+                           uint32_t* flags, hipStream_t st);
+
 // Indexer scores.  gemm=true: tiled GEMM over blocks of consecutive queries;
 // else the per-query key scan, which also writes the split top-k's slice bin
 // lists into topk_ws when that is not null.

@@ -68,6 +68,8 @@ _SIGS = {
                              ctypes.c_float, _P, ctypes.c_int32, _P, _P], ctypes.c_int),
     "dsa_index_share_schedule": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P], ctypes.c_int),
     "dsa_quantize_kv_int4": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int),
+    "dsa_check_device_args": ([ctypes.POINTER(_CBatch), _P, ctypes.c_int32, ctypes.c_int64, _P, _P], ctypes.c_int),
+    "dsa_last_device_arg_flags": ([], ctypes.c_uint32),
     "dsa_workspace_bytes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], ctypes.c_size_t),
     "dsa_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "dsa_abi_version": ([], ctypes.c_int32),
@@ -95,10 +97,16 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+ERR_DEVICE_ARGS = 8
+ARG_Q_SEQ, ARG_Q_POS, ARG_CACHE_ROW, ARG_IDX = 1, 2, 4, 8
+
+
 def _check(fn: str, status: int) -> None:
     if status != 0:
         L = lib()
-        raise DsaError(fn, status, L.dsa_status_string(status).decode(), L.dsa_last_hip_error())
+        err = DsaError(fn, status, L.dsa_status_string(status).decode(), L.dsa_last_hip_error())
+        err.arg_flags = int(L.dsa_last_device_arg_flags()) if status == ERR_DEVICE_ARGS else 0
+        raise err
 
 
 def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
@@ -395,3 +403,21 @@ def dsa_forward_noalloc(batch: Batch, q_idx, w, k_idx, q_nope, q_rope, kv, w_uk,
                                      _ptr(q_rope), _ptr(kv), _ptr(w_uk), _ptr(w_uv), k, softmax_scale,
                                      _ptr(out), od, _ptr(idx), _stream()))
     return out, idx
+
+
+def dsa_check_device_args(batch: Batch, idx: Optional[torch.Tensor] = None, cache_rows: int = 0,
+                          flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device-side argument check: a 1-element int32 device tensor holding the
+    ARG_* bits of every violated device-side precondition (0 when all hold)."""
+    if idx is not None:
+        if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int32 or idx.dim() != 2 \
+                or idx.shape[0] != batch.T or not idx.is_cuda or not idx.is_contiguous():
+            raise ValueError("idx: expected a contiguous [T, k] int32 device tensor")
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=batch.q_seq.device)
+    _int32_out(flags, "flags", (1,))
+    cb = batch.c()
+    _check("dsa_check_device_args",
+           lib().dsa_check_device_args(ctypes.byref(cb), _ptr(idx), 0 if idx is None else int(idx.shape[1]),
+                                       int(cache_rows), _ptr(flags), _stream()))
+    return flags

@@ -35,8 +35,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.dsa_abi_version() == 3
-    for s in range(8):
+    assert L.dsa_abi_version() == 4
+    for s in range(9):
         assert L.dsa_status_string(s)
     assert L.dsa_status_string(99) == b"unknown status"
 
@@ -191,3 +191,18 @@ def test_forward_noalloc_validation(L):
     assert L.dsa_workspace_bytes(dsa.OP_FORWARD, 1, 1 << 21, 8192) <= 64 << 20
     if not _gpu():
         assert f(ctypes.byref(b), *args, 2048, 0.0625, FAKE, 0, None, None) == 7
+
+
+def test_check_device_args_validation(L):
+    b = _batch()
+    f = L.dsa_check_device_args
+    assert f(None, None, 0, 0, FAKE, None) == 1
+    assert f(ctypes.byref(b), None, 0, 0, None, None) == 1          # flags NULL
+    assert f(ctypes.byref(b), None, 0, 0, FAKE + 2, None) == 3      # flags misaligned
+    assert f(ctypes.byref(b), FAKE, 0, 0, FAKE, None) == 2          # idx given, k 0
+    assert f(ctypes.byref(b), FAKE, 8193, 0, FAKE, None) == 2
+    assert f(ctypes.byref(b), None, 0, -1, FAKE, None) == 2         # cache_rows < 0
+    if not _gpu():
+        assert f(ctypes.byref(b), FAKE, 16, 1000, FAKE, None) == 7
+    assert L.dsa_last_device_arg_flags() == 0
+    assert L.dsa_status_string(8).startswith(b"a device-side argument")
