@@ -102,6 +102,26 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(stop) / steps  # ms
 
 
+def time_each(fn, steps, warmup, flush=None):
+    """Per-step HIP-event times (ms) on the current stream: median, p10, p90.
+    With `flush` (a device tensor of 512 MB or more), it is overwritten before
+    every step, outside the timed region, so that no input stays in the 256 MB
+    MALL or in L2 from the previous step."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        if flush is not None:
+            flush.fill_(1.0)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.sort(np.asarray([a.elapsed_time(b) for a, b in ev]))
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)), "p90": float(np.percentile(t, 90))}
+
+
 def paged_copy(inp, d, page_size, seed=4096):
     """The workload's caches scattered over a device page pool (seeded page
     permutation, 3 spare pages): every sequence length must be a multiple of
@@ -125,7 +145,7 @@ def paged_copy(inp, d, page_size, seed=4096):
     return table, pools[0], pools[1]
 
 
-def run_workload(name, steps, warmup, with_ops=True, extra_k=(), page_size=0):
+def run_workload(name, steps, warmup, with_ops=True, extra_k=(), page_size=0, dist=False):
     log(f"[bench] {name}: generating inputs")
     t0 = time.time()
     inp = synth.make_inputs(synth.workload(name))
@@ -144,8 +164,17 @@ def run_workload(name, steps, warmup, with_ops=True, extra_k=(), page_size=0):
     log(f"[bench] {name}: timing {steps} steps after {warmup} warmup")
     torch.cuda.synchronize()
     ms = time_calls(step, steps, warmup)
-    # index_topk as a runtime parameter: the same resident inputs with larger k
     by_k = {}
+    if dist:
+        # per-step distribution, inputs resident; then with a 512 MB write before
+        # every step (nothing of the previous step left in the MALL)
+        by_k["dist"] = time_each(step, steps, 2)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        by_k["flushed"] = time_each(step, steps, 2, flush=flush)
+        del flush
+        log(f"[bench] {name}: per step median {by_k['dist']['median']:.3f} ms; with a 512 MB MALL flush "
+            f"between steps {by_k['flushed']['median']:.3f} ms")
+    # index_topk as a runtime parameter: the same resident inputs with larger k
     for k in extra_k:
         idx_k = torch.empty((T, k), dtype=torch.int32, device="cuda")
         ws_k = torch.empty(dsa.dsa_workspace_bytes(dsa.OP_FORWARD, T, batch.max_ctx, k), dtype=torch.uint8,
@@ -185,6 +214,8 @@ def run_workload(name, steps, warmup, with_ops=True, extra_k=(), page_size=0):
         torch.cuda.empty_cache()
     if not with_ops:
         log(f"[bench] {name}: {ms:.3f} ms/step")
+        del ws, out, idx
+        torch.cuda.empty_cache()
         return inp, ms, {}, by_k
     # per-op breakdown: each ABI call below launches that op's kernels only
     scores = torch.empty((T, dsa.score_ld(batch.max_ctx)), dtype=torch.float32, device="cuda")
@@ -274,6 +305,51 @@ def cpu_baseline(inp, budget_s):
                       f"full-sort top-2048, explicit MLA), {el:.1f}s wall"}
 
 
+def cpu_baseline_prefill(inp, budget_s):
+    """The oracle on a bounded sample of the prefill chunk's queries (each: indexer
+    over its whole history, full-sort top-2048, explicit MLA), in query-tokens/s."""
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    T = len(inp.q_pos)
+    done = 0
+    t0 = time.time()
+    while done < 2 or time.time() - t0 < budget_s:  # queries spread over the chunk
+        O.query_forward(inp, (done * 997) % T, k=TOPK)
+        done += 1
+    el = time.time() - t0
+    log(f"[bench] cpu oracle (prefill): {done} queries in {el:.1f}s")
+    return {"value": done / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of the 4,096 queries of {PREFILL} (every 997th, cyclic; each: indexer over "
+                      f"its 200K+ history, full-sort top-2048, explicit MLA), {el:.1f}s wall"}
+
+
+OTHER_CONFIGS = (
+    # (workload, kind): the other configurations of the benchmark table, each one dsa_forward per step
+    ("decode_b32_ctx32k", "decode"),
+    ("prefill_chunk4096_ctx131k", "prefill"),
+    ("causal_prefill_65k_planted", "prefill"),
+)
+
+
+def other_config(name, kind, steps, warmup):
+    inp, ms, _, _ = run_workload(name, steps, warmup, with_ops=False)
+    alg = algorithmic(inp)
+    T = len(inp.q_pos)
+    r = {"workload": name, "queries": T, "ctx": int(max(inp.wl.seq_lens)), "ms_per_step": ms,
+         "value": T / (ms * 1e-3), "unit": "decode queries/s" if kind == "decode" else "query-tokens/s"}
+    if kind == "decode":
+        r["hbm_frac"] = alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+        r["algorithmic_bytes"] = alg["bytes"]
+    else:
+        r["mfma_frac"] = alg["flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        r["algorithmic_flops"] = alg["flops"]
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,12 +362,18 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling aid: run only the prefill chunk (prints no result line)")
     ap.add_argument("--no-ops", action="store_true", help="profiling aid: skip the per-op timing loops")
+    ap.add_argument("--only", default="",
+                    help="profiling aid: comma-separated workloads whose forward alone is run (prints no result "
+                         "line), e.g. decode_b32_ctx32k,prefill_chunk4096_ctx204k")
     ap.add_argument("--decode-only", action="store_true",
                     help="profiling aid: run only the decode workload (prints no result line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="profiling aid: run a plain 1 GiB device-to-device copy 3 times and exit "
                          "(reference for HBM byte counters)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work per workload, decode and prefill (0 = skip)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the 32K decode batch, the 131K prefill chunk and the full 65K causal prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding "
@@ -309,6 +391,11 @@ def main():
         log("[bench] copied 1 GiB 3 times")
         return
     dsa.lib()
+    if args.only:
+        for name in args.only.split(","):
+            run_workload(name, args.steps, args.warmup, not args.no_ops)
+            torch.cuda.empty_cache()
+        return
     extra_k = () if args.no_topk_variants else (4096, 8192)
     if args.decode_only:
         run_workload(DECODE, args.steps, args.warmup, not args.no_ops, extra_k)
@@ -317,9 +404,12 @@ def main():
         run_workload(PREFILL, args.steps, args.warmup, not args.no_ops, extra_k[-1:])
         return
 
-    inp, ms, ops, dec_k = run_workload(DECODE, args.steps, args.warmup, extra_k=extra_k, page_size=PAGE)
+    inp, ms, ops, dec_k = run_workload(DECODE, args.steps, args.warmup, extra_k=extra_k, page_size=PAGE,
+                                       dist=True)
     dec_paged = dec_k.pop("paged")
     dec_int4 = dec_k.pop("int4")
+    dec_dist = dec_k.pop("dist")
+    dec_flushed = dec_k.pop("flushed")
     alg = algorithmic(inp)
     T = len(inp.q_pos)
     scan_ms = ops["index_scores"]
@@ -345,6 +435,10 @@ def main():
                      "algorithmic_bytes": alg["scan_bytes"]},
         "whole_step": {"algorithmic_bytes": alg["bytes"],
                        "hbm_frac": alg["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "step_ms": {"resident": dec_dist,
+                    "mall_flushed": dict(dec_flushed, note="512 MB written before every step, outside the "
+                                                           "timed region"),
+                    "flushed_value": T / (dec_flushed["median"] * 1e-3)},
         "ops_ms": ops,
         "index_topk_variants": {str(k): {"ms_per_step": v, "value": T / (v * 1e-3), "unit": "decode queries/s"}
                                 for k, v in dec_k.items()},
@@ -360,7 +454,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     del inp
     if not args.no_prefill:
-        pinp, pms, pops, pre_k = run_workload(PREFILL, max(3, args.steps // 5), min(args.warmup, 3),
+        pinp, pms, pops, pre_k = run_workload(PREFILL, max(10, args.steps // 2), max(3, min(args.warmup, 5)),
                                               extra_k=extra_k[-1:], page_size=PAGE)
         pre_paged = pre_k.pop("paged")
         pre_int4 = pre_k.pop("int4")
@@ -378,9 +472,15 @@ def main():
             "mfma_frac_whole_step": palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "idx_gemm_kernel", "achieved": pach,
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pach / MFMA_BF16_PEAK_TFLOPS,
-                         "traffic": None},
+                         "traffic": recorded_traffic("idx_gemm_kernel_hbm_traffic_prefill_chunk4096_ctx204k.json"),
+                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+                         "algorithmic_flops": palg["index_flops"]},
         }
+        if args.cpu_budget > 0:
+            result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pinp, args.cpu_budget)
         del pinp
+    if not args.no_other_configs:
+        result["other_configs"] = [other_config(n, kind, max(5, args.steps // 4), 2) for n, kind in OTHER_CONFIGS]
     print(json.dumps(result), flush=True)
 
 

@@ -102,6 +102,15 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     if (ntiles > 1) pid_fetch(1, pa);
   }
   gload(0, pb);
+  // The query operands and head weights arrive here (their loads were issued
+  // before tile 0's, which stay in flight).  Left to itself the compiler sinks
+  // these loads to the loop entry and then, in every iteration, waits for the
+  // loads issued since (the next tile's keys) before the first MFMA: the key
+  // latency would sit on the compute path of every tile.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(qa[j]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[r]));
   lstore(0);
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -118,16 +127,20 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     for (int r = 0; r < 16; ++r) part = fmaf(wr[r], relu(acc[r]), part);
     const float tot = part + xor_lane(part, 32);
     const int s = k0 + tile * kScanTile + wave * 32 + n;
+    if (tile + 1 < ntiles) lstore(buf ^ 1);
+    // The score store follows the wait for the next tile's keys, and the
+    // barrier waits for LDS only: no step waits for a store's completion (the
+    // next step's wait for its keys covers this older store long after it
+    // has completed).
     if (g == 0 && s <= pos) {
       srow[s] = tot;
       if (lists) hist16_add(hist, score_key(tot));
     }
-    if (tile + 1 < ntiles) lstore(buf ^ 1);
     if (PAGED) {
 #pragma unroll
       for (int c = 0; c < kGr; ++c) pa[c] = pb[c];
     }
-    __syncthreads();
+    lds_sync();
   }
   if (lists)
     write_bin_list<256>(hist,
