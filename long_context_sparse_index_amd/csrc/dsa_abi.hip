@@ -2,6 +2,7 @@
 // chunking and kernel launches on the caller's stream.  No allocation, no
 // host synchronisation, nothing enqueued when a check fails.
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -104,12 +105,39 @@ bool use_gemm(const dsa_batch* b) {
   return b->num_queries >= 8 && (int64_t)b->num_queries >= 8 * (int64_t)b->num_seqs;
 }
 
-// Workspace of dsa_forward for a chunk of T queries.
-struct FwdPlan {
-  size_t scores_off, idx_off, topk_off, mla_off, total;
-  dsa::MlaPlan mla;
+// Candidate path of the prefill forward (page-4 §2.2: the selector keeps the
+// index_topk best of the query's history; see topk.hip): every kCandStride-th
+// position is scored first, and the indexer GEMM then keeps only the scores at
+// or above a per-query threshold taken from that sample.  The threshold's
+// sample rank puts about `target` of a row's scores above it, where target and
+// the list capacity `cap` lie five sampling deviations (sqrt(target *
+// kCandStride)) above k and below cap; rows outside [k, cap] take the full path.
+constexpr int kCandStride = 128;
+struct CandPlan {
+  int64_t target;
+  int cap;
+  int64_t ld_s;  // sample-score row stride
 };
-FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
+CandPlan cand_plan(int32_t k, int32_t max_ctx) {
+  const double R = kCandStride;
+  const double x = (5.0 * std::sqrt(R) + std::sqrt(25.0 * R + 4.0 * k)) / 2.0;
+  const double target = std::ceil(x * x);
+  const double cap = target + 5.0 * std::sqrt(target * R);
+  CandPlan c;
+  c.target = (int64_t)target;
+  c.cap = (int)((cap + 1023.0) / 1024.0) * 1024;
+  c.ld_s = ((int64_t)(max_ctx - 1) / kCandStride + 1 + 3) / 4 * 4;
+  return c;
+}
+
+// Workspace of dsa_forward for a chunk of T queries.  `cand`: the chunk takes
+// the candidate path (its extra arrays follow the MLA workspace).
+struct FwdPlan {
+  size_t scores_off, idx_off, topk_off, mla_off, sample_off, theta_off, cnt_off, flags_off, cand_off, total;
+  dsa::MlaPlan mla;
+  CandPlan cp;
+};
+FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx, bool cand) {
   FwdPlan f{};
   f.scores_off = 0;
   size_t end = align256((size_t)T * score_ld(max_ctx) * sizeof(float));
@@ -119,8 +147,28 @@ FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx) {
   end += align256(dsa::topk_workspace_bytes(T, max_ctx));
   f.mla_off = end;
   f.mla = dsa::plan_mla(T, k);
-  f.total = end + f.mla.total;
+  end += f.mla.total;
+  if (cand) {
+    f.cp = cand_plan(k, max_ctx);
+    f.sample_off = end;
+    end += align256((size_t)T * f.cp.ld_s * sizeof(float));
+    f.theta_off = end;
+    end += align256((size_t)T * sizeof(float));
+    f.cnt_off = end;
+    end += align256((size_t)T * sizeof(int32_t));
+    f.flags_off = end;
+    end += align256((size_t)T * sizeof(int32_t));
+    f.cand_off = end;
+    end += align256((size_t)T * f.cp.cap * 2 * sizeof(uint32_t));
+  }
+  f.total = end;
   return f;
+}
+
+// The chunk of T queries takes the candidate path: indexer GEMM with one
+// workgroup per query block over the whole context, contiguous caches.
+bool use_candidates(const dsa_batch* b, int32_t T, bool gemm) {
+  return gemm && b->page_size == 0 && dsa::gemm_whole_context(T, b->max_ctx);
 }
 
 // The whole path over one workspace: query chunks sized to ws_bytes.
@@ -267,7 +315,8 @@ size_t dsa_workspace_bytes(int32_t op, int32_t num_queries, int32_t max_ctx, int
       return dsa::plan_mla(num_queries, k).total;
     case DSA_OP_FORWARD:
       if (k < 1 || k > DSA_MAX_TOPK) return 0;
-      return plan_forward(num_queries, max_ctx, k, true).total;
+      // (the candidate path's arrays whenever such a chunk could take it)
+      return plan_forward(num_queries, max_ctx, k, true, dsa::gemm_whole_context(num_queries, max_ctx)).total;
     default: return 0;
   }
 }
@@ -386,7 +435,7 @@ dsa_status dsa_forward_noalloc(const dsa_batch* batch, const dsa_bf16* q_idx, co
   if (batch->num_queries == 0) return DSA_OK;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
   // One query must fit the scratch (the workspace of larger batches is chunked).
-  if (plan_forward(1, batch->max_ctx, k, idx_out == nullptr).total > kNoAllocScratchBytes)
+  if (plan_forward(1, batch->max_ctx, k, idx_out == nullptr, false).total > kNoAllocScratchBytes)
     return DSA_ERR_WORKSPACE;
   if ((s = check_device()) != DSA_OK) return s;
   void* ws = nullptr;
@@ -420,12 +469,16 @@ dsa_status forward_impl(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa
   if (!ws) return DSA_ERR_NULL;
   if (!aligned16(ws)) return DSA_ERR_ALIGN;
   const bool need_idx = idx_out == nullptr;
+  const bool gemm = use_gemm(batch);
+  auto plan = [&](int32_t c) {
+    return plan_forward(c, batch->max_ctx, k, need_idx, use_candidates(batch, c, gemm));
+  };
   // Largest chunk (by halving) for which both the full chunks and the last,
   // shorter one fit (a short chunk may use more key splits per query).
   auto fits = [&](int32_t c) {
-    if (plan_forward(c, batch->max_ctx, k, need_idx).total > ws_bytes) return false;
+    if (plan(c).total > ws_bytes) return false;
     const int32_t rem = T % c;
-    return rem == 0 || plan_forward(rem, batch->max_ctx, k, need_idx).total <= ws_bytes;
+    return rem == 0 || plan(rem).total <= ws_bytes;
   };
   int32_t tc = T;
   while (tc > 1 && !fits(tc)) tc = (tc + 1) / 2;
@@ -435,29 +488,53 @@ dsa_status forward_impl(const dsa_batch* batch, const dsa_bf16* q_idx, const dsa
   (void)hipGetLastError();
   hipStream_t st = (hipStream_t)stream;
   const int64_t ld = score_ld(batch->max_ctx);
-  const bool gemm = use_gemm(batch);
   char* base = static_cast<char*>(ws);
   const size_t out_elem = out_dtype == DSA_OUT_F32 ? sizeof(float) : sizeof(uint16_t);
   for (int32_t t0 = 0; t0 < T; t0 += tc) {
     const int32_t n = T - t0 < tc ? T - t0 : tc;
-    const FwdPlan p = plan_forward(n, batch->max_ctx, k, need_idx);
+    const bool cand = use_candidates(batch, n, gemm);
+    const FwdPlan p = plan(n);
     const dsa::LaunchBatch lb = to_launch(batch, t0, n);
     float* scores = reinterpret_cast<float*>(base + p.scores_off);
     int32_t* idx = need_idx ? reinterpret_cast<int32_t*>(base + p.idx_off) : idx_out + (int64_t)t0 * k;
+    const dsa_bf16* q_idx_c = q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM;
+    const dsa_bf16* w_c = w + (int64_t)t0 * DSA_INDEX_HEADS;
     // The key scan writes the split top-k's slice lists as it goes.
     void* topk_ws = base + p.topk_off;
     const bool fused_lists = !gemm && dsa::topk_split(n, topk_ws);
-    hipError_t e = dsa::launch_index_scores(lb, q_idx + (int64_t)t0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
-                                            w + (int64_t)t0 * DSA_INDEX_HEADS, k_idx, scores, ld,
-                                            gemm, fused_lists ? topk_ws : nullptr, st);
     // With the split top-k, the query absorption runs on the finish kernel's
     // spare workgroups instead of its own launch.
     const dsa_bf16* q_nope_c = q_nope + (int64_t)t0 * DSA_HEADS * DSA_QK_NOPE_DIM;
     const bool ride = dsa::topk_split(n, topk_ws);
     const dsa::AbsorbJob job{q_nope_c, w_uk,
                              reinterpret_cast<uint16_t*>(base + p.mla_off + p.mla.q_lat_off)};
-    if (e == hipSuccess)
-      e = dsa::launch_topk(lb, scores, ld, k, idx, topk_ws, fused_lists, ride ? &job : nullptr, st);
+    hipError_t e;
+    if (cand) {
+      // sampled scores -> thresholds -> candidates -> exact top-k; flagged rows
+      // take the full path (key scan and row top-k on those rows only)
+      float* sample = reinterpret_cast<float*>(base + p.sample_off);
+      float* theta = reinterpret_cast<float*>(base + p.theta_off);
+      int32_t* cnt = reinterpret_cast<int32_t*>(base + p.cnt_off);
+      int32_t* flags = reinterpret_cast<int32_t*>(base + p.flags_off);
+      uint32_t* cl = reinterpret_cast<uint32_t*>(base + p.cand_off);
+      e = dsa::launch_index_sample(lb, q_idx_c, w_c, k_idx, sample, p.cp.ld_s, kCandStride, st);
+      if (e == hipSuccess)
+        e = dsa::launch_topk_candidates(lb, sample, p.cp.ld_s, kCandStride, p.cp.target, p.cp.cap, theta,
+                                        nullptr, nullptr, k, nullptr, nullptr, st, true);
+      if (e == hipSuccess)
+        e = dsa::launch_index_candidates(lb, q_idx_c, w_c, k_idx, theta, cl, p.cp.cap, cnt, st);
+      if (e == hipSuccess)
+        e = dsa::launch_topk_candidates(lb, sample, p.cp.ld_s, kCandStride, p.cp.target, p.cp.cap, theta, cl,
+                                        cnt, k, idx, flags, st, false);
+      if (e == hipSuccess)
+        e = dsa::launch_index_scores(lb, q_idx_c, w_c, k_idx, scores, ld, false, nullptr, st, flags);
+      if (e == hipSuccess) e = dsa::launch_topk(lb, scores, ld, k, idx, nullptr, false, nullptr, st, flags);
+    } else {
+      e = dsa::launch_index_scores(lb, q_idx_c, w_c, k_idx, scores, ld, gemm, fused_lists ? topk_ws : nullptr,
+                                   st);
+      if (e == hipSuccess)
+        e = dsa::launch_topk(lb, scores, ld, k, idx, topk_ws, fused_lists, ride ? &job : nullptr, st);
+    }
     if (e == hipSuccess)
       e = dsa::launch_sparse_mla(lb, p.mla, q_nope_c,
                                  q_rope + (int64_t)t0 * DSA_HEADS * DSA_QK_ROPE_DIM, kv, w_uk,

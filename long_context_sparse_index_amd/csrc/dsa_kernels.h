@@ -39,7 +39,21 @@ hipError_t launch_argcheck(const LaunchBatch& b, int num_seqs, int64_t cache_row
 // lists into topk_ws when that is not null.
 hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
-                               void* topk_ws, hipStream_t st);
+                               void* topk_ws, hipStream_t st, const int32_t* row_mask = nullptr);
+// True when the indexer GEMM gives each query block one workgroup over the
+// whole context (the condition of the candidate path below).
+bool gemm_whole_context(int T, int max_ctx);
+// Scores of the sampled positions 0, stride, 2 stride, ... <= q_pos[t] into
+// sample[t * ld_s + i] (GEMM path, contiguous caches).
+hipError_t launch_index_sample(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                               const uint16_t* k_idx, float* sample, int64_t ld_s, int stride, hipStream_t st);
+// Indexer GEMM that keeps, per query t, the (monotone key, position) of every
+// score >= theta[t] in position order in cand[t * cap ..] (u32 pairs; entries
+// past cap counted but not written), the count in cnt[t].  Needs
+// gemm_whole_context(T, max_ctx).
+hipError_t launch_index_candidates(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                                   const uint16_t* k_idx, const float* theta, uint32_t* cand, int cap, int* cnt,
+                                   hipStream_t st);
 
 // Top-k selection.  Batches of few rows use a split path that needs
 // topk_workspace_bytes(T, max_ctx) of workspace; with ws == nullptr every row
@@ -55,7 +69,14 @@ struct AbsorbJob {
   uint16_t* q_lat;
 };
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st);
+                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st,
+                       const int32_t* row_mask = nullptr);
+// Candidate path (see topk.hip): threshold_only -> theta[t] from the sampled
+// scores; else the exact top-k of each row's candidates, flags[t] = 1 for rows
+// that must take the full path (row_mask of the key scan and launch_topk).
+hipError_t launch_topk_candidates(const LaunchBatch& b, const float* sample, int64_t ld_s, int stride,
+                                  int64_t target, int cap, float* theta, const uint32_t* cand, const int32_t* cnt,
+                                  int k, int32_t* idx, int32_t* flags, hipStream_t st, bool threshold_only);
 
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {

@@ -38,11 +38,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int slice_keys,
-    char* __restrict__ lists, SplitWs sw) {
+    char* __restrict__ lists, SplitWs sw, const int32_t* __restrict__ row_mask) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kScanTile * kScanLds];
   __shared__ uint32_t hist[kTkBins / 2];
   __shared__ int wave_tot[4];
   const int t = blockIdx.x;
+  if (row_mask != nullptr && row_mask[t] == 0) return;  // only the rows a mask names
   const int pos = q_pos[t];
   const int k0 = blockIdx.y * slice_keys;
   if (k0 > pos) return;
@@ -194,11 +195,34 @@ inline int gemm_split_keys(int T, int max_ctx) {
 constexpr int kGemmLoads = kGemmKT * kIdxDim * 2 / (kGemmThreads * 16);  // direct loads per thread per tile
 constexpr int kDlStride = 4 * kGemmWaves;  // key rows between a thread's successive direct loads
 
-template <bool PAGED>
+// What the GEMM produces (MODE):
+//   kGemmScores      every score s <= q_pos into scores[t*ld + s];
+//   kGemmSample      the scores of positions 0, R, 2R, ... <= q_pos (R = o.stride)
+//                    into scores[t*ld + i] for position R*i;
+//   kGemmCandidates  no score matrix: each query appends (monotone key, position)
+//                    of every score >= theta[t] (s <= q_pos), in position order,
+//                    to its list cand[t*cap ..] (entries past cap are counted, not
+//                    written) and writes the count to cnt[t].  Needs one
+//                    workgroup per query block over the whole context.
+enum { kGemmScores = 0, kGemmSample = 1, kGemmCandidates = 2 };
+struct GemmOut {
+  float* scores;        // scores / sample scores
+  int64_t ld;
+  int stride;           // kGemmSample: positions per sample
+  const float* theta;   // kGemmCandidates: per query threshold
+  uint32_t* cand;       // kGemmCandidates: [T][cap][2] u32 (key, position)
+  int cap;
+  int* cnt;             // kGemmCandidates: [T]
+};
+
+template <bool PAGED, int MODE>
 __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int T, int split_keys) {
+    const uint16_t* __restrict__ k_idx, GemmOut o, int T, int split_keys) {
+  static_assert(!(PAGED && MODE == kGemmSample), "sampled keys are read from contiguous caches");
+  float* const scores = o.scores;
+  const int64_t ld = o.ld;
   // two buffers as two arrays: with distinct objects the compiler sees that
   // direct loads into one do not alias reads of the other, and does not make
   // those reads wait for the loads
@@ -212,7 +236,8 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
   if (tid < kGemmQB) {
     const int t = t0 + tid;
     s_seq[tid] = t < T ? q_seq[t] : -1;
-    s_pos[tid] = t < T ? q_pos[t] : -1;
+    // kGemmSample works in sample indices: sample i is position stride * i
+    s_pos[tid] = t < T ? (MODE == kGemmSample ? q_pos[t] / o.stride : q_pos[t]) : -1;
   }
   __syncthreads();
   const int split0 = blockIdx.y * split_keys;
@@ -243,6 +268,19 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
   int frag_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) frag_off[j] = n * kIdxDim + (((2 * j + g) ^ (n & 15)) << 3);
+  // kGemmCandidates: per query of the wave, its threshold and list length so far
+  // (wave-uniform; a query belongs to one sequence, so one pass below appends)
+  float th[kGemmQPW];
+  int ncand[kGemmQPW];
+#pragma unroll
+  for (int qi = 0; qi < kGemmQPW; ++qi) {
+    th[qi] = 0.f;
+    ncand[qi] = 0;
+    if constexpr (MODE == kGemmCandidates) {
+      const int tq = t0 + wave * kGemmQPW + qi;
+      th[qi] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(o.theta[min(tq, T - 1)])));
+    }
+  }
 
   for (int i = 0; i < kGemmQB; ++i) {
     const int sq = s_seq[i];
@@ -274,7 +312,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
 #pragma unroll
       for (int c = 0; c < kGemmLoads; ++c) {
         const int key = min(base + kDlStride * c + dl_row, hi);  // rows past hi: never stored
-        int64_t row = row0 + key;
+        int64_t row = row0 + (MODE == kGemmSample ? (int64_t)key * o.stride : (int64_t)key);
         if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (key & ((1 << cr.page_shift) - 1));
         // (named pointers: the host pass rejects cast expressions as this builtin's operands)
         const uint16_t* const gsrc = k_idx + row * kIdxDim + dl_chunk * 8;
@@ -287,16 +325,20 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     // Stores past its end are dropped by the hardware, so the epilogue stores
     // without a branch.
     __amdgpu_buffer_rsrc_t rs[kGemmQPW];
+    int qlim[kGemmQPW];  // kGemmCandidates: last position the query keeps (-1: another sequence)
 #pragma unroll
     for (int qi = 0; qi < kGemmQPW; ++qi) {
       const int local = wave * kGemmQPW + qi;
       const int lim = __builtin_amdgcn_readfirstlane(s_seq[local] == sq ? s_pos[local] : -1);
-      const int nrec = min(max(lim + 1 - kbeg, 0), split_keys) * 4;
-      const uint64_t srow = reinterpret_cast<uint64_t>(scores + (int64_t)(t0 + local) * ld + kbeg);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)srow);
-      const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(srow >> 32));
-      float* const base = reinterpret_cast<float*>(((uint64_t)hi32 << 32) | lo);
-      rs[qi] = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(nrec), kBufferWord3);
+      qlim[qi] = lim;
+      if constexpr (MODE != kGemmCandidates) {
+        const int nrec = min(max(lim + 1 - kbeg, 0), split_keys) * 4;
+        const uint64_t srow = reinterpret_cast<uint64_t>(scores + (int64_t)(t0 + local) * ld + kbeg);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)srow);
+        const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(srow >> 32));
+        float* const base = reinterpret_cast<float*>(((uint64_t)hi32 << 32) | lo);
+        rs[qi] = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(nrec), kBufferWord3);
+      }
     }
     auto chain = [&](int qi, const bf16x8 b[8]) {
       f32x16 acc = {};
@@ -319,7 +361,25 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     auto store_pair = [&](int qi, float pa, float pb, int kb) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
       const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // a(l) + a(l + 32) | b(l - 32) + b(l)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[qi], 4 * (kb + lane), 0, 0);
+      if constexpr (MODE == kGemmCandidates) {
+        // keep key kbeg + kb + lane if it is causal for the query and at least
+        // the threshold; the kept lanes append in lane (= position) order
+        const int pos = kbeg + kb + lane;
+        const bool keep = pos <= qlim[qi] && tot >= th[qi];
+        const uint64_t m = __ballot(keep);
+        if (m != 0) {
+          const int before =
+              (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          const int at = ncand[qi] + before;
+          if (keep && at < o.cap) {
+            uint32_t* const dst = o.cand + ((int64_t)(t0 + wave * kGemmQPW + qi) * o.cap + at) * 2;
+            *reinterpret_cast<u32x2*>(dst) = u32x2{score_key(tot), (uint32_t)pos};
+          }
+          ncand[qi] += __builtin_popcountll(m);
+        }
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[qi], 4 * (kb + lane), 0, 0);
+      }
     };
     auto frags = [&](const uint16_t* buf, int grp, int nt, bf16x8 b[8]) {
       const uint16_t* base = buf + (64 * grp + 32 * nt) * kIdxDim;
@@ -377,31 +437,74 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     }
     store_pair(1, pend_p, reduce(1, pend), pend_k);
   }
+  if constexpr (MODE == kGemmCandidates) {
+#pragma unroll
+    for (int qi = 0; qi < kGemmQPW; ++qi) {
+      const int tq = t0 + wave * kGemmQPW + qi;
+      if (lane == 0 && tq < T) o.cnt[tq] = ncand[qi];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
-                               void* topk_ws, hipStream_t st) {
+                               void* topk_ws, hipStream_t st, const int32_t* row_mask) {
   if (gemm) {
     const int split_keys = gemm_split_keys(b.T, b.max_ctx);
     dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (int)(((int64_t)b.max_ctx + split_keys - 1) / split_keys));
+    GemmOut o{};
+    o.scores = scores;
+    o.ld = ld;
     if (b.paged())
-      idx_gemm_kernel<true><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
-                                                           scores, ld, b.T, split_keys);
+      idx_gemm_kernel<true, kGemmScores><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                                        o, b.T, split_keys);
     else
-      idx_gemm_kernel<false><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
-                                                            scores, ld, b.T, split_keys);
+      idx_gemm_kernel<false, kGemmScores><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
+                                                                         o, b.T, split_keys);
   } else {
     const SplitWs sw = split_ws(b.T, b.max_ctx);
     char* lists = static_cast<char*>(topk_ws);
     if (b.paged())
       idx_scan_kernel<true><<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
-                                                             scores, ld, sw.slice_keys, lists, sw);
+                                                             scores, ld, sw.slice_keys, lists, sw, row_mask);
     else
       idx_scan_kernel<false><<<dim3(b.T, sw.S), 256, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx,
-                                                              scores, ld, sw.slice_keys, lists, sw);
+                                                              scores, ld, sw.slice_keys, lists, sw, row_mask);
   }
+  return hipGetLastError();
+}
+
+bool gemm_whole_context(int T, int max_ctx) { return gemm_split_keys(T, max_ctx) >= max_ctx; }
+
+hipError_t launch_index_sample(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                               const uint16_t* k_idx, float* sample, int64_t ld_s, int stride, hipStream_t st) {
+  const int n_s = (b.max_ctx - 1) / stride + 1;  // samples of the longest row
+  const int split_keys = gemm_split_keys(b.T, n_s);
+  dim3 grid((b.T + kGemmQB - 1) / kGemmQB, (n_s + split_keys - 1) / split_keys);
+  GemmOut o{};
+  o.scores = sample;
+  o.ld = ld_s;
+  o.stride = stride;
+  idx_gemm_kernel<false, kGemmSample><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx, o,
+                                                                     b.T, split_keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_candidates(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
+                                   const uint16_t* k_idx, const float* theta, uint32_t* cand, int cap, int* cnt,
+                                   hipStream_t st) {
+  const int split_keys = gemm_split_keys(b.T, b.max_ctx);
+  if (split_keys < b.max_ctx) return hipErrorInvalidValue;  // needs whole-context workgroups
+  dim3 grid((b.T + kGemmQB - 1) / kGemmQB, 1);
+  GemmOut o{};
+  o.theta = theta;
+  o.cand = cand;
+  o.cap = cap;
+  o.cnt = cnt;
+  if (b.paged()) return hipErrorInvalidValue;  // the candidate path runs on contiguous caches
+  idx_gemm_kernel<false, kGemmCandidates><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w,
+                                                                          k_idx, o, b.T, split_keys);
   return hipGetLastError();
 }
 

@@ -549,9 +549,11 @@ template <int KMAX>
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const int32_t* __restrict__ q_pos,
                                                               const float* __restrict__ scores,
                                                               int64_t ld, int k,
-                                                              int32_t* __restrict__ idx) {
+                                                              int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ row_mask) {
   __shared__ TkShared<KMAX> sh;
   const int t = blockIdx.x, tid = threadIdx.x;
+  if (row_mask != nullptr && row_mask[t] == 0) return;  // only the rows a mask names
   const int n = q_pos[t] + 1;
   int32_t* out = idx + (int64_t)t * k;
   if (n <= k) {
@@ -929,13 +931,14 @@ size_t topk_workspace_bytes(int T, int max_ctx) {
 }
 
 hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, int k, int32_t* idx,
-                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st) {
+                       void* ws, bool lists_ready, const AbsorbJob* absorb, hipStream_t st,
+                       const int32_t* row_mask) {
   const bool small = k <= kTopkSmall;
-  if (!topk_split(b.T, ws)) {
+  if (!topk_split(b.T, ws) || row_mask != nullptr) {
     if (small)
-      topk_row_kernel<kTopkSmall><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
+      topk_row_kernel<kTopkSmall><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, row_mask);
     else
-      topk_row_kernel<kMaxTopk><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx);
+      topk_row_kernel<kMaxTopk><<<b.T, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, row_mask);
     return hipGetLastError();
   }
   const SplitWs w = split_ws(b.T, b.max_ctx);
@@ -949,6 +952,191 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
     topk_finish_kernel<kTopkSmall><<<grid, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w, b.T, ab);
   else
     topk_finish_kernel<kMaxTopk><<<grid, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w, b.T, ab);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- candidate path
+// For prefill chunks whose indexer GEMM keeps candidates instead of scores:
+//   1. the GEMM scores a sample of each row, positions 0, R, 2R, ...;
+//   2. topk_sample_threshold_kernel: per row of n > cap scores, theta = the
+//      r-th largest sampled score with r = ceil(E * n_s / n), so that about E
+//      of the row's scores lie at or above theta (E and cap are chosen on the
+//      host, five sampling deviations from k and from cap); rows of n <= cap
+//      keep every score (theta = -inf);
+//   3. the GEMM keeps the scores >= theta as (key, position) in position order;
+//   4. topk_cand_kernel selects the top k among them exactly (radix select as
+//      above) when the row has between k and cap candidates and its threshold
+//      bin fits in LDS.  Every score of the row's top k is then a candidate (at
+//      least k scores are >= theta, so the k-th largest is too), so the result
+//      equals the full path's.  Rows where this does not hold are flagged and
+//      take the full path (scores by the key scan, then topk_row_kernel, both
+//      limited to the flagged rows).
+constexpr int kThrThreads = 256;
+
+__global__ __launch_bounds__(kThrThreads) void topk_sample_threshold_kernel(
+    const int32_t* __restrict__ q_pos, const float* __restrict__ sample, int64_t ld_s, int stride,
+    int64_t target, int cap, float* __restrict__ theta) {
+  __shared__ uint32_t hist[kTkBins];
+  __shared__ int wave_tot[kThrThreads / 64];
+  __shared__ int sel_bin, sel_above;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int pos = q_pos[t];
+  const int n = pos + 1;
+  if (n <= cap) {
+    if (tid == 0) theta[t] = -INFINITY;
+    return;
+  }
+  const int ns = pos / stride + 1;
+  const int r = (int)min((int64_t)ns, max((int64_t)1, (target * ns + n - 1) / n));
+  const float* row = sample + (int64_t)t * ld_s;
+  // Radix select of the r-th largest sampled key: 12 + 12 + 8 bits; the
+  // sampled scores are re-read from L2 on each pass.
+  uint32_t prefix = 0;
+  int krem = r;
+  constexpr int shift[3] = {20, 8, 0};
+  constexpr int nbins[3] = {kTkBins, kTkBins, 256};
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    for (int i = tid; i < kTkBins; i += kThrThreads) hist[i] = 0u;
+    __syncthreads();
+    const int sh = shift[p];
+    const uint32_t hi_mask = p == 0 ? 0u : (0xFFFFFFFFu << (sh + (p == 1 ? 12 : 8)));
+    for (int i = tid; i < ns; i += kThrThreads) {
+      const uint32_t key = score_key(row[i]);
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> sh) & (nbins[p] - 1)], 1u);
+    }
+    __syncthreads();
+    if (p < 2)
+      find_bin<kThrThreads, kTkBins>(hist, krem, wave_tot, &sel_bin, &sel_above);
+    else
+      find_bin<kThrThreads, 256>(hist, krem, wave_tot, &sel_bin, &sel_above);
+    prefix |= (uint32_t)sel_bin << sh;
+    krem -= sel_above;
+    __syncthreads();
+  }
+  if (tid == 0) theta[t] = key_floor(prefix);  // score >= theta  <=>  key >= prefix
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kTkThreads) void topk_cand_kernel(
+    const int32_t* __restrict__ q_pos, const uint32_t* __restrict__ cand, int cap, const int32_t* __restrict__ cnt,
+    int k, int32_t* __restrict__ idx, int32_t* __restrict__ flags) {
+  __shared__ TkShared<KMAX> sh;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int n = q_pos[t] + 1;
+  int32_t* out = idx + (int64_t)t * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    if (tid == 0) flags[t] = 0;
+    return;
+  }
+  const int c = cnt[t];
+  if (c < k || c > cap) {  // the threshold missed: the row takes the full path
+    if (tid == 0) flags[t] = 1;
+    return;
+  }
+  const u32x2* cd = reinterpret_cast<const u32x2*>(cand) + (int64_t)t * cap;
+  constexpr int kB = 8;  // candidates per thread per round of the histogram pass
+  for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < c; b0 += kB * kTkThreads) {
+    uint32_t key[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = b0 + tid + u * kTkThreads;
+      key[u] = j < c ? cd[j].x : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (b0 + tid + u * kTkThreads < c) atomicAdd(&sh.hist[key[u] >> 20], 1u);
+  }
+  __syncthreads();
+  find_bin<kTkBins>(sh, k);
+  const uint32_t b1 = (uint32_t)sh.sel_bin;
+  int above = sh.sel_above;
+  int cin = (int)sh.hist[b1];
+  __syncthreads();
+  // The candidates to resolve in LDS share a key prefix: the top digit b1, or,
+  // when that bin holds more than fit, b1 and the next 12 bits (a second
+  // histogram over the candidates of bin b1).  Keys with a larger prefix are
+  // kept outright (list A).
+  uint32_t prefix = b1;
+  int pshift = 20;
+  if (cin > kCandCap) {
+    for (int i = tid; i < kTkBins; i += kTkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int b0 = 0; b0 < c; b0 += kB * kTkThreads) {
+      uint32_t key[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int j = b0 + tid + u * kTkThreads;
+        key[u] = j < c ? cd[j].x : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (b0 + tid + u * kTkThreads < c && (key[u] >> 20) == b1) atomicAdd(&sh.hist[(key[u] >> 8) & 0xFFFu], 1u);
+    }
+    __syncthreads();
+    find_bin<kTkBins>(sh, k - above);
+    prefix = (b1 << 12) | (uint32_t)sh.sel_bin;
+    pshift = 8;
+    above += sh.sel_above;
+    cin = (int)sh.hist[sh.sel_bin];
+    __syncthreads();
+    if (cin > kCandCap) {  // more equal 20-bit prefixes than fit: the full path handles the row
+      if (tid == 0) flags[t] = 1;
+      return;
+    }
+  }
+  // ordered compaction: thread tid takes candidates [base + kPerThread tid, +kPerThread)
+  int nA = 0, nC = 0;
+  for (int base = 0; base < c; base += kStep) {
+    const int j0 = base + kPerThread * tid;
+    u32x2 v[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) v[e] = j0 + e < c ? cd[j0 + e] : u32x2{0u, 0u};
+    int ca = 0, cc = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const uint32_t d = v[e].x >> pshift;
+      ca += j0 + e < c && d > prefix;
+      cc += j0 + e < c && d == prefix;
+    }
+    int tot;
+    const int ex = block_excl_scan<kTkWaves>((ca << 16) | cc, sh.wave_tot, tot);
+    int oa = nA + (ex >> 16), oc = nC + (ex & 0xFFFF);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (j0 + e >= c) continue;
+      const uint32_t d = v[e].x >> pshift;
+      if (d > prefix) {
+        sh.list_a[oa++] = (int)v[e].y;
+      } else if (d == prefix) {
+        sh.cand_key[oc] = v[e].x;
+        sh.cand_pos[oc] = (int)v[e].y;
+        ++oc;
+      }
+    }
+    nA += tot >> 16;
+    nC += tot & 0xFFFF;
+  }
+  __syncthreads();
+  // (the LDS candidates all have top digit b1; their lower digits are resolved there)
+  finish_from_candidates(sh, b1, above, cin, k - above, out);
+  if (tid == 0) flags[t] = 0;
+}
+
+hipError_t launch_topk_candidates(const LaunchBatch& b, const float* sample, int64_t ld_s, int stride,
+                                  int64_t target, int cap, float* theta, const uint32_t* cand, const int32_t* cnt,
+                                  int k, int32_t* idx, int32_t* flags, hipStream_t st, bool threshold_only) {
+  if (threshold_only) {
+    topk_sample_threshold_kernel<<<b.T, kThrThreads, 0, st>>>(b.q_pos, sample, ld_s, stride, target, cap, theta);
+    return hipGetLastError();
+  }
+  if (k <= kTopkSmall)
+    topk_cand_kernel<kTopkSmall><<<b.T, kTkThreads, 0, st>>>(b.q_pos, cand, cap, cnt, k, idx, flags);
+  else
+    topk_cand_kernel<kMaxTopk><<<b.T, kTkThreads, 0, st>>>(b.q_pos, cand, cap, cnt, k, idx, flags);
   return hipGetLastError();
 }
 
