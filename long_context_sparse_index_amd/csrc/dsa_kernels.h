@@ -40,8 +40,9 @@ hipError_t launch_argcheck(const LaunchBatch& b, int num_seqs, int64_t cache_row
 hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* scores, int64_t ld, bool gemm,
                                void* topk_ws, hipStream_t st, const int32_t* row_mask = nullptr);
-// True when the indexer GEMM gives each query block one workgroup over the
-// whole context (the condition of the candidate path below).
+// True when the query blocks alone fill the chip and the indexer GEMM gives
+// each one workgroup over the whole context (the condition of the candidate
+// path below).
 bool gemm_whole_context(int T, int max_ctx);
 // Scores of the sampled positions 0, stride, 2 stride, ... <= q_pos[t] into
 // sample[t * ld_s + i] (GEMM path, contiguous caches).

@@ -475,7 +475,10 @@ hipError_t launch_index_scores(const LaunchBatch& b, const uint16_t* q_idx, cons
   return hipGetLastError();
 }
 
-bool gemm_whole_context(int T, int max_ctx) { return gemm_split_keys(T, max_ctx) >= max_ctx; }
+bool gemm_whole_context(int T, int max_ctx) {
+  // (query blocks alone fill the chip: one workgroup per block over the whole context)
+  return (T + kGemmQB - 1) / kGemmQB >= kGemmMinWgs && gemm_split_keys(T, max_ctx) >= max_ctx;
+}
 
 hipError_t launch_index_sample(const LaunchBatch& b, const uint16_t* q_idx, const uint16_t* w,
                                const uint16_t* k_idx, float* sample, int64_t ld_s, int stride, hipStream_t st) {
