@@ -48,15 +48,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Two fp32 -> packed fp16 (lo in bits 0..15, round toward zero) and back.
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-__device__ __forceinline__ float f16_lo(uint32_t v) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
-}
-__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
-
 // Two fp32 -> packed bf16 (lo in bits 0..15), one hardware conversion
 // (round to nearest even).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

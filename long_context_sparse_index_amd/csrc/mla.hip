@@ -65,7 +65,7 @@ constexpr int kCoreThreads = 512;
 constexpr int kRing = 3;
 constexpr int kPLds = kKT + 8;       // bf16 per P^T row (one head)
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold, log2 units
-constexpr int kPartSlab = kHeads * kLat;  // fp16 values of one split partial
+constexpr int kPartSlab = kHeads * kLat;  // bf16 values of one split partial
 constexpr int kAbsent = 1 << 30;          // flag of an absent position in the contiguous core's index list
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kSlots + ((c & ~7) | ((c ^ r) & 7)); }
@@ -466,15 +466,15 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
                   pack_bf16x2(o[e][j][2] * inv, o[e][j][3] * inv)};
     } else {
       // Partials are normalised by the split's own sum (a convex combination of
-      // cache rows, so fp16 holds them to 2^-11) and keep the accumulator order
-      // (see mla_merge_kernel): each store instruction writes 512 B of
-      // consecutive memory.
+      // cache rows, held in bf16: the latent's own type and range, rounded to
+      // nearest even) and keep the accumulator order (see mla_merge_kernel):
+      // each store instruction writes 512 B of consecutive memory.
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = o_part + ((int64_t)t * S + sp) * kPartSlab + ((wave * 4 + j) * 4) * 256 + lane * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         *reinterpret_cast<u32x2*>(dst + e * 256) =
-            u32x2{pack_f16x2(o[e][j][0] * inv, o[e][j][1] * inv), pack_f16x2(o[e][j][2] * inv, o[e][j][3] * inv)};
+            u32x2{cvt_pk_bf16(o[e][j][0] * inv, o[e][j][1] * inv), cvt_pk_bf16(o[e][j][2] * inv, o[e][j][3] * inv)};
       if (wave == 0 && g == 0) {
         const int64_t base = ((int64_t)t * S + sp) * kHeads + h;
         ml_part[base * 2] = s_m[h];
@@ -485,13 +485,22 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 }
 
 // ---------------------------------------------------------------- merge
-// Split partials of (query t, split s) form one slab of kHeads * kLat fp16
+// Split partials of (query t, split s) form one slab of kHeads * kLat bf16
 // values, each normalised by its split's sum l, in the core's accumulator
 // order: element i of the 4-value group number ((w * 4 + j) * 4 + e) * 64 +
 // lane is latent dim 64w + 16e + 4(lane / 16) + i of head 16j + lane % 16.
 // ml_part[t][s][h] = (reference max m, sum l).  grid (T, 32): workgroup
 // (t, 4w + j) combines latent dims 64w .. 64w+63 of heads 16j .. 16j+15, one
 // group of every split per thread, weighting split s by 2^(m_s - max m) l_s.
+// CH: splits whose (m, l) pairs and partials are all requested before any is
+// used (one memory latency per chunk; the launch takes the smallest of 8, 16,
+// 32 that holds the splits, or 32-split chunks).  A later chunk with a larger
+// maximum rescales what is summed so far (with one chunk this is the plain
+// two-pass sum).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+template <int CH>
 __global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restrict__ o_part,
                                                         const float* __restrict__ ml_part, int S,
                                                         uint16_t* __restrict__ o_lat) {
@@ -500,26 +509,20 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restri
   const int h = 16 * j + (lane & 15), g = lane >> 4;
   const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
   const uint16_t* src = o_part + (int64_t)t * S * kPartSlab + (((w * 4 + j) * 4 + jj) * 64 + lane) * 4;
-  // Splits in chunks of kMergeChunk whose (m, l) pairs and partials are all
-  // requested before any is used (one memory latency per chunk).  Past S a
-  // slot repeats split S - 1 with weight 0.  A later chunk with a larger
-  // maximum rescales what is summed so far (with at most one chunk this is
-  // the plain two-pass sum).
-  constexpr int kMergeChunk = 32;
   float mstar = -1e30f, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
-    f32x2 m_l[kMergeChunk];
-    u32x2 v[kMergeChunk];
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    f32x2 m_l[CH];
+    u32x2 v[CH];
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
-      const int s = min(s0 + u, S - 1);
+    for (int u = 0; u < CH; ++u) {
+      const int s = min(s0 + u, S - 1);  // past S: split S - 1 again, weight 0
       m_l[u] = *reinterpret_cast<const f32x2*>(ml + (int64_t)s * kHeads * 2);
       v[u] = *reinterpret_cast<const u32x2*>(src + (int64_t)s * kPartSlab);
     }
     float cm = mstar;
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) cm = s0 + u < S ? fmaxf(cm, m_l[u][0]) : cm;
+    for (int u = 0; u < CH; ++u) cm = s0 + u < S ? fmaxf(cm, m_l[u][0]) : cm;
     if (cm > mstar) {
       const float sc = exp2f(mstar - cm);
       L *= sc;
@@ -527,10 +530,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const uint16_t* __restri
       mstar = cm;
     }
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < CH; ++u) {
       const float wgt = s0 + u < S ? exp2f(m_l[u][0] - mstar) * m_l[u][1] : 0.f;
       L += wgt;
-      acc += wgt * f32x4{f16_lo(v[u].x), f16_hi(v[u].x), f16_lo(v[u].y), f16_hi(v[u].y)};
+      acc += wgt * f32x4{bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y)};
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -859,7 +862,12 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
-    mla_merge_kernel<<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+    if (p.splits <= 8)
+      mla_merge_kernel<8><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+    else if (p.splits <= 16)
+      mla_merge_kernel<16><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+    else
+      mla_merge_kernel<32><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

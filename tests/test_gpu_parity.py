@@ -429,3 +429,25 @@ def test_forward_full_size(name, k):
          f"{ndiff} near-tie positions over {len(sample)} queries; out max-abs {worst_mx:.2e} "
          f"rel-L2 {worst_rel:.2e}")
     assert worst_mx <= OUT_MAX_ABS and worst_rel <= OUT_REL_L2
+
+
+def test_sparse_mla_large_latent_over_key_splits():
+    """Latent rows near 1e5 (beyond the fp16 range) through the key-split path
+    (few queries: several splits and their merge): the split partials keep the
+    latent's range, and the output matches the oracle to the relative bar."""
+    _say("[sparse_mla] large latent, key splits")
+    inp = synth.custom([3000, 2500], [(0, 2999), (1, 2400)], seed=47)
+    lat = synth.bf16_to_f32(inp.kv[:, :512]) * np.float32(1e5)
+    inp.kv = inp.kv.copy()
+    inp.kv[:, :512] = synth.bf16_rne(lat)
+    k = 2048
+    idx = np.stack([O.topk_select(_oracle_scores(inp, t), k) for t in range(2)])
+    d = to_device(inp)
+    out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv,
+                                  torch.from_numpy(idx).cuda(), out_dtype=torch.float32).cpu().numpy()
+    assert np.isfinite(out).all()
+    for t in range(2):
+        ref = _oracle_out(inp, t, idx[t])
+        mx, rel = out_errors(out[t], ref)
+        _say(f"  t={t} max-abs {mx:.3e} (max |ref| {np.abs(ref).max():.3e}) rel-L2 {rel:.2e}")
+        assert rel <= OUT_REL_L2 and mx <= OUT_MAX_ABS * np.abs(ref).max()
