@@ -82,6 +82,9 @@ hipError_t launch_topk_candidates(const LaunchBatch& b, const float* sample, int
 // Sparse MLA: workspace layout and launches.
 struct MlaPlan {
   int T, k, splits, keys_per_split;
+  // few queries with a bf16 cache: the decode core's key splits
+  bool dec;
+  int dec_splits, dec_keys_per_split;
   size_t q_lat_off, o_lat_off, part_off, ml_off, wuvt_off, total;
 };
 MlaPlan plan_mla(int T, int k);

@@ -119,6 +119,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// s_waitcnt vmcnt(n) for n < 64 (the count's upper two bits sit in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vm_wide() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 template <bool PAGED, bool Q4>
 __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr,
@@ -484,6 +491,335 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   }
 }
 
+// ---------------------------------------------------------------- decode core
+// Few queries (decode): grid of (query, group of 16 heads, key split)
+// workgroups of 4 waves, one per SIMD.  Each wave runs its own online softmax
+// over its share of the split's keys (16-key tiles u = wave, wave + 4, ...),
+// gathering each tile by direct-to-LDS loads into its own 2-slot ring, so the
+// tile loop has no workgroup barrier:
+//   QK   logits^T[16 keys][16 heads] = c_tile . q^T, 18 16x16x32 MFMAs with the
+//        group's q (576 = 512 latent + 64 rope) resident as the B operand; lane
+//        (g, l16) gets keys 4g .. 4g+3 of head l16, which is the B operand
+//        layout of a 16x16x16 MFMA over those keys, so P stays in registers;
+//   PV   o^T[512 dims][16 heads] += c_tile^T . P^T, 32 16x16x16 MFMAs whose
+//        latent operand (4 keys of one dim per lane) comes from the row-major
+//        tile by the transposing LDS read.
+// The four waves' (max, sum, o) meet in LDS at the end.  Against the
+// all-heads core this reads every gathered row four times (once per head
+// group; the four workgroups of a (query, split) get block ids equal modulo 8,
+// which places them on one XCD and its L2) but writes a key split's partial
+// for 16 heads only, and a workgroup covers 4x the keys: the split partials,
+// which are as large as 64 gathered rows, shrink fourfold.
+constexpr int kDecHeads = 16;
+constexpr int kDecWaves = 4;
+constexpr int kDecKT = 16;                          // keys per wave tile
+constexpr int kDecLoads = kDecKT + 2;               // gather loads per tile (16 latent rows, 2 of rope)
+constexpr int kDecPadTiles = 3 * kDecWaves;         // absent tiles past a split's last (see the loop)
+constexpr int kDecMaxKps = 1024;                    // keys per split
+constexpr int kDecTMax = 16;                        // batches up to this size
+constexpr int kDecLatStride = kLat / 8 + 2;          // 66 slots per latent row (2 of padding)
+constexpr int kDecRopeSlot0 = kDecKT * kDecLatStride;  // 1056: the rope area after 16 latent rows
+constexpr int kDecTileSlots = kDecRopeSlot0 + kDecKT * (kRope / 8);  // 1184 slots of 16 B
+
+// Wave tile layout (16 rows): the latent parts of the rows first, one 66-slot
+// row each (logical chunk c of row r at r*66 + (c ^ (r / 8)): the XOR only
+// swaps neighbouring chunks, so a lane's successive chunks stay at constant
+// distances and its LDS reads share one address register), then the rope
+// parts, 8 slots each (chunk c of row r at 1056 + r*8 + (c ^ (r / 2))).  The
+// QK row reads (16 rows, one chunk) and the PV transposing reads (8 rows, two
+// chunks per half wave) are both free of bank conflicts.
+__device__ __forceinline__ int dec_lat_slot(int r, int c) { return r * kDecLatStride + (c ^ (r >> 3)); }
+__device__ __forceinline__ int dec_rope_slot(int r, int c) { return kDecRopeSlot0 + r * 8 + (c ^ (r >> 1)); }
+
+__device__ __forceinline__ f32x4 mfma16k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_decode_kernel(
+    const int32_t* __restrict__ q_seq, CacheRows cr, const uint16_t* __restrict__ q_lat,
+    const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    int T, int k, float scale_log2, int kps, int S, uint16_t* __restrict__ o_lat,
+    uint16_t* __restrict__ o_part, float* __restrict__ ml_part) {
+  // Two distinct slot arrays (not one indexed array): the compiler then waits
+  // only for the direct-to-LDS loads that target the array being read.
+  __shared__ __attribute__((aligned(16))) uint16_t slot0[kDecWaves][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot1[kDecWaves][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) int s_idx[kDecMaxKps + kDecPadTiles * kDecKT];
+  __shared__ float s_ml[kDecWaves][kDecHeads][2];
+  // block id -> (query, split) pair P and head group: ids 32a + 8hg + r hold
+  // pair 8a + r, so the four head groups of a pair are equal modulo 8
+  const int id = blockIdx.x;
+  const int P = (id >> 5) * 8 + (id & 7);
+  const int hg = (id >> 3) & 3;
+  if (P >= T * S) return;  // (whole workgroup)
+  const int t = P / S, sp = P - t * S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int j0 = sp * kps;
+  const int j1 = min(k, j0 + kps);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kDecKT - 1) / kDecKT : 0;
+  const int ntw = ntiles > wave ? (ntiles - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's tiles
+  const int seq = q_seq[t];
+  const uint16_t* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kRow;
+  const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
+  const int32_t* irow = idx + (int64_t)t * k;
+  // The split's positions (as in mla_core_kernel: contiguous entries are
+  // positions, an absent one position 0 with kAbsent set; paged entries are
+  // pool rows, an absent one ~row of position 0), padded to whole tiles.
+  {
+    constexpr int kPer = (kDecMaxKps + kDecPadTiles * kDecKT + kDecWaves * 64 - 1) / (kDecWaves * 64);
+    const int nfill = (ntiles + kDecPadTiles) * kDecKT;
+    int v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kDecWaves * 64;
+      const int e = irow[min(j0 + j, k - 1)];
+      v[u] = j0 + j < j1 ? e : -1;
+      if (!PAGED) v[u] = v[u] >= 0 ? v[u] : kAbsent;
+    }
+    if (PAGED) {
+      int pg[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) pg[u] = bt[max(v[u], 0) >> cr.page_shift];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int row = (pg[u] << cr.page_shift) | (max(v[u], 0) & ((1 << cr.page_shift) - 1));
+        v[u] = v[u] >= 0 ? row : ~row;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = tid + u * kDecWaves * 64;
+      if (j < nfill) s_idx[j] = v[u];
+    }
+  }
+  // q operand of QK: lane (g, l16) holds dims 32ks + 8g .. +7 of head 16hg + l16
+  const int hq = kDecHeads * hg + l16;
+  bf16x8 qb[18];
+  {
+    const uint16_t* ql = q_lat + ((int64_t)t * kHeads + hq) * kLat + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(ld16(ql + 32 * ks));
+    const uint16_t* qr = q_rope + ((int64_t)t * kHeads + hq) * kRope + 8 * g;
+    qb[16] = as_bf16x8(ld16(qr));
+    qb[17] = as_bf16x8(ld16(qr + 32));
+  }
+  __syncthreads();
+
+  // Gather of a 16-row tile into a wave's slot: loads 0-15 bring the 1 KB
+  // latent part of row i (lane L fetches logical chunk L ^ (i / 8) into
+  // physical slot L of the row; the row's position is wave-uniform, so the
+  // only per-lane operand is that chunk offset), loads 16 and 17 the rope
+  // parts of all 16 rows (physical slot p of the rope area: row p / 8,
+  // logical chunk (p % 8) ^ (row / 2)).
+  const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
+  const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
+  const uint32_t kv_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kv_a >> 32));
+  const uint16_t* const kv_u = reinterpret_cast<const uint16_t*>(((uint64_t)kv_hi << 32) | kv_lo);
+  const __amdgpu_buffer_rsrc_t kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv_u), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+  const uint32_t voff_lo = (uint32_t)lane * 16u, voff_hi = (uint32_t)(lane ^ 1) * 16u;  // rows 0-7, 8-15
+  const int rope_r0 = lane >> 3;  // row of this lane's chunk in rope load 16 (load 17: + 8)
+  const uint32_t rope_colb = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ (rope_r0 >> 1)) * 16);
+  const uint32_t rope_colb1 = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ ((rope_r0 + 8) >> 1)) * 16);
+  // Returns the tile's mask of present rows (bit r for row r).
+  auto gather = [&](int v, uint16_t* dstt) __attribute__((always_inline)) -> uint32_t {  // this wave's tile v
+    const int u = wave + kDecWaves * v;
+    // lane l: entry of row l % 16.  (Read in asm with its own wait: the
+    // compiler cannot tell s_idx from the gathers' LDS targets and would wait
+    // for every gather in flight before a plain read.)
+    int pv;
+    {
+      const __attribute__((address_space(3))) int* const a =
+          (const __attribute__((address_space(3))) int*)(&s_idx[u * kDecKT + l16]);
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(pv) : "v"(a) : "memory");
+    }
+    const bool present = PAGED ? pv >= 0 : (pv & kAbsent) == 0;
+    const uint32_t pmask = (uint32_t)__ballot(present) & 0xFFFFu;
+    const int pr0 = __shfl(pv, rope_r0, 64), pr1 = __shfl(pv, rope_r0 + 8, 64);
+#pragma unroll
+    for (int i = 0; i < kDecKT; ++i) {
+      uint16_t* const dst = dstt + i * kDecLatStride * 8;
+      const int e = __builtin_amdgcn_readlane(pv, i);
+      const uint32_t voff = i < 8 ? voff_lo : voff_hi;
+      if (PAGED) {
+        const int r = e >= 0 ? e : ~e;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kv_u + (int64_t)r * kRow), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+      } else {
+        // (bit 30 of an absent entry drops out of the 24-bit position)
+        const int soff = (e & 0xFFFFFF) * (kRow * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dst, 16, voff, soff, 0, 0);
+      }
+    }
+    uint16_t* const dr0 = dstt + kDecRopeSlot0 * 8;
+    uint16_t* const dr1 = dstt + (kDecRopeSlot0 + 64) * 8;
+    if (PAGED) {
+      const int r0 = pr0 >= 0 ? pr0 : ~pr0, r1 = pr1 >= 0 ? pr1 : ~pr1;
+      const uint16_t* const g0 = kv_u + (int64_t)r0 * kRow + rope_colb / 2;
+      const uint16_t* const g1 = kv_u + (int64_t)r1 * kRow + rope_colb1 / 2;
+      __builtin_amdgcn_global_load_lds(g0, dr0, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g1, dr1, 16, 0, 0);
+    } else {
+      const uint32_t o0 = (uint32_t)(pr0 & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
+      const uint32_t o1 = (uint32_t)(pr1 & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dr0, 16, o0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dr1, 16, o1, 0, 0, 0);
+    }
+    return pmask;
+  };
+
+  // per-lane LDS offsets (bf16 elements) of chunk g of row l16 (QK) and of
+  // chunk (l16 % 4) / 2, half l16 % 2 of row 4g + l16 / 4 (PV)
+  const int qk_base = dec_lat_slot(l16, g) * 8;
+  const int pv_base = dec_lat_slot(4 * g + (l16 >> 2), (l16 & 3) >> 1) * 8 + 4 * (l16 & 1);
+
+  f32x4 o[32];  // o[b]: dims 16b + 4g .. +3 of head hq
+#pragma unroll
+  for (int b = 0; b < 32; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -1e30f, l_part = 0.f;
+
+  auto compute = [&](const uint16_t* tb, uint32_t pmask) __attribute__((always_inline)) {
+    // ---- QK: keys 4g .. 4g+3 of head hq (three chains); the latent chunks
+    // 4ks + g of row l16 lie 64 bytes apart
+    const uint16_t* const tb_qk = tb + qk_base;
+    f32x4 sc;
+    {
+      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks)
+        acc[ks % 3] = mfma16(
+            as_bf16x8(*reinterpret_cast<const u32x4*>(
+                ks < 16 ? tb_qk + 32 * ks : tb + dec_rope_slot(l16, 4 * (ks - 16) + g) * 8)),
+            qb[ks], acc[ks % 3]);
+      sc = acc[0] + acc[1] + acc[2];
+    }
+    const uint32_t pm = pmask >> (4 * g);  // keys 4g .. 4g+3
+    float z[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = fmaf(sc[i], scale_log2, (pm >> i) & 1u ? 0.f : -INFINITY);
+      tmax = fmaxf(tmax, z[i]);
+    }
+    tmax = fmaxf(tmax, xor_lane(tmax, 16));
+    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    // lazy reference maximum (see mla_core_kernel); v_exp_f32 directly
+    const float m_new = tmax > m_ref + kRescaleLog2 ? tmax : m_ref;
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int b = 0; b < 32; ++b) o[b] *= alpha;
+    }
+    float p[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+      ps += p[i];
+    }
+    l_part = l_part * alpha + ps;
+    const v4i16 pb = __builtin_bit_cast(v4i16, u32x2{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])});
+    // ---- PV: source lane s of group g reads key 4g + s/4, dims 16b + 4(s%4) .. +3
+    const uint16_t* const tb_pv = tb + pv_base;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      const uint16_t* const a = tb_pv + 16 * b;  // (chunks 2b + j lie 32 bytes apart)
+      const v4i16 fa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+      o[b] = mfma16k16(fa, pb, o[b]);
+    }
+  };
+
+  uint16_t* const my0 = slot0[wave];
+  uint16_t* const my1 = slot1[wave];
+  // Step v computes tile v from slot v % 2 once this wave's loads of it are
+  // in (its loads of tile v + 1 may still be in flight), then gathers tile
+  // v + 2 into that slot once the wave's reads of it are complete.  The loop
+  // body has no branch (the compiler then keeps track of which slot a wait is
+  // for): a wave runs an even number of steps and gathers two tiles past its
+  // last; those tiles hold absent entries (position 0's row, masked), and an
+  // odd count's last step computes such a tile to no effect.
+  uint32_t pm0, pm1;  // present rows of the tiles in slot 0 and 1
+  auto step = [&](int v, auto BUFC) __attribute__((always_inline)) {
+    constexpr int buf = decltype(BUFC)::value;
+    uint32_t& pm = buf == 0 ? pm0 : pm1;
+    wait_vm_wide<kDecLoads>();
+    compute(buf == 0 ? my0 : my1, pm);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    pm = gather(v + 2, buf == 0 ? my0 : my1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int nsteps = (ntw + 1) & ~1;
+  pm0 = gather(0, my0);
+  pm1 = gather(1, my1);
+  // the query operand loads (issued before the gathers) are complete here;
+  // marking them consumed keeps the compiler from waiting for every gather
+  // before the loop
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
+  for (int v = 0; v < nsteps; v += 2) {
+    step(v, std::integral_constant<int, 0>{});
+    step(v + 1, std::integral_constant<int, 1>{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // (the two gathers past the last step)
+
+  // ---- the four waves' partial results: reference maxima and sums meet in
+  // LDS, then each wave adds up 8 latent blocks (128 dims) of all four
+  float l_sum = l_part + xor_lane(l_part, 16);
+  l_sum += xor_lane(l_sum, 32);
+  if (g == 0) {
+    s_ml[wave][l16][0] = m_ref;
+    s_ml[wave][l16][1] = l_sum;
+  }
+  __syncthreads();  // (also: every wave is done with its slots)
+  float mstar = -1e30f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) mstar = fmaxf(mstar, s_ml[w][l16][0]);
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) L += __builtin_amdgcn_exp2f(s_ml[w][l16][0] - mstar) * s_ml[w][l16][1];
+  const float wgt = __builtin_amdgcn_exp2f(m_ref - mstar);
+  // wave w's scaled o goes to [32 blocks][64 lanes] of f32x4 (32 KB): waves
+  // 0, 1 in slot0, waves 2, 3 in slot1
+  static_assert(sizeof(slot0) >= 2 * 32 * 64 * sizeof(f32x4), "reduction area");
+  auto red = [&](int w) __attribute__((always_inline)) -> f32x4* {
+    return reinterpret_cast<f32x4*>(w < 2 ? &slot0[0][0] : &slot1[0][0]) + (w & 1) * 32 * 64;
+  };
+  {
+    f32x4* const mine = red(wave);
+#pragma unroll
+    for (int b = 0; b < 32; ++b) mine[b * 64 + lane] = o[b] * wgt;
+  }
+  __syncthreads();
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const int b = 8 * wave + bb;
+    f32x4 sum = red(0)[b * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) sum += red(w)[b * 64 + lane];
+    sum *= inv;
+    if (S == 1) {
+      *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + hq) * kLat + 16 * b + 4 * g) =
+          u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+    } else {
+      // mla_merge_kernel's order: group ((w'*4 + head group)*4 + e)*64 + lane, b = 4w' + e
+      *reinterpret_cast<u32x2*>(o_part + ((int64_t)t * S + sp) * kPartSlab +
+                                ((((b >> 2) * 4 + hg) * 4 + (b & 3)) * 64 + lane) * 4) =
+          u32x2{cvt_pk_bf16(sum[0], sum[1]), cvt_pk_bf16(sum[2], sum[3])};
+    }
+  }
+  if (S > 1 && wave == 0 && g == 0) {
+    const int64_t base = ((int64_t)t * S + sp) * kHeads + hq;
+    ml_part[base * 2] = mstar;
+    ml_part[base * 2 + 1] = L;
+  }
+}
+
 // ---------------------------------------------------------------- merge
 // Split partials of (query t, split s) form one slab of kHeads * kLat bf16
 // values, each normalised by its split's sum l, in the core's accumulator
@@ -804,15 +1140,27 @@ MlaPlan plan_mla(int T, int k) {
   kps = (kps + kKT - 1) / kKT * kKT;
   p.keys_per_split = kps;
   p.splits = (k + kps - 1) / kps;
+  // Decode core: about 256 workgroups of (query, 16 heads, split), splits of
+  // whole 64-key rounds (16 keys per wave) and at most kDecMaxKps keys.
+  p.dec = T > 0 && T <= kDecTMax;
+  if (p.dec) {
+    const int s0 = (64 + T - 1) / T;
+    int dk = (k + s0 - 1) / s0;
+    dk = (dk + kDecKT * kDecWaves - 1) / (kDecKT * kDecWaves) * (kDecKT * kDecWaves);
+    dk = dk < kDecMaxKps ? dk : kDecMaxKps;
+    p.dec_keys_per_split = dk;
+    p.dec_splits = (k + dk - 1) / dk;
+  }
+  const int max_splits = p.dec && p.dec_splits > p.splits ? p.dec_splits : p.splits;
   const size_t lat = (size_t)T * kHeads * kLat * sizeof(uint16_t);
   p.q_lat_off = 0;
   p.o_lat_off = align_up(lat, 256);
   size_t end = p.o_lat_off + align_up(lat, 256);
-  if (p.splits > 1) {
+  if (max_splits > 1) {
     p.part_off = end;
-    end += align_up((size_t)T * p.splits * kHeads * kLat * sizeof(uint16_t), 256);
+    end += align_up((size_t)T * max_splits * kHeads * kLat * sizeof(uint16_t), 256);
     p.ml_off = end;
-    end += align_up((size_t)T * p.splits * kHeads * 2 * sizeof(float), 256);
+    end += align_up((size_t)T * max_splits * kHeads * 2 * sizeof(float), 256);
   }
   if (T >= kUpTMin) {
     p.wuvt_off = end;
@@ -827,10 +1175,12 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
                              const uint16_t* w_uv, const int32_t* idx, float scale, void* out,
                              int out_f32, void* ws, bool q_lat_ready, hipStream_t st) {
   char* base = static_cast<char*>(ws);
+  const bool dec = p.dec && !b.kv_int4;
+  const int S = dec ? p.dec_splits : p.splits;
   uint16_t* q_lat = reinterpret_cast<uint16_t*>(base + p.q_lat_off);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(base + p.o_lat_off);
-  uint16_t* o_part = p.splits > 1 ? reinterpret_cast<uint16_t*>(base + p.part_off) : nullptr;
-  float* ml_part = p.splits > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
+  uint16_t* o_part = S > 1 ? reinterpret_cast<uint16_t*>(base + p.part_off) : nullptr;
+  float* ml_part = S > 1 ? reinterpret_cast<float*>(base + p.ml_off) : nullptr;
   const int T = b.T;
   const int ntb = (T + 31) / 32;
   hipError_t e;
@@ -846,8 +1196,18 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(T, p.splits);
-  const int kps = p.keys_per_split, S = p.splits;
-  if (b.paged() && b.kv_int4)
+  const int kps = p.keys_per_split;
+  if (dec) {
+    const int dgrid = 32 * ((T * S + 7) / 8);
+    if (b.paged())
+      mla_decode_kernel<true><<<dgrid, kDecWaves * 64, 0, st>>>(
+          b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
+          p.dec_keys_per_split, S, o_lat, o_part, ml_part);
+    else
+      mla_decode_kernel<false><<<dgrid, kDecWaves * 64, 0, st>>>(
+          b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
+          p.dec_keys_per_split, S, o_lat, o_part, ml_part);
+  } else if (b.paged() && b.kv_int4)
     mla_core_kernel<true, true><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
                                                                scale_log2, kps, S, o_lat, o_part, ml_part);
   else if (b.paged())
@@ -861,13 +1221,13 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
                                                                  scale_log2, kps, S, o_lat, o_part, ml_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
-    if (p.splits <= 8)
-      mla_merge_kernel<8><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
-    else if (p.splits <= 16)
-      mla_merge_kernel<16><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+  if (S > 1) {
+    if (S <= 8)
+      mla_merge_kernel<8><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, S, o_lat);
+    else if (S <= 16)
+      mla_merge_kernel<16><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, S, o_lat);
     else
-      mla_merge_kernel<32><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, p.splits, o_lat);
+      mla_merge_kernel<32><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, S, o_lat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
