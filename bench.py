@@ -428,7 +428,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": DECODE, "sequences": 8, "ctx": 204800, "queries": T, "index_topk": TOPK},
-        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel",
+                     "launch": "dsa_index_scores: the forward's key scan without the slice lists, same grid",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": recorded_traffic("idx_scan_kernel_hbm_traffic_decode_b8_ctx204k.json"),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
@@ -470,7 +472,10 @@ def main():
             "kv_int4": {"ms_per_step": pre_int4, "value": len(pinp.q_pos) / (pre_int4 * 1e-3),
                         "unit": "query-tokens/s", "vs_bf16_cache": pms / pre_int4, "row_bytes": 400},
             "mfma_frac_whole_step": palg["flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "roofline": {"bound": "mfma", "kernel": "idx_gemm_kernel", "achieved": pach,
+            "roofline": {"bound": "mfma", "kernel": "idx_gemm_kernel",
+                         "launch": "dsa_index_scores: the indexer GEMM writing the score matrix (the forward runs "
+                                   "the same tile loop keeping candidates instead)",
+                         "achieved": pach,
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pach / MFMA_BF16_PEAK_TFLOPS,
                          "traffic": recorded_traffic("idx_gemm_kernel_hbm_traffic_prefill_chunk4096_ctx204k.json"),
                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
