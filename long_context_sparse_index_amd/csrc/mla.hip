@@ -820,6 +820,312 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ---------------------------------------------------------------- core, one split per query
+// Batches whose queries each take one key split (prefill chunks): one
+// workgroup per query, 8 waves in two roles, one per SIMD each:
+//   waves 0-3 (QK)  wave hg computes logits^T[32 keys][16 heads of group hg]
+//                   of tile i (36 16x16x32 MFMAs against its resident q), its
+//                   online softmax (a head's 32 keys are all in the wave: no
+//                   exchange), and writes P^T and the rescale factors of tile i;
+//   waves 4-7 (PV)  wave w accumulates o^T[128 latent dims of slice w][64
+//                   heads] for tile i - 1 (32 MFMAs), reading tile i - 1's P^T.
+// So every SIMD runs one wave's QK and softmax next to another's PV, and a
+// tile costs one barrier.  Tiles of 32 gathered rows use a 4-slot ring: tile
+// i + 2 is gathered during step i into the slot of tile i - 2 (QK'd two steps
+// ago, PV'd in the last one); each row is one direct-to-LDS load (its
+// position wave-uniform), the rope parts four more.  The positions come from
+// the index row in global memory one step before their gather.
+// Tile layout (38,912 B): latent row r at slots r*68 .. r*68+63, logical chunk
+// c at r*68 + (c ^ ((r >> 2) & 3)) (the XOR touches the chunk's two low bits
+// only, so a lane's successive QK chunks sit at constant distances, PV's at
+// constant distances per parity), slots r*68+64 .. +67 unused by the gather;
+// rope area at slot 2176, chunk c of row r at 2176 + r*8 + (c ^ ((r >> 1) & 7)).
+// QK row reads and PV transposing reads are free of bank conflicts.  P^T of
+// head h for tiles of parity b lives in the unused slots of row h % 32 of
+// ring slot 2b + h / 32 (chunk q of keys 8q..8q+7 at q ^ ((row >> 2) & 3));
+// P^T, the rescale factors and the key biases are read and written with
+// inline LDS instructions that wait for themselves, because the compiler
+// cannot tell those accesses from the pending gathers into the same arrays
+// and would otherwise wait for every gather in flight.
+constexpr int kWsLat = kLat / 8 + 4;                   // 68 slots per latent row
+constexpr int kWsRope0 = kKT * kWsLat;                 // 2176
+constexpr int kWsTileSlots = kWsRope0 + kKT * (kRope / 8);  // 2432 slots = 38,912 B
+constexpr int kWsNL = 5;                               // gather loads per tile of a QK wave (PV waves: 4)
+
+__device__ __forceinline__ int ws_lat_slot(int r, int c) { return r * kWsLat + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int ws_rope_slot(int r, int c) { return kWsRope0 + r * 8 + (c ^ ((r >> 1) & 7)); }
+// byte offset of P^T chunk q (keys 8q .. 8q+7) of head h, parity b, within
+// ring slot 2b + h / 32
+__device__ __forceinline__ int ws_pt_off(int h, int q) {
+  const int r = h & 31;
+  return (r * kWsLat + kLat / 8) * 16 + 16 * (q ^ ((r >> 2) & 3));
+}
+
+__global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
+    const int32_t* __restrict__ q_seq, CacheRows cr, const uint16_t* __restrict__ q_lat,
+    const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    int k, float scale_log2, uint16_t* __restrict__ o_lat) {
+  // Four distinct arrays: the compiler then waits only for the gathers that
+  // target the array being read.
+  __shared__ __attribute__((aligned(16))) uint16_t tile0[kWsTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile1[kWsTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile2[kWsTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile3[kWsTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) float s_alpha[2][kHeads];
+  __shared__ __attribute__((aligned(16))) float s_bias[4][kKT];
+  __shared__ float s_l[kHeads];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool qk = wave < 4;
+  const int wr = wave & 3;  // QK: head group; PV: latent slice
+  const int l16 = lane & 15, g = lane >> 4;
+  const int seq = q_seq[t];
+  const uint16_t* const kv_seq = kv + cr.seq_row0[seq] * kRow;  // (contiguous caches)
+  const int32_t* irow = idx + (int64_t)t * k;
+  const int ntiles = (k + kKT - 1) / kKT;
+
+  auto slot = [&](int b) __attribute__((always_inline)) -> uint16_t* {
+    return b == 0 ? tile0 : (b == 1 ? tile1 : (b == 2 ? tile2 : tile3));
+  };
+  auto lds_addr = [](const void* p) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  };
+
+  // ---- positions: lane l holds the entry of row l % 32 of a tile: the
+  // position, or position 0 with kAbsent set for an absent one (-1 in the
+  // index row, or past k), which the gather's 24-bit offset multiply ignores
+  auto pos_load = [&](int u) __attribute__((always_inline)) -> int {
+    const int j = u * kKT + (lane & 31);
+    return j < k ? irow[min(j, k - 1)] : -1;
+  };
+  auto pos_entry = [&](int e) __attribute__((always_inline)) -> int { return e >= 0 ? e : kAbsent; };
+  const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
+  const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
+  const uint32_t kv_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kv_a >> 32));
+  const uint16_t* const kv_u = reinterpret_cast<const uint16_t*>(((uint64_t)kv_hi << 32) | kv_lo);
+  const __amdgpu_buffer_rsrc_t kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kv_u), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+  // latent rows wave, wave + 8, +16, +24 of a tile; QK waves also rope load wave
+  uint32_t voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) voff[q] = (uint32_t)((lane ^ (((wave + 8 * q) >> 2) & 3)) * 16);
+  const int rope_row = 8 * wr + (lane >> 3);
+  const uint32_t rope_colb = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ ((rope_row >> 1) & 7)) * 16);
+  // gather of a tile into ring slot dst from its entries pe (pos_entry applied)
+  auto gather = [&](int pe, uint16_t* dst, int bslot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = wave + 8 * q;
+      const int e = __builtin_amdgcn_readlane(pe, r);
+      uint16_t* const d = dst + r * kWsLat * 8;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, voff[q], (e & 0xFFFFFF) * (kRow * 2), 0, 0);
+    }
+    if (qk) {
+      const int e = __shfl(pe, rope_row, 64);
+      uint16_t* const d = dst + (kWsRope0 + 64 * wr) * 8;
+      const uint32_t off = (uint32_t)(e & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, off, 0, 0, 0);
+      // key biases of the tile (0 present, -inf absent), wave 0
+      if (wave == 0 && lane < kKT) {
+        const float bias = (pe & kAbsent) == 0 ? 0.f : -INFINITY;
+        asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(&s_bias[bslot][lane])), "v"(bias) : "memory");
+      }
+    }
+  };
+
+  const int hq = 16 * wr + l16;
+  // per-lane LDS offsets (bf16 elements): QK chunk g of rows l16 and 16 + l16;
+  // PV rows 8g + l16/4 and 8g + 4 + l16/4, chunk 16 wr + (l16 % 4)/2 (even
+  // dim blocks) and + 2 (odd ones), half l16 % 2
+  const int qk_off0 = ws_lat_slot(l16, g) * 8, qk_off1 = ws_lat_slot(16 + l16, g) * 8;
+  const int pv_r0 = 8 * g + (l16 >> 2), pv_jj = (l16 & 3) >> 1;
+  const int pv_e0 = ws_lat_slot(pv_r0, 16 * wr + pv_jj) * 8 + 4 * (l16 & 1);
+  const int pv_o0 = ws_lat_slot(pv_r0, 16 * wr + 2 + pv_jj) * 8 + 4 * (l16 & 1);
+  const int pv_e1 = ws_lat_slot(pv_r0 + 4, 16 * wr + pv_jj) * 8 + 4 * (l16 & 1);
+  const int pv_o1 = ws_lat_slot(pv_r0 + 4, 16 * wr + 2 + pv_jj) * 8 + 4 * (l16 & 1);
+
+  // QK + softmax of the tile in ring slot b (parity par): writes P^T and alpha
+  auto qk_step = [&](const uint16_t* tb, int b, int par, const bf16x8 (&qb)[18], float& m_ref,
+                     float& l_part) __attribute__((always_inline)) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* const base = tb + (kb ? qk_off1 : qk_off0);
+      const int r = 16 * kb + l16;
+      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint16_t* const a = ks < 16 ? base + 32 * ks : tb + ws_rope_slot(r, 4 * (ks - 16) + g) * 8;
+        acc[ks % 3] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(a)), qb[ks], acc[ks % 3]);
+      }
+      sc[kb] = acc[0] + acc[1] + acc[2];
+    }
+    f32x4 bias[2];
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(bias[0]), "=v"(bias[1])
+                 : "v"(lds_addr(&s_bias[b][4 * g])), "v"(lds_addr(&s_bias[b][16 + 4 * g]))
+                 : "memory");
+    float z[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[4 * kb + i] = fmaf(sc[kb][i], scale_log2, bias[kb][i]);
+        tmax = fmaxf(tmax, z[4 * kb + i]);
+      }
+    tmax = fmaxf(tmax, xor_lane(tmax, 16));
+    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    const float m_new = tmax > m_ref + kRescaleLog2 ? tmax : m_ref;
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+      ps += p[i];
+    }
+    l_part = l_part * alpha + ps;
+    // P^T of head hq, keys 16kb + 4g .. +3: half (g & 1) of chunk 2kb + g/2
+    const uint16_t* const pt_slot = slot(2 * par + (hq >> 5));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t a = lds_addr(pt_slot) + ws_pt_off(hq, 2 * kb + (g >> 1)) + 8 * (g & 1);
+      const u32x2 v = {cvt_pk_bf16(p[4 * kb], p[4 * kb + 1]), cvt_pk_bf16(p[4 * kb + 2], p[4 * kb + 3])};
+      asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+    }
+    if (g == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(&s_alpha[par][hq])), "v"(alpha) : "memory");
+  };
+  // PV of the tile in ring slot b (parity par)
+  auto pv_step = [&](const uint16_t* tb, int par, f32x4 (&o)[8][4]) __attribute__((always_inline)) {
+    float al[4];
+    u32x4 pb[4];
+    {
+      const uint32_t a0 = lds_addr(&s_alpha[par][l16]);
+      const uint32_t p0 = lds_addr(slot(2 * par)) + ws_pt_off(l16, g);
+      const uint32_t p1 = lds_addr(slot(2 * par)) + ws_pt_off(16 + l16, g);
+      const uint32_t p2 = lds_addr(slot(2 * par + 1)) + ws_pt_off(l16, g);
+      const uint32_t p3 = lds_addr(slot(2 * par + 1)) + ws_pt_off(16 + l16, g);
+      asm volatile(
+          "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:64\n\tds_read_b32 %2, %8 offset:128\n\t"
+          "ds_read_b32 %3, %8 offset:192\n\tds_read_b128 %4, %9\n\tds_read_b128 %5, %10\n\t"
+          "ds_read_b128 %6, %11\n\tds_read_b128 %7, %12\n\ts_waitcnt lgkmcnt(0)"
+          : "=v"(al[0]), "=v"(al[1]), "=v"(al[2]), "=v"(al[3]), "=v"(pb[0]), "=v"(pb[1]), "=v"(pb[2]), "=v"(pb[3])
+          : "v"(a0), "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+          : "memory");
+    }
+    bool need = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) need |= al[j] != 1.f;
+    if (__any(need)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[e][j] *= al[j];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int de = 2 * (e & ~1);  // chunk distance of dim block e from its parity's base
+      const uint16_t* const a0 = tb + ((e & 1) ? pv_o0 : pv_e0) + 8 * de;
+      const uint16_t* const a1 = tb + ((e & 1) ? pv_o1 : pv_e1) + 8 * de;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a0));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a1));
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[e][j] = mfma16(fa, as_bf16x8(pb[j]), o[e][j]);
+    }
+  };
+
+  // The two roles run the same schedule of gathers and barriers in separate
+  // code paths (so that neither holds the other's registers: q and the
+  // softmax state in QK waves, the 128 accumulators in PV waves).
+  // Prologue: gathers of tiles 0 and 1, positions of tile 2.  Step i (slot
+  // b = i % 4): tile i + 2 is gathered into the slot of tile i - 2 and the
+  // positions of tile i + 3 are requested; QK waves take tile i (past the
+  // last tile: absent rows, no effect), PV waves tile i - 1 (from step 1 on);
+  // then each wave waits for its own loads of tile i + 1 (issued one step
+  // earlier: only this step's position load and gather are younger) and the
+  // barrier publishes them together with tile i's P^T and alpha.
+  auto run = [&](auto QKC, auto&& work) __attribute__((always_inline)) {
+    constexpr bool kQk = decltype(QKC)::value;
+    int pe_next;
+    {
+      const int e0 = pos_entry(pos_load(0));
+      const int e1 = pos_entry(pos_load(1));
+      pe_next = pos_entry(pos_load(2));
+      gather(e0, tile0, 0);
+      gather(e1, tile1, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // (both tiles, the query operands and the next positions)
+    lds_barrier();
+    auto step = [&](int i, auto BC, auto PVC) __attribute__((always_inline)) {
+      constexpr int b = decltype(BC)::value;
+      const int pe = pe_next;
+      pe_next = pos_entry(pos_load(i + 3));
+      gather(pe, slot((b + 2) % 4), (b + 2) % 4);
+      work(i, BC, PVC);
+      if constexpr (kQk) wait_vm_wide<kWsNL + 1>();
+      else wait_vm_wide<kWsNL>();
+      lds_barrier();
+    };
+    using Yes = std::integral_constant<bool, true>;
+    step(0, std::integral_constant<int, 0>{}, std::integral_constant<bool, false>{});
+    for (int i = 1; i <= ntiles; i += 4) {
+      step(i, std::integral_constant<int, 1>{}, Yes{});
+      step(i + 1, std::integral_constant<int, 2>{}, Yes{});
+      step(i + 2, std::integral_constant<int, 3>{}, Yes{});
+      step(i + 3, std::integral_constant<int, 0>{}, Yes{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // no gather may still target this workgroup's LDS at exit
+  };
+
+  if (qk) {
+    bf16x8 qb[18];
+    {
+      const uint16_t* ql = q_lat + ((int64_t)t * kHeads + hq) * kLat + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qb[ks] = as_bf16x8(ld16(ql + 32 * ks));
+      const uint16_t* qr = q_rope + ((int64_t)t * kHeads + hq) * kRope + 8 * g;
+      qb[16] = as_bf16x8(ld16(qr));
+      qb[17] = as_bf16x8(ld16(qr + 32));
+    }
+    float m_ref = -1e30f, l_part = 0.f;
+    run(std::integral_constant<bool, true>{}, [&](int, auto BC, auto) __attribute__((always_inline)) {
+      constexpr int b = decltype(BC)::value;
+      qk_step(slot(b), b, b & 1, qb, m_ref, l_part);
+    });
+    // 1 / (sum of a head's weights) for the PV waves
+    float l_sum = l_part + xor_lane(l_part, 16);
+    l_sum += xor_lane(l_sum, 32);
+    if (g == 0) s_l[hq] = l_sum;
+    __syncthreads();
+  } else {
+    f32x4 o[8][4];  // o[e][j]: dims 128 wr + 16e + 4g .. +3 of head 16j + l16
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[e][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    run(std::integral_constant<bool, false>{}, [&](int, auto BC, auto PVC) __attribute__((always_inline)) {
+      constexpr int b = decltype(BC)::value;
+      if constexpr (decltype(PVC)::value) pv_step(slot((b + 3) % 4), (b + 1) & 1, o);
+    });
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 16 * j + l16;
+      const float L = s_l[h];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* dst = o_lat + ((int64_t)t * kHeads + h) * kLat + 128 * wr + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x2*>(dst + 16 * e) =
+            u32x2{pack_bf16x2(o[e][j][0] * inv, o[e][j][1] * inv), pack_bf16x2(o[e][j][2] * inv, o[e][j][3] * inv)};
+    }
+  }
+}
+
 // ---------------------------------------------------------------- merge
 // Split partials of (query t, split s) form one slab of kHeads * kLat bf16
 // values, each normalised by its split's sum l, in the core's accumulator
@@ -1207,6 +1513,9 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
       mla_decode_kernel<false><<<dgrid, kDecWaves * 64, 0, st>>>(
           b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
           p.dec_keys_per_split, S, o_lat, o_part, ml_part);
+  } else if (S == 1 && !b.paged() && !b.kv_int4) {
+    mla_ws_kernel<<<T, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx,
+                                             p.k, scale_log2, o_lat);
   } else if (b.paged() && b.kv_int4)
     mla_core_kernel<true, true><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
                                                                scale_log2, kps, S, o_lat, o_part, ml_part);
