@@ -112,6 +112,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Maximum and sum of v over lanes l, l ^ 16, l ^ 32 and l ^ 48, in every lane.
+// v_permlane16_swap exchanges 16-lane rows 1 and 3 of its first operand with
+// rows 0 and 2 of its second, v_permlane32_swap the upper half of the first
+// with the lower half of the second; with v in both operands the two results
+// hold, in each lane, v of the lane and of its partner row (half).  Plain VALU
+// work, unlike a shuffle through the LDS crossbar.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // s_waitcnt vmcnt(n) (n < 16), other counters untouched.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -322,8 +341,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
       z[jj] = v;
       tmax = fmaxf(tmax, v);
     }
-    tmax = fmaxf(tmax, xor_lane(tmax, 16));
-    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    tmax = rows_max(tmax);
     if (g == 0) s_max[hf][hq] = tmax;
     lds_barrier();
     mid();
@@ -451,8 +469,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
   __builtin_amdgcn_s_waitcnt(0);  // no load may still target this workgroup's LDS at exit
 
   // ---- finish: l of a head = its lanes' partial sums over both key halves
-  float l_sum = l_part + xor_lane(l_part, 16);
-  l_sum += xor_lane(l_sum, 32);
+  const float l_sum = rows_sum(l_part);
   if (g == 0) {
     s_l[hf][hq] = l_sum;
     if (hf == 0) s_m[hq] = m_ref;
@@ -705,8 +722,7 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
       z[i] = fmaf(sc[i], scale_log2, (pm >> i) & 1u ? 0.f : -INFINITY);
       tmax = fmaxf(tmax, z[i]);
     }
-    tmax = fmaxf(tmax, xor_lane(tmax, 16));
-    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    tmax = rows_max(tmax);
     // lazy reference maximum (see mla_core_kernel); v_exp_f32 directly
     const float m_new = tmax > m_ref + kRescaleLog2 ? tmax : m_ref;
     const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -769,8 +785,7 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
   // ---- the four waves' partial results: reference maxima and sums meet in
   // LDS, then each wave adds up 8 latent blocks (128 dims) of all four
-  float l_sum = l_part + xor_lane(l_part, 16);
-  l_sum += xor_lane(l_sum, 32);
+  const float l_sum = rows_sum(l_part);
   if (g == 0) {
     s_ml[wave][l16][0] = m_ref;
     s_ml[wave][l16][1] = l_sum;
@@ -835,31 +850,30 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
 // ago, PV'd in the last one); each row is one direct-to-LDS load (its
 // position wave-uniform), the rope parts four more.  The positions come from
 // the index row in global memory one step before their gather.
-// Tile layout (38,912 B): latent row r at slots r*68 .. r*68+63, logical chunk
-// c at r*68 + (c ^ ((r >> 2) & 3)) (the XOR touches the chunk's two low bits
-// only, so a lane's successive QK chunks sit at constant distances, PV's at
-// constant distances per parity), slots r*68+64 .. +67 unused by the gather;
-// rope area at slot 2176, chunk c of row r at 2176 + r*8 + (c ^ ((r >> 1) & 7)).
-// QK row reads and PV transposing reads are free of bank conflicts.  P^T of
-// head h for tiles of parity b lives in the unused slots of row h % 32 of
-// ring slot 2b + h / 32 (chunk q of keys 8q..8q+7 at q ^ ((row >> 2) & 3));
-// P^T, the rescale factors and the key biases are read and written with
-// inline LDS instructions that wait for themselves, because the compiler
-// cannot tell those accesses from the pending gathers into the same arrays
-// and would otherwise wait for every gather in flight.
-constexpr int kWsLat = kLat / 8 + 4;                   // 68 slots per latent row
-constexpr int kWsRope0 = kKT * kWsLat;                 // 2176
-constexpr int kWsTileSlots = kWsRope0 + kKT * (kRope / 8);  // 2432 slots = 38,912 B
+// Tile layout (36,864 B, slots of 16 B): latent row r at slots r*64 .. r*64+63,
+// logical chunk c at r*64 + (c ^ swz(r)) with swz(r) = (r ^ 2r) mod 16; rope
+// area at slot 2048, chunk c of row r at 2048 + r*8 + (c ^ ((r >> 1) & 7)).
+// With these swizzles (chosen by measuring SQ_LDS_BANK_CONFLICT over candidate
+// layouts on gfx950) the QK row reads, the QK rope reads and the PV
+// transposing reads are all free of bank conflicts.  swz is linear over XOR and
+// depends on r mod 16 only, so a lane's QK reads need 4 base addresses (one per
+// chunk step mod 4; rows r + 16 add a constant) and its PV reads 8 (rows r + 4
+// reuse them with the dim block index XOR 6).  P^T of the tiles of parity b is
+// s_pt[b]: chunk q (keys 8q .. 8q+7) of head h at slot h*4 + (q ^ ((h >> 1) & 3))
+// (conflict-free PV reads).  P^T and the rescale factors are read and written,
+// and the key biases written, with inline LDS instructions that wait for
+// themselves, because the compiler would otherwise order them after the
+// pending gathers.
+constexpr int kWsLat = kLat / 8;                       // 64 slots per latent row
+constexpr int kWsRope0 = kKT * kWsLat;                 // 2048
+constexpr int kWsTileSlots = kWsRope0 + kKT * (kRope / 8);  // 2304 slots = 36,864 B
 constexpr int kWsNL = 5;                               // gather loads per tile of a QK wave (PV waves: 4)
 
-__device__ __forceinline__ int ws_lat_slot(int r, int c) { return r * kWsLat + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int ws_swz(int r) { return (r ^ (r << 1)) & 15; }
+__device__ __forceinline__ int ws_lat_slot(int r, int c) { return r * kWsLat + (c ^ ws_swz(r)); }
 __device__ __forceinline__ int ws_rope_slot(int r, int c) { return kWsRope0 + r * 8 + (c ^ ((r >> 1) & 7)); }
-// byte offset of P^T chunk q (keys 8q .. 8q+7) of head h, parity b, within
-// ring slot 2b + h / 32
-__device__ __forceinline__ int ws_pt_off(int h, int q) {
-  const int r = h & 31;
-  return (r * kWsLat + kLat / 8) * 16 + 16 * (q ^ ((r >> 2) & 3));
-}
+// byte offset of P^T chunk q (keys 8q .. 8q+7) of head h within s_pt[b]
+__device__ __forceinline__ int ws_pt_off(int h, int q) { return 16 * (h * 4 + (q ^ ((h >> 1) & 3))); }
 
 __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr, const uint16_t* __restrict__ q_lat,
@@ -871,6 +885,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t tile1[kWsTileSlots * 8];
   __shared__ __attribute__((aligned(16))) uint16_t tile2[kWsTileSlots * 8];
   __shared__ __attribute__((aligned(16))) uint16_t tile3[kWsTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_pt[2][kHeads * kKT];
   __shared__ __attribute__((aligned(16))) float s_alpha[2][kHeads];
   __shared__ __attribute__((aligned(16))) float s_bias[4][kKT];
   __shared__ float s_l[kHeads];
@@ -900,6 +915,15 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     return j < k ? irow[min(j, k - 1)] : -1;
   };
   auto pos_entry = [&](int e) __attribute__((always_inline)) -> int { return e >= 0 ? e : kAbsent; };
+  // QK waves: lane l also loads the entry of the rope row it gathers, 8 wr + l / 8
+  const int rope_row = 8 * wr + (lane >> 3);
+  // (a load without a branch: inside one, the compiler computes the gather
+  // offset from the entry right after the load and waits for it there)
+  auto rope_pos_load = [&](int u) __attribute__((always_inline)) -> int {
+    const int j = u * kKT + rope_row;
+    const int v = irow[max(min(j, k - 1), 0)];
+    return j < k ? v : -1;
+  };
   const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
   const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
   const uint32_t kv_hi = __builtin_amdgcn_readfirstlane((uint32_t)(kv_a >> 32));
@@ -909,11 +933,11 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // latent rows wave, wave + 8, +16, +24 of a tile; QK waves also rope load wave
   uint32_t voff[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) voff[q] = (uint32_t)((lane ^ (((wave + 8 * q) >> 2) & 3)) * 16);
-  const int rope_row = 8 * wr + (lane >> 3);
+  for (int q = 0; q < 4; ++q) voff[q] = (uint32_t)((lane ^ ws_swz(wave + 8 * q)) * 16);
   const uint32_t rope_colb = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ ((rope_row >> 1) & 7)) * 16);
-  // gather of a tile into ring slot dst from its entries pe (pos_entry applied)
-  auto gather = [&](int pe, uint16_t* dst, int bslot) __attribute__((always_inline)) {
+  // gather of a tile into ring slot dst from its entries pe (and pr, the rope
+  // row entries of a QK wave; pos_entry applied)
+  auto gather = [&](int pe, int pr, uint16_t* dst, int bslot) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = wave + 8 * q;
@@ -922,9 +946,8 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, voff[q], (e & 0xFFFFFF) * (kRow * 2), 0, 0);
     }
     if (qk) {
-      const int e = __shfl(pe, rope_row, 64);
       uint16_t* const d = dst + (kWsRope0 + 64 * wr) * 8;
-      const uint32_t off = (uint32_t)(e & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
+      const uint32_t off = (uint32_t)(pr & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, off, 0, 0, 0);
       // key biases of the tile (0 present, -inf absent), wave 0
       if (wave == 0 && lane < kKT) {
@@ -935,15 +958,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   };
 
   const int hq = 16 * wr + l16;
-  // per-lane LDS offsets (bf16 elements): QK chunk g of rows l16 and 16 + l16;
-  // PV rows 8g + l16/4 and 8g + 4 + l16/4, chunk 16 wr + (l16 % 4)/2 (even
-  // dim blocks) and + 2 (odd ones), half l16 % 2
-  const int qk_off0 = ws_lat_slot(l16, g) * 8, qk_off1 = ws_lat_slot(16 + l16, g) * 8;
+
+  // per-lane LDS offsets (bf16 elements) of the reads from a tile: QK chunks
+  // 4j + g of row l16 (j = ks mod 4); PV dim block e (chunk 16 wr + 2e +
+  // (l16 % 4) / 2, half l16 % 2) of row 8g + l16 / 4
+  int qkb[4], pvb[8];
   const int pv_r0 = 8 * g + (l16 >> 2), pv_jj = (l16 & 3) >> 1;
-  const int pv_e0 = ws_lat_slot(pv_r0, 16 * wr + pv_jj) * 8 + 4 * (l16 & 1);
-  const int pv_o0 = ws_lat_slot(pv_r0, 16 * wr + 2 + pv_jj) * 8 + 4 * (l16 & 1);
-  const int pv_e1 = ws_lat_slot(pv_r0 + 4, 16 * wr + pv_jj) * 8 + 4 * (l16 & 1);
-  const int pv_o1 = ws_lat_slot(pv_r0 + 4, 16 * wr + 2 + pv_jj) * 8 + 4 * (l16 & 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qkb[j] = ws_lat_slot(l16, 4 * j + g) * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pvb[e] = ws_lat_slot(pv_r0, 16 * wr + 2 * e + pv_jj) * 8 + 4 * (l16 & 1);
 
   // QK + softmax of the tile in ring slot b (parity par): writes P^T and alpha
   auto qk_step = [&](const uint16_t* tb, int b, int par, const bf16x8 (&qb)[18], float& m_ref,
@@ -951,21 +975,19 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     f32x4 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint16_t* const base = tb + (kb ? qk_off1 : qk_off0);
       const int r = 16 * kb + l16;
       f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const uint16_t* const a = ks < 16 ? base + 32 * ks : tb + ws_rope_slot(r, 4 * (ks - 16) + g) * 8;
+        // chunk 4 ks + g of row r: base (ks mod 4) + 16 chunks per 4 steps + 16 rows per kb
+        const uint16_t* const a = ks < 16 ? tb + qkb[ks & 3] + 128 * (ks >> 2) + 16 * kWsLat * 8 * kb
+                                          : tb + ws_rope_slot(r, 4 * (ks - 16) + g) * 8;
         acc[ks % 3] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(a)), qb[ks], acc[ks % 3]);
       }
       sc[kb] = acc[0] + acc[1] + acc[2];
     }
-    f32x4 bias[2];
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(bias[0]), "=v"(bias[1])
-                 : "v"(lds_addr(&s_bias[b][4 * g])), "v"(lds_addr(&s_bias[b][16 + 4 * g]))
-                 : "memory");
+    const f32x4 bias[2] = {*reinterpret_cast<const f32x4*>(&s_bias[b][4 * g]),
+                           *reinterpret_cast<const f32x4*>(&s_bias[b][16 + 4 * g])};
     float z[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -975,8 +997,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
         z[4 * kb + i] = fmaf(sc[kb][i], scale_log2, bias[kb][i]);
         tmax = fmaxf(tmax, z[4 * kb + i]);
       }
-    tmax = fmaxf(tmax, xor_lane(tmax, 16));
-    tmax = fmaxf(tmax, xor_lane(tmax, 32));
+    tmax = rows_max(tmax);
     const float m_new = tmax > m_ref + kRescaleLog2 ? tmax : m_ref;
     const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
     m_ref = m_new;
@@ -989,10 +1010,9 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     }
     l_part = l_part * alpha + ps;
     // P^T of head hq, keys 16kb + 4g .. +3: half (g & 1) of chunk 2kb + g/2
-    const uint16_t* const pt_slot = slot(2 * par + (hq >> 5));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t a = lds_addr(pt_slot) + ws_pt_off(hq, 2 * kb + (g >> 1)) + 8 * (g & 1);
+      const uint32_t a = lds_addr(&s_pt[par][0]) + ws_pt_off(hq, 2 * kb + (g >> 1)) + 8 * (g & 1);
       const u32x2 v = {cvt_pk_bf16(p[4 * kb], p[4 * kb + 1]), cvt_pk_bf16(p[4 * kb + 2], p[4 * kb + 3])};
       asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
     }
@@ -1003,17 +1023,16 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     float al[4];
     u32x4 pb[4];
     {
+      // heads l16 + 16j: alpha 64 B apart, P^T rows 1 KB apart (the chunk swizzle
+      // depends on (h >> 1) & 3, the same for every j)
       const uint32_t a0 = lds_addr(&s_alpha[par][l16]);
-      const uint32_t p0 = lds_addr(slot(2 * par)) + ws_pt_off(l16, g);
-      const uint32_t p1 = lds_addr(slot(2 * par)) + ws_pt_off(16 + l16, g);
-      const uint32_t p2 = lds_addr(slot(2 * par + 1)) + ws_pt_off(l16, g);
-      const uint32_t p3 = lds_addr(slot(2 * par + 1)) + ws_pt_off(16 + l16, g);
+      const uint32_t p0 = lds_addr(&s_pt[par][0]) + ws_pt_off(l16, g);
       asm volatile(
           "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:64\n\tds_read_b32 %2, %8 offset:128\n\t"
-          "ds_read_b32 %3, %8 offset:192\n\tds_read_b128 %4, %9\n\tds_read_b128 %5, %10\n\t"
-          "ds_read_b128 %6, %11\n\tds_read_b128 %7, %12\n\ts_waitcnt lgkmcnt(0)"
+          "ds_read_b32 %3, %8 offset:192\n\tds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:1024\n\t"
+          "ds_read_b128 %6, %9 offset:2048\n\tds_read_b128 %7, %9 offset:3072\n\ts_waitcnt lgkmcnt(0)"
           : "=v"(al[0]), "=v"(al[1]), "=v"(al[2]), "=v"(al[3]), "=v"(pb[0]), "=v"(pb[1]), "=v"(pb[2]), "=v"(pb[3])
-          : "v"(a0), "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+          : "v"(a0), "v"(p0)
           : "memory");
     }
     bool need = false;
@@ -1027,9 +1046,9 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int de = 2 * (e & ~1);  // chunk distance of dim block e from its parity's base
-      const uint16_t* const a0 = tb + ((e & 1) ? pv_o0 : pv_e0) + 8 * de;
-      const uint16_t* const a1 = tb + ((e & 1) ? pv_o1 : pv_e1) + 8 * de;
+      // rows pv_r0 and pv_r0 + 4 (= pv_r0 ^ 4, swizzled by swz ^ 12: dim block e ^ 6)
+      const uint16_t* const a0 = tb + pvb[e];
+      const uint16_t* const a1 = tb + pvb[e ^ 6] + 4 * kWsLat * 8;
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a0));
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a1));
       const bf16x8 fa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1041,32 +1060,51 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // The two roles run the same schedule of gathers and barriers in separate
   // code paths (so that neither holds the other's registers: q and the
   // softmax state in QK waves, the 128 accumulators in PV waves).
-  // Prologue: gathers of tiles 0 and 1, positions of tile 2.  Step i (slot
+  // Prologue: gathers of tiles 0 and 1, positions of tile 2 (rope: 2, 3).  Step i (slot
   // b = i % 4): tile i + 2 is gathered into the slot of tile i - 2 and the
   // positions of tile i + 3 are requested; QK waves take tile i (past the
   // last tile: absent rows, no effect), PV waves tile i - 1 (from step 1 on);
   // then each wave waits for its own loads of tile i + 1 (issued one step
-  // earlier: only this step's position load and gather are younger) and the
+  // earlier: only this step's position loads and gather are younger) and the
   // barrier publishes them together with tile i's P^T and alpha.
   auto run = [&](auto QKC, auto&& work) __attribute__((always_inline)) {
     constexpr bool kQk = decltype(QKC)::value;
-    int pe_next;
+    // rope entries (QK waves) run one step further ahead than the latent ones:
+    // loaded two steps before their gather, they have arrived by the wait that
+    // ends the step before it, so using them waits for no younger gather
+    int pe_next, pr_next = 0, pr_next2 = 0;
     {
       const int e0 = pos_entry(pos_load(0));
       const int e1 = pos_entry(pos_load(1));
-      pe_next = pos_entry(pos_load(2));
-      gather(e0, tile0, 0);
-      gather(e1, tile1, 1);
+      int r0 = 0, r1 = 0;
+      if constexpr (kQk) {
+        r0 = pos_entry(rope_pos_load(0));
+        r1 = pos_entry(rope_pos_load(1));
+        pr_next = rope_pos_load(2);
+        pr_next2 = rope_pos_load(3);
+      }
+      pe_next = pos_load(2);
+      gather(e0, r0, tile0, 0);
+      gather(e1, r1, tile1, 1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // (both tiles, the query operands and the next positions)
     lds_barrier();
     auto step = [&](int i, auto BC, auto PVC) __attribute__((always_inline)) {
       constexpr int b = decltype(BC)::value;
-      const int pe = pe_next;
-      pe_next = pos_entry(pos_load(i + 3));
-      gather(pe, slot((b + 2) % 4), (b + 2) % 4);
+      // (entries travel raw and get pos_entry here: a loop-carried value
+      // computed from a load makes the compiler wait for it at the loop edge)
+      const int pe = pos_entry(pe_next), pr = pos_entry(pr_next);
+      pe_next = pos_load(i + 3);
+      if constexpr (kQk) {
+        pr_next = pr_next2;
+        pr_next2 = rope_pos_load(i + 4);
+      }
+      // the position loads go out before the gathers: the waits for them count
+      // only older loads
+      __builtin_amdgcn_sched_barrier(0);
+      gather(pe, pr, slot((b + 2) % 4), (b + 2) % 4);
       work(i, BC, PVC);
-      if constexpr (kQk) wait_vm_wide<kWsNL + 1>();
+      if constexpr (kQk) wait_vm_wide<kWsNL + 2>();
       else wait_vm_wide<kWsNL>();
       lds_barrier();
     };
@@ -1097,8 +1135,7 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
       qk_step(slot(b), b, b & 1, qb, m_ref, l_part);
     });
     // 1 / (sum of a head's weights) for the PV waves
-    float l_sum = l_part + xor_lane(l_part, 16);
-    l_sum += xor_lane(l_sum, 32);
+    const float l_sum = rows_sum(l_part);
     if (g == 0) s_l[hq] = l_sum;
     __syncthreads();
   } else {
