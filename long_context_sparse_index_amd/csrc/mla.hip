@@ -972,22 +972,37 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // QK + softmax of the tile in ring slot b (parity par): writes P^T and alpha
   auto qk_step = [&](const uint16_t* tb, int b, int par, const bf16x8 (&qb)[18], float& m_ref,
                      float& l_part) __attribute__((always_inline)) {
-    f32x4 sc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int r = 16 * kb + l16;
-      f32x4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        // chunk 4 ks + g of row r: base (ks mod 4) + 16 chunks per 4 steps + 16 rows per kb
-        const uint16_t* const a = ks < 16 ? tb + qkb[ks & 3] + 128 * (ks >> 2) + 16 * kWsLat * 8 * kb
-                                          : tb + ws_rope_slot(r, 4 * (ks - 16) + g) * 8;
-        acc[ks % 3] = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(a)), qb[ks], acc[ks % 3]);
-      }
-      sc[kb] = acc[0] + acc[1] + acc[2];
-    }
+    // chunk ks of row 16 kb + l16: latent chunk 4 ks + g at base (ks mod 4) + 16
+    // chunks per 4 steps + 16 rows per kb; ks 16, 17: rope chunks
+    auto qk_a = [&](int kb, int ks) __attribute__((always_inline)) -> u32x4 {
+      const uint16_t* const a = ks < 16 ? tb + qkb[ks & 3] + 128 * (ks >> 2) + 16 * kWsLat * 8 * kb
+                                        : tb + ws_rope_slot(16 * kb + l16, 4 * (ks - 16) + g) * 8;
+      return *reinterpret_cast<const u32x4*>(a);
+    };
+    // The 36 operands (block kb = n / 18, step ks = n % 18) are read kQkDepth
+    // ahead of their MFMA, so the MFMA chain does not wait on LDS latency read
+    // by read (the interleave is pinned; the compiler would keep fewer in flight).
     const f32x4 bias[2] = {*reinterpret_cast<const f32x4*>(&s_bias[b][4 * g]),
                            *reinterpret_cast<const f32x4*>(&s_bias[b][16 + 4 * g])};
+    constexpr int kQkDepth = 8;
+    u32x4 A[36];
+#pragma unroll
+    for (int n = 0; n < kQkDepth; ++n) A[n] = qk_a(n / 18, n % 18);
+    f32x4 acc[2][3] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
+                       {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
+#pragma unroll
+    for (int n = 0; n < 36; ++n) {
+      const int kb = n / 18, ks = n % 18;
+      acc[kb][ks % 3] = mfma16(as_bf16x8(A[n]), qb[ks], acc[kb][ks % 3]);
+      if (n + kQkDepth < 36) A[n + kQkDepth] = qk_a((n + kQkDepth) / 18, (n + kQkDepth) % 18);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth + 2, 0);  // the biases and the first operands
+#pragma unroll
+    for (int n = 0; n < 36; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (n + kQkDepth < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    const f32x4 sc[2] = {acc[0][0] + acc[0][1] + acc[0][2], acc[1][0] + acc[1][1] + acc[1][2]};
     float z[8];
     float tmax = -INFINITY;
 #pragma unroll
