@@ -875,6 +875,30 @@ __device__ __forceinline__ int ws_rope_slot(int r, int c) { return kWsRope0 + r 
 // byte offset of P^T chunk q (keys 8q .. 8q+7) of head h within s_pt[b]
 __device__ __forceinline__ int ws_pt_off(int h, int q) { return 16 * (h * 4 + (q ^ ((h >> 1) & 3))); }
 
+// Paged caches, one split per query: the index row of query t turned into pool
+// rows, entries[t*stride + j] = the pool row of idx[t*k + j] (complemented when
+// the entry is -1: then the row of position 0, finite data that the core masks),
+// and entries[t*stride + k] = the complemented row of position 0 (what the core
+// reads for rows past k).  The entries live in the first k + 1 words of the
+// query's own o_lat row (64 KB), which the core writes only after its last read.
+constexpr int kWsEntryStride = kHeads * kLat / 2;  // int32 words per o_lat row
+static_assert(kMaxTopk + 1 <= kWsEntryStride, "a query's entries fit its o_lat row");
+__global__ __launch_bounds__(256) void ws_paged_entries_kernel(const int32_t* __restrict__ q_seq, CacheRows cr,
+                                                               const int32_t* __restrict__ idx, int k,
+                                                               int32_t* __restrict__ entries) {
+  const int t = blockIdx.x;
+  const int32_t* bt = cr.table + (int64_t)q_seq[t] * cr.max_pages;
+  const int32_t* irow = idx + (int64_t)t * k;
+  int32_t* erow = entries + (int64_t)t * kWsEntryStride;
+  const int mask = (1 << cr.page_shift) - 1;
+  const int row0 = bt[0] << cr.page_shift;
+  for (int j = threadIdx.x; j <= k; j += 256) {
+    const int pos = j < k ? irow[j] : -1;
+    erow[j] = pos >= 0 ? (bt[pos >> cr.page_shift] << cr.page_shift) | (pos & mask) : ~row0;
+  }
+}
+
+template <bool PAGED>
 __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr, const uint16_t* __restrict__ q_lat,
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
@@ -896,8 +920,9 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   const int wr = wave & 3;  // QK: head group; PV: latent slice
   const int l16 = lane & 15, g = lane >> 4;
   const int seq = q_seq[t];
-  const uint16_t* const kv_seq = kv + cr.seq_row0[seq] * kRow;  // (contiguous caches)
-  const int32_t* irow = idx + (int64_t)t * k;
+  // paged: kv is the pool and idx the pool-row entries (ws_paged_entries_kernel)
+  const uint16_t* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kRow;
+  const int32_t* irow = idx + (int64_t)t * (PAGED ? kWsEntryStride : k);
   const int ntiles = (k + kKT - 1) / kKT;
 
   auto slot = [&](int b) __attribute__((always_inline)) -> uint16_t* {
@@ -910,17 +935,24 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // ---- positions: lane l holds the entry of row l % 32 of a tile: the
   // position, or position 0 with kAbsent set for an absent one (-1 in the
   // index row, or past k), which the gather's 24-bit offset multiply ignores
+  // Paged: an entry is a pool row, complemented when absent; rows past k read
+  // the entry at k (the complemented row of position 0).
   auto pos_load = [&](int u) __attribute__((always_inline)) -> int {
     const int j = u * kKT + (lane & 31);
+    if constexpr (PAGED) return irow[min(j, k)];
     return j < k ? irow[min(j, k - 1)] : -1;
   };
-  auto pos_entry = [&](int e) __attribute__((always_inline)) -> int { return e >= 0 ? e : kAbsent; };
+  auto pos_entry = [&](int e) __attribute__((always_inline)) -> int {
+    if constexpr (PAGED) return e;
+    return e >= 0 ? e : kAbsent;
+  };
   // QK waves: lane l also loads the entry of the rope row it gathers, 8 wr + l / 8
   const int rope_row = 8 * wr + (lane >> 3);
   // (a load without a branch: inside one, the compiler computes the gather
   // offset from the entry right after the load and waits for it there)
   auto rope_pos_load = [&](int u) __attribute__((always_inline)) -> int {
     const int j = u * kKT + rope_row;
+    if constexpr (PAGED) return irow[min(j, k)];
     const int v = irow[max(min(j, k - 1), 0)];
     return j < k ? v : -1;
   };
@@ -943,18 +975,43 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
       const int r = wave + 8 * q;
       const int e = __builtin_amdgcn_readlane(pe, r);
       uint16_t* const d = dst + r * kWsLat * 8;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, voff[q], (e & 0xFFFFFF) * (kRow * 2), 0, 0);
+      if constexpr (PAGED) {
+        // a resource based at the row: a pool may pass 2^32 bytes
+        const uint16_t* const rowp = kv_u + (int64_t)(e ^ (e >> 31)) * kRow;
+        const __amdgpu_buffer_rsrc_t rr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rowp), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, d, 16, voff[q], 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, voff[q], (e & 0xFFFFFF) * (kRow * 2), 0, 0);
+      }
     }
     if (qk) {
-      uint16_t* const d = dst + (kWsRope0 + 64 * wr) * 8;
-      const uint32_t off = (uint32_t)(pr & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, off, 0, 0, 0);
+      if constexpr (!PAGED) {  // (paged: rope_fetch / rope_store)
+        uint16_t* const d = dst + (kWsRope0 + 64 * wr) * 8;
+        const uint32_t off = (uint32_t)(pr & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, off, 0, 0, 0);
+      }
       // key biases of the tile (0 present, -inf absent), wave 0
       if (wave == 0 && lane < kKT) {
-        const float bias = (pe & kAbsent) == 0 ? 0.f : -INFINITY;
+        const float bias = (PAGED ? pe >= 0 : (pe & kAbsent) == 0) ? 0.f : -INFINITY;
         asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(&s_bias[bslot][lane])), "v"(bias) : "memory");
       }
     }
+  };
+
+  // Paged caches, QK waves: the rope parts travel through registers (a per-lane
+  // 64-bit address; a direct-to-LDS global load here would make the compiler
+  // wait for every load in flight wherever it waits for one).  Lane l holds the
+  // 16 B that the rope DMA would put in slot l of the wave's 1 KB rope block:
+  // row 8 wr + l / 8, logical chunk (l & 7) ^ ((row >> 1) & 7).  The load goes
+  // out two steps before the tile is computed and is stored to LDS (an inline
+  // store: a compiled one into the ring array would wait for its gathers) in
+  // the step before.
+  auto rope_fetch = [&](int pr) __attribute__((always_inline)) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kv_u + (int64_t)(pr ^ (pr >> 31)) * kRow + rope_colb / 2);
+  };
+  auto rope_store = [&](uint16_t* dst, const u32x4& v) __attribute__((always_inline)) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(dst + (kWsRope0 + 64 * wr + lane) * 8)), "v"(v) : "memory");
   };
 
   const int hq = 16 * wr + l16;
@@ -1088,21 +1145,28 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     // loaded two steps before their gather, they have arrived by the wait that
     // ends the step before it, so using them waits for no younger gather
     int pe_next, pr_next = 0, pr_next2 = 0;
+    u32x4 rope_cur = {0u, 0u, 0u, 0u};  // paged QK waves: rope of the tile after the next
     {
       const int e0 = pos_entry(pos_load(0));
       const int e1 = pos_entry(pos_load(1));
       int r0 = 0, r1 = 0;
+      u32x4 rope0 = {0u, 0u, 0u, 0u};
       if constexpr (kQk) {
         r0 = pos_entry(rope_pos_load(0));
         r1 = pos_entry(rope_pos_load(1));
         pr_next = rope_pos_load(2);
         pr_next2 = rope_pos_load(3);
+        if constexpr (PAGED) {
+          rope0 = rope_fetch(r0);
+          rope_cur = rope_fetch(r1);
+        }
       }
       pe_next = pos_load(2);
       gather(e0, r0, tile0, 0);
       gather(e1, r1, tile1, 1);
+      __builtin_amdgcn_s_waitcnt(0);  // (both tiles, the query operands and the next positions)
+      if constexpr (PAGED && kQk) rope_store(tile0, rope0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // (both tiles, the query operands and the next positions)
     lds_barrier();
     auto step = [&](int i, auto BC, auto PVC) __attribute__((always_inline)) {
       constexpr int b = decltype(BC)::value;
@@ -1110,15 +1174,21 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
       // computed from a load makes the compiler wait for it at the loop edge)
       const int pe = pos_entry(pe_next), pr = pos_entry(pr_next);
       pe_next = pos_load(i + 3);
+      u32x4 rope_next = {0u, 0u, 0u, 0u};
       if constexpr (kQk) {
         pr_next = pr_next2;
         pr_next2 = rope_pos_load(i + 4);
+        if constexpr (PAGED) rope_next = rope_fetch(pr);  // (tile i + 2; in place of its rope DMA)
       }
       // the position loads go out before the gathers: the waits for them count
       // only older loads
       __builtin_amdgcn_sched_barrier(0);
       gather(pe, pr, slot((b + 2) % 4), (b + 2) % 4);
       work(i, BC, PVC);
+      if constexpr (PAGED && kQk) {
+        rope_store(slot((b + 1) % 4), rope_cur);  // tile i + 1, published by this step's barrier
+        rope_cur = rope_next;
+      }
       if constexpr (kQk) wait_vm_wide<kWsNL + 2>();
       else wait_vm_wide<kWsNL>();
       lds_barrier();
@@ -1565,9 +1635,18 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
       mla_decode_kernel<false><<<dgrid, kDecWaves * 64, 0, st>>>(
           b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
           p.dec_keys_per_split, S, o_lat, o_part, ml_part);
-  } else if (S == 1 && !b.paged() && !b.kv_int4) {
-    mla_ws_kernel<<<T, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx,
-                                             p.k, scale_log2, o_lat);
+  } else if (S == 1 && !b.kv_int4) {
+    if (b.paged()) {
+      int32_t* const entries = reinterpret_cast<int32_t*>(o_lat);
+      ws_paged_entries_kernel<<<T, 256, 0, st>>>(b.q_seq, b.rows, idx, p.k, entries);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      mla_ws_kernel<true><<<T, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv),
+                                                      entries, p.k, scale_log2, o_lat);
+    } else {
+      mla_ws_kernel<false><<<T, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope,
+                                                       static_cast<const uint16_t*>(kv), idx, p.k, scale_log2, o_lat);
+    }
   } else if (b.paged() && b.kv_int4)
     mla_core_kernel<true, true><<<grid, kCoreThreads, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kv, idx, p.k,
                                                                scale_log2, kps, S, o_lat, o_part, ml_part);

@@ -111,3 +111,42 @@ def test_paged_full_size_decode_sampled():
     out, idx = op.cpu().numpy(), ip.cpu().numpy()
     for t in (0, 5):
         _oracle_check(inp, t, idx[t], out[t], 2048)
+
+
+@pytest.mark.parametrize("page_size", [16, 128])
+def test_paged_one_split_equals_contiguous(page_size):
+    """Batches with one key split per query (the warp-specialised core) on paged
+    caches: index rows turned into pool rows, ragged k, -1 entries anywhere (the
+    row of position 0, never the NaN spare rows), bit-identical to the
+    contiguous layout; the forward too."""
+    lens, qs = [2600, 1800], [(i % 2, 1500 + i) for i in range(260)]
+    _say(f"[paged one split] page_size={page_size}")
+    inp = synth.custom(lens, qs, seed=53)
+    pc = synth.to_paged(inp, page_size, seed=page_size + 1)
+    dc = to_device(inp)
+    dp = to_device_paged(inp, pc, dc)
+    rng = np.random.default_rng(3)
+    k = 100
+    T = len(qs)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = int(inp.q_pos[t]) + 1
+        m = int(rng.integers(1, k + 1))
+        row = np.concatenate([rng.choice(n, m, replace=False).astype(np.int32), np.full(k - m, -1, np.int32)])
+        idx[t] = rng.permutation(row)
+    ti = torch.from_numpy(idx).cuda()
+    oc = dsa.dsa_sparse_mla_attn(dc.batch, dc.q_nope, dc.q_rope, dc.kv, dc.w_uk, dc.w_uv, ti, out_dtype=torch.float32)
+    op = dsa.dsa_sparse_mla_attn(dp.batch, dp.q_nope, dp.q_rope, dp.kv, dp.w_uk, dp.w_uv, ti, out_dtype=torch.float32)
+    assert torch.isfinite(op).all()
+    assert torch.equal(oc, op)
+    out = op.cpu().numpy()
+    for t in (0, 1, T // 2, T - 1):
+        b = int(inp.q_seq[t])
+        r0 = int(inp.seq_row0[b])
+        kept = idx[t][idx[t] >= 0].astype(np.int64)
+        ref = O.mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept], inp.w_uk, inp.w_uv)
+        mx, rel = out_errors(out[t], ref)
+        assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2, (t, mx, rel)
+    fc, ic = run_forward(dc)
+    fp, ip = run_forward(dp)
+    assert torch.equal(ic, ip) and torch.equal(fc, fp)

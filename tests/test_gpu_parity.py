@@ -260,6 +260,45 @@ def test_sparse_mla_absent_entries_and_order():
     assert np.abs(outb.float().cpu().numpy() - ref16).max() <= 2 ** -7 * np.abs(out).max()
 
 
+# One-split batches (more than 16 queries with one key split each: the
+# warp-specialised core): ragged tile counts, tiny k, -1 entries anywhere and
+# unsorted rows, a query with no entry, two sequences.
+ONE_SPLIT_CASES = {
+    "k7_one_ragged_tile": (([900], [(0, 700 + 5 * i) for i in range(40)]), 7),
+    "k33_two_tiles": (([1500, 800], [(i % 2, 500 + i) for i in range(260)]), 33),
+    "k100_absent_unsorted": (([1400], [(0, 1000 + i) for i in range(300)]), 100),
+}
+
+
+@pytest.mark.parametrize("case", list(ONE_SPLIT_CASES))
+def test_sparse_mla_one_split_edge_cases(case):
+    (lens, qs), k = ONE_SPLIT_CASES[case]
+    _say(f"[sparse_mla one split] {case} k={k}")
+    inp = synth.custom(lens, qs, seed=43)
+    T = len(qs)
+    rng = np.random.default_rng(7)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = int(inp.q_pos[t]) + 1
+        m = int(rng.integers(1, k + 1))  # entries kept, the rest -1
+        sel = rng.choice(n, min(m, n), replace=False).astype(np.int32)
+        row = np.concatenate([sel, np.full(k - len(sel), -1, np.int32)])
+        idx[t] = rng.permutation(row) if t % 2 else row
+    idx[T // 3, :] = -1  # no entry: zeros
+    d = to_device(inp)
+    out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv,
+                                  torch.from_numpy(idx).cuda(), out_dtype=torch.float32).cpu().numpy()
+    assert np.all(out[T // 3] == 0.0)
+    worst_mx = worst_rel = 0.0
+    for t in range(0, T, max(1, T // 24)):
+        if t == T // 3:
+            continue
+        mx, rel = out_errors(out[t], _oracle_out(inp, t, idx[t]))
+        worst_mx, worst_rel = max(worst_mx, mx), max(worst_rel, rel)
+    _say(f"  max-abs {worst_mx:.2e} rel-L2 {worst_rel:.2e}")
+    assert worst_mx <= OUT_MAX_ABS and worst_rel <= OUT_REL_L2
+
+
 # ------------------------------------------------------------------ end to end
 def _e2e(inp, sample, k=2048, ws=None, d=None):
     d = d if d is not None else to_device(inp)
