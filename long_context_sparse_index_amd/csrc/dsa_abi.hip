@@ -166,9 +166,9 @@ FwdPlan plan_forward(int32_t T, int32_t max_ctx, int32_t k, bool need_idx, bool 
 }
 
 // The chunk of T queries takes the candidate path: indexer GEMM with one
-// workgroup per query block over the whole context, contiguous caches.
+// workgroup per query block over the whole context.
 bool use_candidates(const dsa_batch* b, int32_t T, bool gemm) {
-  return gemm && b->page_size == 0 && dsa::gemm_whole_context(T, b->max_ctx);
+  return gemm && dsa::gemm_whole_context(T, b->max_ctx);
 }
 
 // The whole path over one workspace: query chunks sized to ws_bytes.

@@ -220,7 +220,6 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, CacheRows cr,
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ k_idx, GemmOut o, int T, int split_keys) {
-  static_assert(!(PAGED && MODE == kGemmSample), "sampled keys are read from contiguous caches");
   float* const scores = o.scores;
   const int64_t ld = o.ld;
   // two buffers as two arrays: with distinct objects the compiler sees that
@@ -301,19 +300,30 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     // PAGED: load i of a tile lies in granule (kGemmWaves i + wave) / 4 (16
     // keys, one page); the page ids of tile + 2 are loaded (into pv) while
     // tile is computed, and made scalar (pa, wave-uniform) once they have
-    // arrived.
+    // arrived.  kGemmSample: consecutive keys of a tile are positions R apart,
+    // so each lane loads the page of its own key's position (and keeps it).
+    constexpr bool kLanePages = PAGED && MODE == kGemmSample;
     auto pid_fetch = [&](int tile, int p[kGemmLoads]) {
 #pragma unroll
-      for (int c = 0; c < kGemmLoads; ++c)
-        p[c] = bt[min(kbeg + tile * kGemmKT + kGranule * ((kGemmWaves * c + wave) >> 2), hi) >> cr.page_shift];
+      for (int c = 0; c < kGemmLoads; ++c) {
+        if constexpr (kLanePages)
+          p[c] = bt[(min(kbeg + tile * kGemmKT + kDlStride * c + dl_row, hi) * o.stride) >> cr.page_shift];
+        else
+          p[c] = bt[min(kbeg + tile * kGemmKT + kGranule * ((kGemmWaves * c + wave) >> 2), hi) >> cr.page_shift];
+      }
+    };
+    auto page_ready = [&](int v) __attribute__((always_inline)) -> int {
+      if constexpr (kLanePages) return v;
+      return __builtin_amdgcn_readfirstlane(v);
     };
     auto dma = [&](int tile, const int p[kGemmLoads], uint16_t* buf) {
       const int base = kbeg + tile * kGemmKT;
 #pragma unroll
       for (int c = 0; c < kGemmLoads; ++c) {
         const int key = min(base + kDlStride * c + dl_row, hi);  // rows past hi: never stored
-        int64_t row = row0 + (MODE == kGemmSample ? (int64_t)key * o.stride : (int64_t)key);
-        if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (key & ((1 << cr.page_shift) - 1));
+        const int64_t pos = MODE == kGemmSample ? (int64_t)key * o.stride : (int64_t)key;
+        int64_t row = row0 + pos;
+        if (PAGED) row = ((int64_t)p[c] << cr.page_shift) | (pos & ((1 << cr.page_shift) - 1));
         // (named pointers: the host pass rejects cast expressions as this builtin's operands)
         const uint16_t* const gsrc = k_idx + row * kIdxDim + dl_chunk * 8;
         uint16_t* const dst = buf + (kGemmWaves * c + wave) * 512;
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
     if (PAGED && ntiles > 1) {
       pid_fetch(1, pv);
 #pragma unroll
-      for (int c = 0; c < kGemmLoads; ++c) pa[c] = __builtin_amdgcn_readfirstlane(pv[c]);
+      for (int c = 0; c < kGemmLoads; ++c) pa[c] = page_ready(pv[c]);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
     __syncthreads();
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(kGemmThreads) void idx_gemm_kernel(
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile + 1 are in LDS
       if (PAGED && tile + 2 < ntiles) {
 #pragma unroll
-        for (int c = 0; c < kGemmLoads; ++c) pa[c] = __builtin_amdgcn_readfirstlane(pv[c]);
+        for (int c = 0; c < kGemmLoads; ++c) pa[c] = page_ready(pv[c]);
       }
       __syncthreads();                      // ... and every wave's; every wave is done with cur
     };
@@ -489,8 +499,12 @@ hipError_t launch_index_sample(const LaunchBatch& b, const uint16_t* q_idx, cons
   o.scores = sample;
   o.ld = ld_s;
   o.stride = stride;
-  idx_gemm_kernel<false, kGemmSample><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx, o,
-                                                                     b.T, split_keys);
+  if (b.paged())
+    idx_gemm_kernel<true, kGemmSample><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx, o,
+                                                                      b.T, split_keys);
+  else
+    idx_gemm_kernel<false, kGemmSample><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w, k_idx, o,
+                                                                       b.T, split_keys);
   return hipGetLastError();
 }
 
@@ -505,9 +519,12 @@ hipError_t launch_index_candidates(const LaunchBatch& b, const uint16_t* q_idx, 
   o.cand = cand;
   o.cap = cap;
   o.cnt = cnt;
-  if (b.paged()) return hipErrorInvalidValue;  // the candidate path runs on contiguous caches
-  idx_gemm_kernel<false, kGemmCandidates><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w,
-                                                                          k_idx, o, b.T, split_keys);
+  if (b.paged())
+    idx_gemm_kernel<true, kGemmCandidates><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w,
+                                                                           k_idx, o, b.T, split_keys);
+  else
+    idx_gemm_kernel<false, kGemmCandidates><<<grid, kGemmThreads, 0, st>>>(b.q_seq, b.q_pos, b.rows, q_idx, w,
+                                                                            k_idx, o, b.T, split_keys);
   return hipGetLastError();
 }
 

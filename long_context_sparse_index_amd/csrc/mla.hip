@@ -937,24 +937,25 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // index row, or past k), which the gather's 24-bit offset multiply ignores
   // Paged: an entry is a pool row, complemented when absent; rows past k read
   // the entry at k (the complemented row of position 0).
+  // Every step issues the same number of loads (the step's waits count them):
+  // the index words are loaded unconditionally, at a clamped index, and the
+  // test for rows past k is applied where an entry is used (entry()), so the
+  // loaded words travel raw (a loop-carried value computed from a load makes
+  // the compiler wait for it at the loop edge).
   auto pos_load = [&](int u) __attribute__((always_inline)) -> int {
     const int j = u * kKT + (lane & 31);
-    if constexpr (PAGED) return irow[min(j, k)];
-    return j < k ? irow[min(j, k - 1)] : -1;
+    return irow[PAGED ? min(j, k) : max(min(j, k - 1), 0)];
   };
-  auto pos_entry = [&](int e) __attribute__((always_inline)) -> int {
-    if constexpr (PAGED) return e;
-    return e >= 0 ? e : kAbsent;
+  // the entry of tile u's row `row` from its raw index word
+  auto entry = [&](int raw, int u, int row) __attribute__((always_inline)) -> int {
+    if constexpr (PAGED) return raw;  // (rows past k read the entry at k)
+    return u * kKT + row < k && raw >= 0 ? raw : kAbsent;
   };
-  // QK waves: lane l also loads the entry of the rope row it gathers, 8 wr + l / 8
+  // QK waves: lane l also loads the index word of the rope row it gathers, 8 wr + l / 8
   const int rope_row = 8 * wr + (lane >> 3);
-  // (a load without a branch: inside one, the compiler computes the gather
-  // offset from the entry right after the load and waits for it there)
   auto rope_pos_load = [&](int u) __attribute__((always_inline)) -> int {
     const int j = u * kKT + rope_row;
-    if constexpr (PAGED) return irow[min(j, k)];
-    const int v = irow[max(min(j, k - 1), 0)];
-    return j < k ? v : -1;
+    return irow[PAGED ? min(j, k) : max(min(j, k - 1), 0)];
   };
   const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
   const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
@@ -967,13 +968,14 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) voff[q] = (uint32_t)((lane ^ ws_swz(wave + 8 * q)) * 16);
   const uint32_t rope_colb = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ ((rope_row >> 1) & 7)) * 16);
-  // gather of a tile into ring slot dst from its entries pe (and pr, the rope
-  // row entries of a QK wave; pos_entry applied)
-  auto gather = [&](int pe, int pr, uint16_t* dst, int bslot) __attribute__((always_inline)) {
+  // gather of tile u into ring slot dst from the raw index words of its rows
+  // (pw, and rw for the rope rows of a QK wave); a latent row's entry is made
+  // in scalar registers after the readlane
+  auto gather = [&](int pw, int rw, int u, uint16_t* dst, int bslot) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = wave + 8 * q;
-      const int e = __builtin_amdgcn_readlane(pe, r);
+      const int e = entry(__builtin_amdgcn_readlane(pw, r), u, r);
       uint16_t* const d = dst + r * kWsLat * 8;
       if constexpr (PAGED) {
         // a resource based at the row: a pool may pass 2^32 bytes
@@ -988,11 +990,13 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     if (qk) {
       if constexpr (!PAGED) {  // (paged: rope_fetch / rope_store)
         uint16_t* const d = dst + (kWsRope0 + 64 * wr) * 8;
+        const int pr = entry(rw, u, rope_row);
         const uint32_t off = (uint32_t)(pr & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, d, 16, off, 0, 0, 0);
       }
       // key biases of the tile (0 present, -inf absent), wave 0
       if (wave == 0 && lane < kKT) {
+        const int pe = entry(pw, u, lane);
         const float bias = (PAGED ? pe >= 0 : (pe & kAbsent) == 0) ? 0.f : -INFINITY;
         asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(&s_bias[bslot][lane])), "v"(bias) : "memory");
       }
@@ -1147,43 +1151,40 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     int pe_next, pr_next = 0, pr_next2 = 0;
     u32x4 rope_cur = {0u, 0u, 0u, 0u};  // paged QK waves: rope of the tile after the next
     {
-      const int e0 = pos_entry(pos_load(0));
-      const int e1 = pos_entry(pos_load(1));
+      const int e0 = pos_load(0), e1 = pos_load(1);  // (raw words)
       int r0 = 0, r1 = 0;
       u32x4 rope0 = {0u, 0u, 0u, 0u};
       if constexpr (kQk) {
-        r0 = pos_entry(rope_pos_load(0));
-        r1 = pos_entry(rope_pos_load(1));
+        r0 = rope_pos_load(0);
+        r1 = rope_pos_load(1);
         pr_next = rope_pos_load(2);
         pr_next2 = rope_pos_load(3);
         if constexpr (PAGED) {
-          rope0 = rope_fetch(r0);
-          rope_cur = rope_fetch(r1);
+          rope0 = rope_fetch(entry(r0, 0, rope_row));
+          rope_cur = rope_fetch(entry(r1, 1, rope_row));
         }
       }
       pe_next = pos_load(2);
-      gather(e0, r0, tile0, 0);
-      gather(e1, r1, tile1, 1);
+      gather(e0, r0, 0, tile0, 0);
+      gather(e1, r1, 1, tile1, 1);
       __builtin_amdgcn_s_waitcnt(0);  // (both tiles, the query operands and the next positions)
       if constexpr (PAGED && kQk) rope_store(tile0, rope0);
     }
     lds_barrier();
     auto step = [&](int i, auto BC, auto PVC) __attribute__((always_inline)) {
       constexpr int b = decltype(BC)::value;
-      // (entries travel raw and get pos_entry here: a loop-carried value
-      // computed from a load makes the compiler wait for it at the loop edge)
-      const int pe = pos_entry(pe_next), pr = pos_entry(pr_next);
+      const int pw = pe_next, rw = pr_next;  // (raw words of tile i + 2)
       pe_next = pos_load(i + 3);
       u32x4 rope_next = {0u, 0u, 0u, 0u};
       if constexpr (kQk) {
         pr_next = pr_next2;
         pr_next2 = rope_pos_load(i + 4);
-        if constexpr (PAGED) rope_next = rope_fetch(pr);  // (tile i + 2; in place of its rope DMA)
+        if constexpr (PAGED) rope_next = rope_fetch(entry(rw, i + 2, rope_row));  // (in place of its rope DMA)
       }
       // the position loads go out before the gathers: the waits for them count
       // only older loads
       __builtin_amdgcn_sched_barrier(0);
-      gather(pe, pr, slot((b + 2) % 4), (b + 2) % 4);
+      gather(pw, rw, i + 2, slot((b + 2) % 4), (b + 2) % 4);
       work(i, BC, PVC);
       if constexpr (PAGED && kQk) {
         rope_store(slot((b + 1) % 4), rope_cur);  // tile i + 1, published by this step's barrier

@@ -150,3 +150,43 @@ def test_paged_one_split_equals_contiguous(page_size):
     fc, ic = run_forward(dc)
     fp, ip = run_forward(dp)
     assert torch.equal(ic, ip) and torch.equal(fc, fp)
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_paged_candidate_path_equals_contiguous(page_size):
+    """A chunk whose query blocks fill the chip takes the candidate path (sampled
+    scores read through the block table one page per sampled key, thresholds,
+    candidate GEMM, candidate top-k) on paged caches too: bit-identical to the
+    contiguous layout."""
+    _say(f"[paged candidates] page_size={page_size}")
+    inp = synth.custom([6000], [(0, 1904 + i) for i in range(4096)], seed=54)
+    pc = synth.to_paged(inp, page_size, seed=page_size + 2)
+    dc = to_device(inp)
+    dp = to_device_paged(inp, pc, dc)
+    oc, ic = run_forward(dc)
+    op, ip = run_forward(dp)
+    assert torch.equal(ic, ip)
+    assert torch.equal(oc, op)
+    assert torch.isfinite(op).all()
+    torch.cuda.synchronize()
+    out, idx = op.cpu().numpy(), ip.cpu().numpy()
+    for t in (0, 2047, 4095):
+        _oracle_check(inp, t, idx[t], out[t], 2048)
+
+
+def test_paged_full_size_prefill_sampled():
+    """prefill_chunk4096_ctx204k with 64-token pages (the benchmark's paged
+    prefill): identical to the contiguous layout, sampled queries against the
+    oracle."""
+    _say("[paged full] prefill_chunk4096_ctx204k: generating inputs")
+    inp = synth.make_inputs(synth.workload("prefill_chunk4096_ctx204k"))
+    pc = synth.to_paged(inp, 64, seed=65)
+    dc = to_device(inp)
+    dp = to_device_paged(inp, pc, dc)
+    oc, ic = run_forward(dc)
+    op, ip = run_forward(dp)
+    assert torch.equal(ic, ip) and torch.equal(oc, op)
+    torch.cuda.synchronize()
+    out, idx = op.cpu().numpy(), ip.cpu().numpy()
+    for t in (0, 4095):
+        _oracle_check(inp, t, idx[t], out[t], 2048)

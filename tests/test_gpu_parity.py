@@ -490,3 +490,20 @@ def test_sparse_mla_large_latent_over_key_splits():
         mx, rel = out_errors(out[t], ref)
         _say(f"  t={t} max-abs {mx:.3e} (max |ref| {np.abs(ref).max():.3e}) rel-L2 {rel:.2e}")
         assert rel <= OUT_REL_L2 and mx <= OUT_MAX_ABS * np.abs(ref).max()
+
+
+def test_sparse_mla_one_split_repeatable():
+    """The one-split core gives bit-identical outputs on repeated calls at the
+    benchmark's prefill size (4,096 queries x 2,048 rows, 64 key tiles each).
+    Regression: steps past a query's last tile once issued fewer loads than the
+    step's wait counted, so an in-flight gather of a real tile could be read
+    early (a few queries per call differed)."""
+    _say("[sparse_mla repeat] prefill_chunk4096_ctx204k")
+    inp = synth.make_inputs(synth.workload("prefill_chunk4096_ctx204k"))
+    d = to_device(inp)
+    _, idx = run_forward(d)
+    outs = [dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv, idx, out_dtype=torch.float32)
+            for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
