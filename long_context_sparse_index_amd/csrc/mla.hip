@@ -942,9 +942,22 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
   // test for rows past k is applied where an entry is used (entry()), so the
   // loaded words travel raw (a loop-carried value computed from a load makes
   // the compiler wait for it at the loop edge).
+  // Contiguous: the index row read as a buffer of k words, whose loads past
+  // the end return 0 (rows that entry() makes absent), at a lane offset made
+  // afresh at each load: a lane number kept live across the step loop has
+  // been spilled there, and its reload at the loop edge waited for every
+  // gather in flight.
+  const __amdgpu_buffer_rsrc_t irow_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(irow), (short)0, PAGED ? 0 : k * 4, kBufferWord3);
   auto pos_load = [&](int u) __attribute__((always_inline)) -> int {
-    const int j = u * kKT + (lane & 31);
-    return irow[PAGED ? min(j, k) : max(min(j, k - 1), 0)];
+    if constexpr (PAGED) {
+      const int j = u * kKT + (lane & 31);
+      return irow[min(j, k)];
+    } else {
+      uint32_t l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      return (int)__builtin_amdgcn_raw_buffer_load_b32(irow_rsrc, (l & 31) * 4, u * kKT * 4, 0);
+    }
   };
   // the entry of tile u's row `row` from its raw index word
   auto entry = [&](int raw, int u, int row) __attribute__((always_inline)) -> int {
@@ -1196,12 +1209,17 @@ __global__ __launch_bounds__(kCoreThreads) void mla_ws_kernel(
     };
     using Yes = std::integral_constant<bool, true>;
     step(0, std::integral_constant<int, 0>{}, std::integral_constant<bool, false>{});
-    for (int i = 1; i <= ntiles; i += 4) {
+    // (k >= 1, so there is a tile 1 to take; a loop with an entry test had the
+    // compiler sink step 0's position load past its gathers into that test,
+    // and the loop head then waited for the gathers of the step before it)
+    int i = 1;
+    do {
       step(i, std::integral_constant<int, 1>{}, Yes{});
       step(i + 1, std::integral_constant<int, 2>{}, Yes{});
       step(i + 2, std::integral_constant<int, 3>{}, Yes{});
       step(i + 3, std::integral_constant<int, 0>{}, Yes{});
-    }
+      i += 4;
+    } while (i <= ntiles);
     __builtin_amdgcn_s_waitcnt(0);  // no gather may still target this workgroup's LDS at exit
   };
 
