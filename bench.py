@@ -353,8 +353,8 @@ def other_config(name, kind, steps, warmup):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-index-share", action="store_true", help="skip the IndexShare layer-group measurement")
     ap.add_argument("--no-topk-variants", action="store_true",
@@ -456,7 +456,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     del inp
     if not args.no_prefill:
-        pinp, pms, pops, pre_k = run_workload(PREFILL, max(10, args.steps // 2), max(3, min(args.warmup, 5)),
+        pre_steps, pre_warmup = max(10, min(args.steps // 2, 25)), max(3, min(args.warmup, 5))
+        pinp, pms, pops, pre_k = run_workload(PREFILL, pre_steps, pre_warmup,
                                               extra_k=extra_k[-1:], page_size=PAGE)
         pre_paged = pre_k.pop("paged")
         pre_int4 = pre_k.pop("int4")
@@ -464,7 +465,7 @@ def main():
         pach = palg["index_flops"] / (pops["index_scores"] * 1e-3) / 1e12
         result["prefill"] = {
             "workload": PREFILL, "value": len(pinp.q_pos) / (pms * 1e-3), "unit": "query-tokens/s",
-            "ms_per_step": pms, "ops_ms": pops,
+            "ms_per_step": pms, "steps": pre_steps, "warmup": pre_warmup, "ops_ms": pops,
             "index_topk_variants": {str(k): {"ms_per_step": v, "value": len(pinp.q_pos) / (v * 1e-3),
                                              "unit": "query-tokens/s"} for k, v in pre_k.items()},
             "paged": {"page_size": PAGE, "ms_per_step": pre_paged, "value": len(pinp.q_pos) / (pre_paged * 1e-3),
@@ -485,7 +486,7 @@ def main():
             result["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pinp, args.cpu_budget)
         del pinp
     if not args.no_other_configs:
-        result["other_configs"] = [other_config(n, kind, max(5, args.steps // 4), 2) for n, kind in OTHER_CONFIGS]
+        result["other_configs"] = [other_config(n, kind, max(5, min(args.steps // 4, 12)), 2) for n, kind in OTHER_CONFIGS]
     print(json.dumps(result), flush=True)
 
 
