@@ -152,6 +152,41 @@ def test_paged_one_split_equals_contiguous(page_size):
     assert torch.equal(ic, ip) and torch.equal(fc, fp)
 
 
+def test_paged_one_split_at_index_topk_8192():
+    """The warp-specialised core on 16-token pages at k 8192 (the largest index
+    row, its entries and the row past k filling most of each query's entries
+    area): ragged rows with -1 entries, bit-identical to the contiguous layout,
+    and the oracle on four queries."""
+    lens, qs = [12000, 9500], [(i % 2, 9000 + i) for i in range(260)]
+    _say("[paged one split] k=8192 page_size=16")
+    inp = synth.custom(lens, qs, seed=59)
+    pc = synth.to_paged(inp, 16, seed=61)
+    dc = to_device(inp)
+    dp = to_device_paged(inp, pc, dc)
+    rng = np.random.default_rng(7)
+    k = 8192
+    T = len(qs)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = int(inp.q_pos[t]) + 1
+        m = int(rng.integers(k - 300, k + 1)) if t % 3 else int(rng.integers(1, k + 1))
+        row = np.concatenate([rng.choice(n, m, replace=False).astype(np.int32), np.full(k - m, -1, np.int32)])
+        idx[t] = np.sort(row) if t % 2 else rng.permutation(row)
+    ti = torch.from_numpy(idx).cuda()
+    oc = dsa.dsa_sparse_mla_attn(dc.batch, dc.q_nope, dc.q_rope, dc.kv, dc.w_uk, dc.w_uv, ti, out_dtype=torch.float32)
+    op = dsa.dsa_sparse_mla_attn(dp.batch, dp.q_nope, dp.q_rope, dp.kv, dp.w_uk, dp.w_uv, ti, out_dtype=torch.float32)
+    assert torch.isfinite(op).all()
+    assert torch.equal(oc, op)
+    out = op.cpu().numpy()
+    for t in (0, 1, T // 2, T - 1):
+        b = int(inp.q_seq[t])
+        r0 = int(inp.seq_row0[b])
+        kept = idx[t][idx[t] >= 0].astype(np.int64)
+        ref = O.mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept], inp.w_uk, inp.w_uv)
+        mx, rel = out_errors(out[t], ref)
+        assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2, (t, mx, rel)
+
+
 @pytest.mark.parametrize("page_size", [16, 64])
 def test_paged_candidate_path_equals_contiguous(page_size):
     """A chunk whose query blocks fill the chip takes the candidate path (sampled
