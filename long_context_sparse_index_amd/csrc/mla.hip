@@ -552,27 +552,45 @@ __device__ __forceinline__ f32x4 mfma16k16(v4i16 a, v4i16 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-template <bool PAGED>
+template <bool PAGED, int NS>
 __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_decode_kernel(
     const int32_t* __restrict__ q_seq, CacheRows cr, const uint16_t* __restrict__ q_lat,
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int T, int k, float scale_log2, int kps, int S, uint16_t* __restrict__ o_lat,
     uint16_t* __restrict__ o_part, float* __restrict__ ml_part) {
-  // Two distinct slot arrays (not one indexed array): the compiler then waits
-  // only for the direct-to-LDS loads that target the array being read.
-  __shared__ __attribute__((aligned(16))) uint16_t slot0[kDecWaves][kDecTileSlots * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t slot1[kDecWaves][kDecTileSlots * 8];
-  __shared__ __attribute__((aligned(16))) int s_idx[kDecMaxKps + kDecPadTiles * kDecKT];
+  // NS = 0: per-wave rings (above).  NS = 1..4, the paired form: a workgroup
+  // covers 32 heads (two head groups) and a split of 32*NS keys, the 2*NS
+  // tiles of which are all gathered at once; wave (hs, st) = (wave % 2,
+  // wave / 2) computes head group 2*hh + hs over the tiles st, st + 2, ... of
+  // the split, and the two waves of a stream st gather half of each of its
+  // tiles (rows 8hs .. 8hs+7 and rope load hs), so every gathered row serves
+  // 32 heads and a split's rows reach LDS in one round.
+  constexpr bool kPair = NS > 0;
+  static_assert(NS >= 0 && NS <= 4, "paired form: at most 4 steps (8 tiles)");
+  // Distinct slot arrays (not one indexed array): the compiler then waits
+  // only for the direct-to-LDS loads that target the array being read.  Ring
+  // form: slotN[w] is wave w's slot N; paired form: slotN[st] is step N's tile
+  // of stream st.
+  constexpr int kSlotRows = kPair ? 2 : kDecWaves;
+  constexpr int kXSlots = kPair ? kDecTileSlots * 8 : 8;  // (slots 2, 3: paired form only)
+  __shared__ __attribute__((aligned(16))) uint16_t slot0[kSlotRows][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot1[kSlotRows][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot2[2][kXSlots];
+  __shared__ __attribute__((aligned(16))) uint16_t slot3[2][kXSlots];
+  __shared__ __attribute__((aligned(16))) int s_idx[kPair ? 32 * NS : kDecMaxKps + kDecPadTiles * kDecKT];
   __shared__ float s_ml[kDecWaves][kDecHeads][2];
-  // block id -> (query, split) pair P and head group: ids 32a + 8hg + r hold
-  // pair 8a + r, so the four head groups of a pair are equal modulo 8
+  // block id -> (query, split) pair P and head group.  Ring form: ids 32a +
+  // 8hg + r hold pair 8a + r, so the four head groups of a pair are equal
+  // modulo 8 (one XCD, one L2); paired form: ids 16a + 8hh + r hold pair 8a +
+  // r, head groups 2hh and 2hh + 1.
   const int id = blockIdx.x;
-  const int P = (id >> 5) * 8 + (id & 7);
-  const int hg = (id >> 3) & 3;
+  const int P = kPair ? (id >> 4) * 8 + (id & 7) : (id >> 5) * 8 + (id & 7);
   if (P >= T * S) return;  // (whole workgroup)
   const int t = P / S, sp = P - t * S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave & 1, st = wave >> 1;  // (paired form)
+  const int hg = kPair ? 2 * ((id >> 3) & 1) + hs : (id >> 3) & 3;
   const int l16 = lane & 15, g = lane >> 4;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
@@ -586,8 +604,9 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   // positions, an absent one position 0 with kAbsent set; paged entries are
   // pool rows, an absent one ~row of position 0), padded to whole tiles.
   {
-    constexpr int kPer = (kDecMaxKps + kDecPadTiles * kDecKT + kDecWaves * 64 - 1) / (kDecWaves * 64);
-    const int nfill = (ntiles + kDecPadTiles) * kDecKT;
+    constexpr int kFill = kPair ? 32 * NS : kDecMaxKps + kDecPadTiles * kDecKT;
+    constexpr int kPer = (kFill + kDecWaves * 64 - 1) / (kDecWaves * 64);
+    const int nfill = kPair ? kFill : (ntiles + kDecPadTiles) * kDecKT;
     int v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -689,6 +708,46 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     return pmask;
   };
 
+  // Paired form: half hs of tile u of the split (rows 8hs .. 8hs+7, as in
+  // gather, and rope load hs); returns the mask of the tile's present rows.
+  auto gather_half = [&](int u, uint16_t* dstt) __attribute__((always_inline)) -> uint32_t {
+    int pv;
+    {
+      const __attribute__((address_space(3))) int* const a =
+          (const __attribute__((address_space(3))) int*)(&s_idx[u * kDecKT + l16]);
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(pv) : "v"(a) : "memory");
+    }
+    const bool present = PAGED ? pv >= 0 : (pv & kAbsent) == 0;
+    const uint32_t pmask = (uint32_t)__ballot(present) & 0xFFFFu;
+    const int rb = 8 * hs;  // (wave-uniform)
+    const int prh = __shfl(pv, rope_r0 + rb, 64);
+    const uint32_t voff = hs ? voff_hi : voff_lo;
+#pragma unroll
+    for (int i = 0; i < kDecKT / 2; ++i) {
+      uint16_t* const dst = dstt + (rb + i) * kDecLatStride * 8;
+      const int e = __builtin_amdgcn_readlane(pv, rb + i);
+      if (PAGED) {
+        const int r = e >= 0 ? e : ~e;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kv_u + (int64_t)r * kRow), (short)0, (int)0xFFFFFFFF, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+      } else {
+        const int soff = (e & 0xFFFFFF) * (kRow * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dst, 16, voff, soff, 0, 0);
+      }
+    }
+    uint16_t* const drh = dstt + (kDecRopeSlot0 + 64 * hs) * 8;
+    const uint32_t colb = hs ? rope_colb1 : rope_colb;
+    if (PAGED) {
+      const int r = prh >= 0 ? prh : ~prh;
+      __builtin_amdgcn_global_load_lds(kv_u + (int64_t)r * kRow + colb / 2, drh, 16, 0, 0);
+    } else {
+      const uint32_t o = (uint32_t)(prh & 0xFFFFFF) * (uint32_t)(kRow * 2) + colb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, drh, 16, o, 0, 0, 0);
+    }
+    return pmask;
+  };
+
   // per-lane LDS offsets (bf16 elements) of chunk g of row l16 (QK) and of
   // chunk (l16 % 4) / 2, half l16 % 2 of row 4g + l16 / 4 (PV)
   const int qk_base = dec_lat_slot(l16, g) * 8;
@@ -750,41 +809,72 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  uint16_t* const my0 = slot0[wave];
-  uint16_t* const my1 = slot1[wave];
-  // Step v computes tile v from slot v % 2 once this wave's loads of it are
-  // in (its loads of tile v + 1 may still be in flight), then gathers tile
-  // v + 2 into that slot once the wave's reads of it are complete.  The loop
-  // body has no branch (the compiler then keeps track of which slot a wait is
-  // for): a wave runs an even number of steps and gathers two tiles past its
-  // last; those tiles hold absent entries (position 0's row, masked), and an
-  // odd count's last step computes such a tile to no effect.
-  uint32_t pm0, pm1;  // present rows of the tiles in slot 0 and 1
-  auto step = [&](int v, auto BUFC) __attribute__((always_inline)) {
-    constexpr int buf = decltype(BUFC)::value;
-    uint32_t& pm = buf == 0 ? pm0 : pm1;
-    wait_vm_wide<kDecLoads>();
-    compute(buf == 0 ? my0 : my1, pm);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    pm = gather(v + 2, buf == 0 ? my0 : my1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  const int nsteps = (ntw + 1) & ~1;
-  pm0 = gather(0, my0);
-  pm1 = gather(1, my1);
-  // the query operand loads (issued before the gathers) are complete here;
-  // marking them consumed keeps the compiler from waiting for every gather
-  // before the loop
+  if constexpr (!kPair) {
+    uint16_t* const my0 = slot0[wave];
+    uint16_t* const my1 = slot1[wave];
+    // Step v computes tile v from slot v % 2 once this wave's loads of it are
+    // in (its loads of tile v + 1 may still be in flight), then gathers tile
+    // v + 2 into that slot once the wave's reads of it are complete.  The loop
+    // body has no branch (the compiler then keeps track of which slot a wait is
+    // for): a wave runs an even number of steps and gathers two tiles past its
+    // last; those tiles hold absent entries (position 0's row, masked), and an
+    // odd count's last step computes such a tile to no effect.
+    uint32_t pm0, pm1;  // present rows of the tiles in slot 0 and 1
+    auto step = [&](int v, auto BUFC) __attribute__((always_inline)) {
+      constexpr int buf = decltype(BUFC)::value;
+      uint32_t& pm = buf == 0 ? pm0 : pm1;
+      wait_vm_wide<kDecLoads>();
+      compute(buf == 0 ? my0 : my1, pm);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      pm = gather(v + 2, buf == 0 ? my0 : my1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const int nsteps = (ntw + 1) & ~1;
+    pm0 = gather(0, my0);
+    pm1 = gather(1, my1);
+    // the query operand loads (issued before the gathers) are complete here;
+    // marking them consumed keeps the compiler from waiting for every gather
+    // before the loop
+  #pragma unroll
+    for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
+    for (int v = 0; v < nsteps; v += 2) {
+      step(v, std::integral_constant<int, 0>{});
+      step(v + 1, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // (the two gathers past the last step)
+  } else {
+    // Paired form: half of each of this stream's NS tiles, all in flight at
+    // once (9 loads per half tile); before step v the wave waits for its
+    // halves of tiles up to v, and the barrier makes the other wave's halves
+    // visible too.
+    auto arr = [&](int v) __attribute__((always_inline)) -> uint16_t* {
+      return v == 0 ? slot0[st] : v == 1 ? slot1[st] : v == 2 ? slot2[st] : slot3[st];
+    };
+    uint32_t pmv[NS];
 #pragma unroll
-  for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
-  for (int v = 0; v < nsteps; v += 2) {
-    step(v, std::integral_constant<int, 0>{});
-    step(v + 1, std::integral_constant<int, 1>{});
+    for (int v = 0; v < NS; ++v) pmv[v] = gather_half(st + 2 * v, arr(v));
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
+    auto pstep = [&](auto VC) __attribute__((always_inline)) {
+      constexpr int v = decltype(VC)::value;
+      if constexpr (v < NS) {
+        wait_vm_wide<(NS - 1 - v) * (kDecKT / 2 + 1)>();
+        lds_barrier();
+        compute(arr(v), pmv[v]);
+      }
+    };
+    pstep(std::integral_constant<int, 0>{});
+    pstep(std::integral_constant<int, 1>{});
+    pstep(std::integral_constant<int, 2>{});
+    pstep(std::integral_constant<int, 3>{});
   }
-  __builtin_amdgcn_s_waitcnt(0);  // (the two gathers past the last step)
 
-  // ---- the four waves' partial results: reference maxima and sums meet in
-  // LDS, then each wave adds up 8 latent blocks (128 dims) of all four
+  // ---- the waves' partial results of a head group (ring form: all four;
+  // paired form: the two streams of head group 2hh + hs): reference maxima and
+  // sums meet in LDS, then each wave adds up its share of the 32 latent
+  // blocks of 16 dims over those waves
+  constexpr int kComb = kPair ? 2 : kDecWaves;
+  auto cw = [&](int c) __attribute__((always_inline)) { return kPair ? hs + 2 * c : c; };
   const float l_sum = rows_sum(l_part);
   if (g == 0) {
     s_ml[wave][l16][0] = m_ref;
@@ -793,16 +883,21 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();  // (also: every wave is done with its slots)
   float mstar = -1e30f;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) mstar = fmaxf(mstar, s_ml[w][l16][0]);
+  for (int c = 0; c < kComb; ++c) mstar = fmaxf(mstar, s_ml[cw(c)][l16][0]);
   float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) L += __builtin_amdgcn_exp2f(s_ml[w][l16][0] - mstar) * s_ml[w][l16][1];
+  for (int c = 0; c < kComb; ++c) L += __builtin_amdgcn_exp2f(s_ml[cw(c)][l16][0] - mstar) * s_ml[cw(c)][l16][1];
   const float wgt = __builtin_amdgcn_exp2f(m_ref - mstar);
-  // wave w's scaled o goes to [32 blocks][64 lanes] of f32x4 (32 KB): waves
-  // 0, 1 in slot0, waves 2, 3 in slot1
-  static_assert(sizeof(slot0) >= 2 * 32 * 64 * sizeof(f32x4), "reduction area");
+  // wave w's scaled o goes to [32 blocks][64 lanes] of f32x4 (32 KB): ring
+  // form, waves 0, 1 in slot0 and waves 2, 3 in slot1; paired form, wave w in
+  // slot w
+  static_assert(sizeof(slot0) >= (kPair ? 1 : 2) * 32 * 64 * sizeof(f32x4), "reduction area");
   auto red = [&](int w) __attribute__((always_inline)) -> f32x4* {
-    return reinterpret_cast<f32x4*>(w < 2 ? &slot0[0][0] : &slot1[0][0]) + (w & 1) * 32 * 64;
+    if constexpr (kPair)
+      return reinterpret_cast<f32x4*>(w == 0 ? &slot0[0][0] : w == 1 ? &slot1[0][0] : w == 2 ? &slot2[0][0]
+                                                                                            : &slot3[0][0]);
+    else
+      return reinterpret_cast<f32x4*>(w < 2 ? &slot0[0][0] : &slot1[0][0]) + (w & 1) * 32 * 64;
   };
   {
     f32x4* const mine = red(wave);
@@ -811,12 +906,13 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
   __syncthreads();
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  constexpr int kBlocks = 32 / kComb;  // blocks per wave: ring 8, paired 16
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    const int b = 8 * wave + bb;
-    f32x4 sum = red(0)[b * 64 + lane];
+  for (int bb = 0; bb < kBlocks; ++bb) {
+    const int b = kBlocks * (kPair ? st : wave) + bb;
+    f32x4 sum = red(cw(0))[b * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) sum += red(w)[b * 64 + lane];
+    for (int c = 1; c < kComb; ++c) sum += red(cw(c))[b * 64 + lane];
     sum *= inv;
     if (S == 1) {
       *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + hq) * kLat + 16 * b + 4 * g) =
@@ -828,7 +924,7 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
           u32x2{cvt_pk_bf16(sum[0], sum[1]), cvt_pk_bf16(sum[2], sum[3])};
     }
   }
-  if (S > 1 && wave == 0 && g == 0) {
+  if (S > 1 && (kPair ? st : wave) == 0 && g == 0) {
     const int64_t base = ((int64_t)t * S + sp) * kHeads + hq;
     ml_part[base * 2] = mstar;
     ml_part[base * 2 + 1] = L;
@@ -1570,6 +1666,16 @@ __global__ __launch_bounds__(512) void head_gemm_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------- plan + launch
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Steps per stream of the paired decode core (32 heads per workgroup, about
+// 256 workgroups) for a decode batch of T queries at top-k k, when its splits
+// need at most 4 steps of two 16-key tiles; 0: the per-wave rings.
+static int dec_pair_steps(int T, int k) {
+  const int sp = (128 + T - 1) / T;
+  const int pk = (k + sp - 1) / sp;
+  const int ns = (pk + 2 * kDecKT - 1) / (2 * kDecKT);
+  return ns <= 4 ? ns : 0;
+}
+
 MlaPlan plan_mla(int T, int k) {
   MlaPlan p{};
   p.T = T;
@@ -1587,16 +1693,23 @@ MlaPlan plan_mla(int T, int k) {
   kps = (kps + kKT - 1) / kKT * kKT;
   p.keys_per_split = kps;
   p.splits = (k + kps - 1) / kps;
-  // Decode core: about 256 workgroups of (query, 16 heads, split), splits of
-  // whole 64-key rounds (16 keys per wave) and at most kDecMaxKps keys.
+  // Decode core: the paired form where it applies, else about 256 workgroups
+  // of (query, 16 heads, split), splits of whole 64-key rounds (16 keys per
+  // wave) and at most kDecMaxKps keys.
   p.dec = T > 0 && T <= kDecTMax;
   if (p.dec) {
-    const int s0 = (64 + T - 1) / T;
-    int dk = (k + s0 - 1) / s0;
-    dk = (dk + kDecKT * kDecWaves - 1) / (kDecKT * kDecWaves) * (kDecKT * kDecWaves);
-    dk = dk < kDecMaxKps ? dk : kDecMaxKps;
-    p.dec_keys_per_split = dk;
-    p.dec_splits = (k + dk - 1) / dk;
+    const int ns = dec_pair_steps(T, k);
+    if (ns > 0) {
+      p.dec_keys_per_split = 2 * kDecKT * ns;
+      p.dec_splits = (k + p.dec_keys_per_split - 1) / p.dec_keys_per_split;
+    } else {
+      const int s0 = (64 + T - 1) / T;
+      int dk = (k + s0 - 1) / s0;
+      dk = (dk + kDecKT * kDecWaves - 1) / (kDecKT * kDecWaves) * (kDecKT * kDecWaves);
+      dk = dk < kDecMaxKps ? dk : kDecMaxKps;
+      p.dec_keys_per_split = dk;
+      p.dec_splits = (k + dk - 1) / dk;
+    }
   }
   const int max_splits = p.dec && p.dec_splits > p.splits ? p.dec_splits : p.splits;
   const size_t lat = (size_t)T * kHeads * kLat * sizeof(uint16_t);
@@ -1645,15 +1758,31 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   const dim3 grid(T, p.splits);
   const int kps = p.keys_per_split;
   if (dec) {
-    const int dgrid = 32 * ((T * S + 7) / 8);
-    if (b.paged())
-      mla_decode_kernel<true><<<dgrid, kDecWaves * 64, 0, st>>>(
-          b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
-          p.dec_keys_per_split, S, o_lat, o_part, ml_part);
-    else
-      mla_decode_kernel<false><<<dgrid, kDecWaves * 64, 0, st>>>(
-          b.q_seq, b.rows, q_lat, q_rope, static_cast<const uint16_t*>(kv), idx, T, p.k, scale_log2,
-          p.dec_keys_per_split, S, o_lat, o_part, ml_part);
+    const int ns = dec_pair_steps(T, p.k);
+    const int dgrid = (ns ? 16 : 32) * ((T * S + 7) / 8);
+    const uint16_t* const kvb = static_cast<const uint16_t*>(kv);
+    const int dk = p.dec_keys_per_split;
+#define DSA_DEC_LAUNCH(PG, NS)                                                                       \
+  mla_decode_kernel<PG, NS><<<dgrid, kDecWaves * 64, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kvb, idx, T, \
+                                                               p.k, scale_log2, dk, S, o_lat, o_part, ml_part)
+    if (b.paged()) {
+      switch (ns) {
+        case 1: DSA_DEC_LAUNCH(true, 1); break;
+        case 2: DSA_DEC_LAUNCH(true, 2); break;
+        case 3: DSA_DEC_LAUNCH(true, 3); break;
+        case 4: DSA_DEC_LAUNCH(true, 4); break;
+        default: DSA_DEC_LAUNCH(true, 0); break;
+      }
+    } else {
+      switch (ns) {
+        case 1: DSA_DEC_LAUNCH(false, 1); break;
+        case 2: DSA_DEC_LAUNCH(false, 2); break;
+        case 3: DSA_DEC_LAUNCH(false, 3); break;
+        case 4: DSA_DEC_LAUNCH(false, 4); break;
+        default: DSA_DEC_LAUNCH(false, 0); break;
+      }
+    }
+#undef DSA_DEC_LAUNCH
   } else if (S == 1 && !b.kv_int4) {
     if (b.paged()) {
       int32_t* const entries = reinterpret_cast<int32_t*>(o_lat);
