@@ -88,6 +88,22 @@ def recorded_traffic(name):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
+def attn_op_roofline(alg, T, op_ms):
+    """The sparse-MLA op (dsa_sparse_mla_attn: absorption, core, split merge if
+    any, up-projection) against both peaks: algorithmic bytes (gathered rows,
+    both absorption weights, per-query q_nope/q_rope in and bf16 out) per HBM
+    peak, and algorithmic flops (the core's 139,264 per kept row plus the
+    absorption and up-projection) per bf16 MFMA peak."""
+    t = op_ms * 1e-3
+    nbytes = alg["gather_bytes"] + 64 * 512 * (192 + 256) * 2 + T * (64 * 192 * 2 + 64 * 64 * 2 + 64 * 256 * 2)
+    flops = alg["attn_flops"] + 2 * 64 * 512 * (192 + 256) * T
+    return {"launch": "dsa_sparse_mla_attn (absorption, core, split merge, up-projection)", "ms": op_ms,
+            "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / t / 1e9, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+            "gather_gbs": alg["gather_bytes"] / t / 1e9,
+            "algorithmic_flops": flops, "tflops": flops / t / 1e12,
+            "mfma_frac": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+
 def time_calls(fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -442,6 +458,7 @@ def main():
                                                            "timed region"),
                     "flushed_value": T / (dec_flushed["median"] * 1e-3)},
         "ops_ms": ops,
+        "attention_op": attn_op_roofline(alg, T, ops["sparse_mla"]),
         "index_topk_variants": {str(k): {"ms_per_step": v, "value": T / (v * 1e-3), "unit": "decode queries/s"}
                                 for k, v in dec_k.items()},
         "paged": {"page_size": PAGE, "ms_per_step": dec_paged, "value": T / (dec_paged * 1e-3),
@@ -466,6 +483,7 @@ def main():
         result["prefill"] = {
             "workload": PREFILL, "value": len(pinp.q_pos) / (pms * 1e-3), "unit": "query-tokens/s",
             "ms_per_step": pms, "steps": pre_steps, "warmup": pre_warmup, "ops_ms": pops,
+            "attention_op": attn_op_roofline(palg, len(pinp.q_pos), pops["sparse_mla"]),
             "index_topk_variants": {str(k): {"ms_per_step": v, "value": len(pinp.q_pos) / (v * 1e-3),
                                              "unit": "query-tokens/s"} for k, v in pre_k.items()},
             "paged": {"page_size": PAGE, "ms_per_step": pre_paged, "value": len(pinp.q_pos) / (pre_paged * 1e-3),
