@@ -918,9 +918,8 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
       *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + hq) * kLat + 16 * b + 4 * g) =
           u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
     } else {
-      // mla_merge_kernel's order: group ((w'*4 + head group)*4 + e)*64 + lane, b = 4w' + e
-      *reinterpret_cast<u32x2*>(o_part + ((int64_t)t * S + sp) * kPartSlab +
-                                ((((b >> 2) * 4 + hg) * 4 + (b & 3)) * 64 + lane) * 4) =
+      // head-major, as merge_upproj_kernel reads them: o_part[t][sp][h][512]
+      *reinterpret_cast<u32x2*>(o_part + ((int64_t)t * S + sp) * kPartSlab + (int64_t)hq * kLat + 16 * b + 4 * g) =
           u32x2{cvt_pk_bf16(sum[0], sum[1]), cvt_pk_bf16(sum[2], sum[3])};
     }
   }
@@ -1509,6 +1508,130 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- merge + upproj, decode
+// After the decode core (batches of up to 16 queries) with key splits: the
+// split merge and the V up-projection of one head as one launch.  grid (64
+// heads, 4 blocks of 64 output dims), 512 threads.  The decode core writes its
+// partials head-major (o_part[t][s][h][512], normalised by the split's own
+// sum) so that a head's are contiguous 1 KB rows.  Every load goes out before
+// any is used: the W_UV slice (64 KB), and per thread the rows of one
+// (query, 8-dim chunk) pair for the first 16 splits with their (m, l).  The
+// merged o_lat rows (bf16, as the separate merge stores them) form the A tile
+// [16 queries][512] in LDS; out[t][h][64 dims] = A . W_UV[h][:, block] by
+// 16x16x32 MFMAs, wave w taking dims 16(w % 4) .. +15 over half w / 4 of K.
+constexpr int kMuThreads = 512;
+static_assert(kDecTMax <= 16, "the A tile holds up to 16 queries");
+constexpr int kMuCh = 16;                  // splits requested at once
+constexpr int kMuARow = kLat + 8;          // A tile row (bf16, 16 B pad)
+
+__global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t* __restrict__ o_part,
+                                                                  const float* __restrict__ ml_part, int S,
+                                                                  const uint16_t* __restrict__ w_uv,
+                                                                  void* __restrict__ out, int out_f32, int T) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kUpEB * kWvLds];
+  __shared__ __attribute__((aligned(16))) uint16_t sa[16 * kMuARow];
+  __shared__ f32x4 red[4][64];
+  const int h = blockIdx.x, eb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // W_UV[h][c][64 eb .. +63]: unit u covers c = 4q .. 4q+3, e = 8r .. 8r+7
+  constexpr int kUnits = (kLat / 4) * (kUpEB / 8) / kMuThreads;
+  u32x4 rows[kUnits][4];
+#pragma unroll
+  for (int it = 0; it < kUnits; ++it) {
+    const int u = tid + kMuThreads * it;
+    const int q = u >> 3, r = u & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rows[it][i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
+  }
+  // merge: thread pairs (query t, chunk of 8 dims), tid + 512 i, i < 2
+  const int npairs = T * (kLat / 8);
+  for (int p0 = 0; p0 < npairs; p0 += kMuThreads) {
+    const int pr = p0 + tid;
+    const bool live = pr < npairs;
+    const int t = live ? pr >> 6 : 0, c8 = pr & 63;
+    const uint16_t* src = o_part + ((int64_t)t * S * kHeads + h) * kLat + 8 * c8;
+    const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
+    float mstar = -1e30f, L = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kMuCh) {
+      f32x2 m_l[kMuCh];
+      u32x4 v[kMuCh];
+#pragma unroll
+      for (int u = 0; u < kMuCh; ++u) {
+        const int sp = min(s0 + u, S - 1);  // past S: split S - 1 again, weight 0
+        m_l[u] = *reinterpret_cast<const f32x2*>(ml + (int64_t)sp * kHeads * 2);
+        v[u] = ld16(src + (int64_t)sp * kPartSlab);
+      }
+      float cm = mstar;
+#pragma unroll
+      for (int u = 0; u < kMuCh; ++u) cm = s0 + u < S ? fmaxf(cm, m_l[u][0]) : cm;
+      if (cm > mstar) {
+        const float sc = exp2f(mstar - cm);
+        L *= sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= sc;
+        mstar = cm;
+      }
+#pragma unroll
+      for (int u = 0; u < kMuCh; ++u) {
+        const float wgt = s0 + u < S ? exp2f(m_l[u][0] - mstar) * m_l[u][1] : 0.f;
+        L += wgt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += wgt * __uint_as_float(v[u][i] << 16);
+          acc[2 * i + 1] += wgt * __uint_as_float(v[u][i] & 0xFFFF0000u);
+        }
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (live)
+      *reinterpret_cast<u32x4*>(&sa[t * kMuARow + 8 * c8]) =
+          u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  }
+  // W_UV slice transposed into wt[e][c] (B operand: 8 consecutive c per lane)
+#pragma unroll
+  for (int it = 0; it < kUnits; ++it) {
+    const int u = tid + kMuThreads * it;
+    const int q = u >> 3, r = u & 7;
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
+      const int dw = e8 >> 1;
+      const u32x2 v = {__builtin_amdgcn_perm(rows[it][1][dw], rows[it][0][dw], sel),
+                       __builtin_amdgcn_perm(rows[it][3][dw], rows[it][2][dw], sel)};
+      *reinterpret_cast<u32x2*>(&wt[(8 * r + e8) * kWvLds + 4 * q]) = v;
+    }
+  }
+  __syncthreads();
+  // out rows 4g + i (queries), column l16 of dim block eblk
+  const int l16 = lane & 15, g = lane >> 4;
+  const int eblk = wave & 3, kh = wave >> 2;
+  const uint16_t* ap = &sa[l16 * kMuARow + kh * 256 + 8 * g];
+  const uint16_t* bp = &wt[(eblk * 16 + l16) * kWvLds + kh * 256 + 8 * g];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    acc = mfma16(as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 32 * ks)),
+                 as_bf16x8(*reinterpret_cast<const u32x4*>(bp + 32 * ks)), acc);
+  if (kh == 1) red[eblk][lane] = acc;
+  __syncthreads();
+  if (kh == 0) {
+    acc += red[eblk][lane];
+    const int e = eb * kUpEB + eblk * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+      if (t < T) {
+        const int64_t o = ((int64_t)t * kHeads + h) * kV + e;
+        if (out_f32) reinterpret_cast<float*>(out)[o] = acc[i];
+        else reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- upproj, many queries
 // W_UV[h] is [c][e] with e contiguous, while MFMA operands take 8 consecutive
 // c per lane.  For large batches the weights are transposed once per call into
@@ -1809,6 +1932,10 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
                                                                  scale_log2, kps, S, o_lat, o_part, ml_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dec && S > 1) {  // the decode core's head-major partials: merge and up-projection in one launch
+    merge_upproj_kernel<<<dim3(kHeads, kV / kUpEB), kMuThreads, 0, st>>>(o_part, ml_part, S, w_uv, out, out_f32, T);
+    return hipGetLastError();
+  }
   if (S > 1) {
     if (S <= 8)
       mla_merge_kernel<8><<<dim3(T, 32), 256, 0, st>>>(o_part, ml_part, S, o_lat);
