@@ -1511,9 +1511,10 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
 // ---------------------------------------------------------------- merge + upproj, decode
 // After the decode core (batches of up to 16 queries) with key splits: the
 // split merge and the V up-projection of one head as one launch.  grid (64
-// heads, 4 blocks of 64 output dims), 512 threads.  The decode core writes its
-// partials head-major (o_part[t][s][h][512], normalised by the split's own
-// sum) so that a head's are contiguous 1 KB rows.  Every load goes out before
+// heads, 4 blocks of 64 output dims, groups of tq <= 16 queries), 512
+// threads.  The decode core writes its partials head-major (o_part[t][s][h]
+// [512], normalised by the split's own sum) so that a head's are contiguous
+// 1 KB rows.  Every load goes out before
 // any is used: the W_UV slice (64 KB), and per thread the rows of one
 // (query, 8-dim chunk) pair for the first 16 splits with their (m, l).  The
 // merged o_lat rows (bf16, as the separate merge stores them) form the A tile
@@ -1522,16 +1523,19 @@ __global__ __launch_bounds__(256) void upproj_kernel(const uint16_t* __restrict_
 constexpr int kMuThreads = 512;
 static_assert(kDecTMax <= 16, "the A tile holds up to 16 queries");
 constexpr int kMuCh = 16;                  // splits requested at once
+constexpr int kMuQueries = 16;             // queries per workgroup (at most 16: the A tile's rows)
 constexpr int kMuARow = kLat + 8;          // A tile row (bf16, 16 B pad)
 
 __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t* __restrict__ o_part,
                                                                   const float* __restrict__ ml_part, int S,
                                                                   const uint16_t* __restrict__ w_uv,
-                                                                  void* __restrict__ out, int out_f32, int T) {
+                                                                  void* __restrict__ out, int out_f32, int T,
+                                                                  int tq) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kUpEB * kWvLds];
   __shared__ __attribute__((aligned(16))) uint16_t sa[16 * kMuARow];
   __shared__ f32x4 red[4][64];
   const int h = blockIdx.x, eb = blockIdx.y;
+  const int t0 = blockIdx.z * tq, nq = min(tq, T - t0);  // this workgroup's queries
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // W_UV[h][c][64 eb .. +63]: unit u covers c = 4q .. 4q+3, e = 8r .. 8r+7
   constexpr int kUnits = (kLat / 4) * (kUpEB / 8) / kMuThreads;
@@ -1544,12 +1548,13 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
     for (int i = 0; i < 4; ++i)
       rows[it][i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
   }
-  // merge: thread pairs (query t, chunk of 8 dims), tid + 512 i, i < 2
-  const int npairs = T * (kLat / 8);
+  // merge: thread pairs (query t0 + tl, chunk of 8 dims), tid + 512 i, i < 2
+  const int npairs = nq * (kLat / 8);
   for (int p0 = 0; p0 < npairs; p0 += kMuThreads) {
     const int pr = p0 + tid;
     const bool live = pr < npairs;
-    const int t = live ? pr >> 6 : 0, c8 = pr & 63;
+    const int tl = live ? pr >> 6 : 0, c8 = pr & 63;
+    const int t = t0 + tl;
     const uint16_t* src = o_part + ((int64_t)t * S * kHeads + h) * kLat + 8 * c8;
     const float* ml = ml_part + ((int64_t)t * S * kHeads + h) * 2;
     float mstar = -1e30f, L = 0.f;
@@ -1586,7 +1591,7 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (live)
-      *reinterpret_cast<u32x4*>(&sa[t * kMuARow + 8 * c8]) =
+      *reinterpret_cast<u32x4*>(&sa[tl * kMuARow + 8 * c8]) =
           u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
   }
@@ -1622,9 +1627,9 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
     const int e = eb * kUpEB + eblk * 16 + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      if (t < T) {
-        const int64_t o = ((int64_t)t * kHeads + h) * kV + e;
+      const int tl = 4 * g + i;
+      if (tl < nq) {
+        const int64_t o = ((int64_t)(t0 + tl) * kHeads + h) * kV + e;
         if (out_f32) reinterpret_cast<float*>(out)[o] = acc[i];
         else reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
       }
@@ -1933,7 +1938,9 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dec && S > 1) {  // the decode core's head-major partials: merge and up-projection in one launch
-    merge_upproj_kernel<<<dim3(kHeads, kV / kUpEB), kMuThreads, 0, st>>>(o_part, ml_part, S, w_uv, out, out_f32, T);
+    const int tq = kMuQueries;
+    merge_upproj_kernel<<<dim3(kHeads, kV / kUpEB, (T + tq - 1) / tq), kMuThreads, 0, st>>>(o_part, ml_part, S, w_uv,
+                                                                                           out, out_f32, T, tq);
     return hipGetLastError();
   }
   if (S > 1) {

@@ -235,6 +235,36 @@ def test_sparse_mla_matches_oracle_given_oracle_indices(case):
         assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 8, 12, 16])
+def test_sparse_mla_decode_core_forms(T):
+    """Decode batches of every size the decode core takes (1-16 queries; the
+    paired form with 1-4 steps per stream for up to 8 queries at k 2048, the
+    per-wave rings above), each query in its own sequence with ragged
+    contexts, index rows with -1 entries (and one row unsorted): every
+    query's output against the oracle, through the split merge and
+    up-projection launch."""
+    rng = np.random.default_rng(100 + T)
+    lens = [int(x) for x in rng.integers(2100, 4200, size=T)]
+    inp = synth.custom(lens, [(b, lens[b] - 1) for b in range(T)], seed=300 + T)
+    k = 2048
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = lens[t]
+        m = int(rng.integers(k // 2, k + 1))
+        sel = np.sort(rng.choice(n, m, replace=False)).astype(np.int32)
+        row = np.concatenate([sel, np.full(k - m, -1, np.int32)])
+        idx[t] = rng.permutation(row) if t == T - 1 else row
+    d = to_device(inp)
+    out = dsa.dsa_sparse_mla_attn(d.batch, d.q_nope, d.q_rope, d.kv, d.w_uk, d.w_uv,
+                                  torch.from_numpy(idx).cuda(), out_dtype=torch.float32).cpu().numpy()
+    worst_mx = worst_rel = 0.0
+    for t in range(T):
+        mx, rel = out_errors(out[t], _oracle_out(inp, t, idx[t]))
+        worst_mx, worst_rel = max(worst_mx, mx), max(worst_rel, rel)
+    _say(f"[sparse_mla] decode core T={T}: max-abs {worst_mx:.2e} rel-L2 {worst_rel:.2e}")
+    assert worst_mx <= OUT_MAX_ABS and worst_rel <= OUT_REL_L2
+
+
 def test_sparse_mla_absent_entries_and_order():
     """-1 entries anywhere are skipped; the order of idx does not matter; a
     query with no entry gets zeros; bf16 output equals rounded fp32 output."""
