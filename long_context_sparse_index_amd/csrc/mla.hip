@@ -509,11 +509,12 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 }
 
 // ---------------------------------------------------------------- decode core
-// Few queries (decode): grid of (query, group of 16 heads, key split)
-// workgroups of 4 waves, one per SIMD.  Each wave runs its own online softmax
-// over its share of the split's keys (16-key tiles u = wave, wave + 4, ...),
-// gathering each tile by direct-to-LDS loads into its own 2-slot ring, so the
-// tile loop has no workgroup barrier:
+// Few queries (decode, up to 16): workgroups of (query, key split, 32 heads),
+// 4 waves, one per SIMD; wave (hs, st) = (wave % 2, wave / 2) computes head
+// group 2hh + hs (16 heads) over the 16-key tiles st, st + 2, ... of the
+// split, so each tile serves two waves (32 heads), and those two waves each
+// gather half of it by direct-to-LDS loads (rows 8hs .. 8hs+7 and one of its
+// two rope loads); a barrier per step publishes the other wave's half.
 //   QK   logits^T[16 keys][16 heads] = c_tile . q^T, 18 16x16x32 MFMAs with the
 //        group's q (576 = 512 latent + 64 rope) resident as the B operand; lane
 //        (g, l16) gets keys 4g .. 4g+3 of head l16, which is the B operand
@@ -521,17 +522,13 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 //   PV   o^T[512 dims][16 heads] += c_tile^T . P^T, 32 16x16x16 MFMAs whose
 //        latent operand (4 keys of one dim per lane) comes from the row-major
 //        tile by the transposing LDS read.
-// The four waves' (max, sum, o) meet in LDS at the end.  Against the
-// all-heads core this reads every gathered row four times (once per head
-// group; the four workgroups of a (query, split) get block ids equal modulo 8,
-// which places them on one XCD and its L2) but writes a key split's partial
-// for 16 heads only, and a workgroup covers 4x the keys: the split partials,
-// which are as large as 64 gathered rows, shrink fourfold.
+// The two waves of a head group meet in LDS at the end (max, sum, o) and
+// write the split's partial.  The two workgroups of a (query, split) get
+// block ids equal modulo 8, which places them on one XCD and its L2, so a row
+// gathered for both head halves is read from HBM about once.
 constexpr int kDecHeads = 16;
 constexpr int kDecWaves = 4;
 constexpr int kDecKT = 16;                          // keys per wave tile
-constexpr int kDecLoads = kDecKT + 2;               // gather loads per tile (16 latent rows, 2 of rope)
-constexpr int kDecPadTiles = 3 * kDecWaves;         // absent tiles past a split's last (see the loop)
 constexpr int kDecMaxKps = 1024;                    // keys per split
 constexpr int kDecTMax = 16;                        // batches up to this size
 constexpr int kDecLatStride = kLat / 8 + 2;          // 66 slots per latent row (2 of padding)
@@ -558,55 +555,45 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int T, int k, float scale_log2, int kps, int S, uint16_t* __restrict__ o_lat,
     uint16_t* __restrict__ o_part, float* __restrict__ ml_part) {
-  // NS = 0: per-wave rings (above).  NS = 1..4, the paired form: a workgroup
-  // covers 32 heads (two head groups) and a split of 32*NS keys, the 2*NS
-  // tiles of which are all gathered at once; wave (hs, st) = (wave % 2,
-  // wave / 2) computes head group 2*hh + hs over the tiles st, st + 2, ... of
-  // the split, and the two waves of a stream st gather half of each of its
-  // tiles (rows 8hs .. 8hs+7 and rope load hs), so every gathered row serves
-  // 32 heads and a split's rows reach LDS in one round.
-  constexpr bool kPair = NS > 0;
-  static_assert(NS >= 0 && NS <= 4, "paired form: at most 4 steps (8 tiles)");
-  // Distinct slot arrays (not one indexed array): the compiler then waits
-  // only for the direct-to-LDS loads that target the array being read.  Ring
-  // form: slotN[w] is wave w's slot N; paired form: slotN[st] is step N's tile
-  // of stream st.
-  constexpr int kSlotRows = kPair ? 2 : kDecWaves;
-  constexpr int kXSlots = kPair ? kDecTileSlots * 8 : 8;  // (slots 2, 3: paired form only)
-  __shared__ __attribute__((aligned(16))) uint16_t slot0[kSlotRows][kDecTileSlots * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t slot1[kSlotRows][kDecTileSlots * 8];
-  __shared__ __attribute__((aligned(16))) uint16_t slot2[2][kXSlots];
-  __shared__ __attribute__((aligned(16))) uint16_t slot3[2][kXSlots];
-  __shared__ __attribute__((aligned(16))) int s_idx[kPair ? 32 * NS : kDecMaxKps + kDecPadTiles * kDecKT];
+  // NS = 1..4: splits of 32*NS keys, whose 2*NS tiles are all gathered at
+  // once; NS = 8: splits of 8, 12, ... 32 steps (kps / 32, a multiple of 4),
+  // the four tile arrays of a stream forming a ring: tile v + 3 is gathered
+  // at step v (after its barrier) into the array of tile v - 1.
+  constexpr bool kRing = NS == 8;
+  static_assert((NS >= 1 && NS <= 4) || NS == 8, "1-4 steps, or 8 for the ring");
+  // Four distinct tile arrays (not one indexed array): the compiler then waits
+  // only for the direct-to-LDS loads that target the array being read.
+  // slotN[st] holds step N's tile of stream st (step N mod 4 for the ring).
+  __shared__ __attribute__((aligned(16))) uint16_t slot0[2][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot1[2][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot2[2][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot3[2][kDecTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) int s_idx[kRing ? kDecMaxKps : 32 * NS];
   __shared__ float s_ml[kDecWaves][kDecHeads][2];
-  // block id -> (query, split) pair P and head group.  Ring form: ids 32a +
-  // 8hg + r hold pair 8a + r, so the four head groups of a pair are equal
-  // modulo 8 (one XCD, one L2); paired form: ids 16a + 8hh + r hold pair 8a +
-  // r, head groups 2hh and 2hh + 1.
+  // block id -> (query, split) pair P and head half hh: ids 16a + 8hh + r
+  // hold pair 8a + r, head groups 2hh and 2hh + 1
   const int id = blockIdx.x;
-  const int P = kPair ? (id >> 4) * 8 + (id & 7) : (id >> 5) * 8 + (id & 7);
+  const int P = (id >> 4) * 8 + (id & 7);
   if (P >= T * S) return;  // (whole workgroup)
   const int t = P / S, sp = P - t * S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hs = wave & 1, st = wave >> 1;  // (paired form)
-  const int hg = kPair ? 2 * ((id >> 3) & 1) + hs : (id >> 3) & 3;
+  const int hs = wave & 1, st = wave >> 1;
+  const int hg = 2 * ((id >> 3) & 1) + hs;
   const int l16 = lane & 15, g = lane >> 4;
   const int j0 = sp * kps;
   const int j1 = min(k, j0 + kps);
-  const int ntiles = j1 > j0 ? (j1 - j0 + kDecKT - 1) / kDecKT : 0;
-  const int ntw = ntiles > wave ? (ntiles - wave + kDecWaves - 1) / kDecWaves : 0;  // this wave's tiles
   const int seq = q_seq[t];
   const uint16_t* const kv_seq = PAGED ? kv : kv + cr.seq_row0[seq] * kRow;
   const int32_t* bt = PAGED ? cr.table + (int64_t)seq * cr.max_pages : nullptr;
   const int32_t* irow = idx + (int64_t)t * k;
   // The split's positions (as in mla_core_kernel: contiguous entries are
   // positions, an absent one position 0 with kAbsent set; paged entries are
-  // pool rows, an absent one ~row of position 0), padded to whole tiles.
+  // pool rows, an absent one ~row of position 0), padded to the split's tiles.
   {
-    constexpr int kFill = kPair ? 32 * NS : kDecMaxKps + kDecPadTiles * kDecKT;
+    constexpr int kFill = kRing ? kDecMaxKps : 32 * NS;
     constexpr int kPer = (kFill + kDecWaves * 64 - 1) / (kDecWaves * 64);
-    const int nfill = kPair ? kFill : (ntiles + kDecPadTiles) * kDecKT;
+    const int nfill = kRing ? kps : kFill;
     int v[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -644,11 +631,11 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
   __syncthreads();
 
-  // Gather of a 16-row tile into a wave's slot: loads 0-15 bring the 1 KB
-  // latent part of row i (lane L fetches logical chunk L ^ (i / 8) into
+  // Half hs of tile u of the split: loads 0-7 bring the 1 KB latent parts of
+  // rows 8hs .. 8hs+7 (lane L fetches logical chunk L ^ (row / 8) into
   // physical slot L of the row; the row's position is wave-uniform, so the
-  // only per-lane operand is that chunk offset), loads 16 and 17 the rope
-  // parts of all 16 rows (physical slot p of the rope area: row p / 8,
+  // only per-lane operand is that chunk offset), load 8 rope load hs, the rope
+  // parts of those 8 rows (physical slot p of rope area hs: row 8hs + p / 8,
   // logical chunk (p % 8) ^ (row / 2)).
   const uint64_t kv_a = reinterpret_cast<uint64_t>(kv_seq);
   const uint32_t kv_lo = __builtin_amdgcn_readfirstlane((uint32_t)kv_a);
@@ -660,56 +647,10 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int rope_r0 = lane >> 3;  // row of this lane's chunk in rope load 16 (load 17: + 8)
   const uint32_t rope_colb = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ (rope_r0 >> 1)) * 16);
   const uint32_t rope_colb1 = (uint32_t)(kLat * 2) + (uint32_t)(((lane & 7) ^ ((rope_r0 + 8) >> 1)) * 16);
-  // Returns the tile's mask of present rows (bit r for row r).
-  auto gather = [&](int v, uint16_t* dstt) __attribute__((always_inline)) -> uint32_t {  // this wave's tile v
-    const int u = wave + kDecWaves * v;
-    // lane l: entry of row l % 16.  (Read in asm with its own wait: the
-    // compiler cannot tell s_idx from the gathers' LDS targets and would wait
-    // for every gather in flight before a plain read.)
-    int pv;
-    {
-      const __attribute__((address_space(3))) int* const a =
-          (const __attribute__((address_space(3))) int*)(&s_idx[u * kDecKT + l16]);
-      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(pv) : "v"(a) : "memory");
-    }
-    const bool present = PAGED ? pv >= 0 : (pv & kAbsent) == 0;
-    const uint32_t pmask = (uint32_t)__ballot(present) & 0xFFFFu;
-    const int pr0 = __shfl(pv, rope_r0, 64), pr1 = __shfl(pv, rope_r0 + 8, 64);
-#pragma unroll
-    for (int i = 0; i < kDecKT; ++i) {
-      uint16_t* const dst = dstt + i * kDecLatStride * 8;
-      const int e = __builtin_amdgcn_readlane(pv, i);
-      const uint32_t voff = i < 8 ? voff_lo : voff_hi;
-      if (PAGED) {
-        const int r = e >= 0 ? e : ~e;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(kv_u + (int64_t)r * kRow), (short)0, (int)0xFFFFFFFF, kBufferWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
-      } else {
-        // (bit 30 of an absent entry drops out of the 24-bit position)
-        const int soff = (e & 0xFFFFFF) * (kRow * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dst, 16, voff, soff, 0, 0);
-      }
-    }
-    uint16_t* const dr0 = dstt + kDecRopeSlot0 * 8;
-    uint16_t* const dr1 = dstt + (kDecRopeSlot0 + 64) * 8;
-    if (PAGED) {
-      const int r0 = pr0 >= 0 ? pr0 : ~pr0, r1 = pr1 >= 0 ? pr1 : ~pr1;
-      const uint16_t* const g0 = kv_u + (int64_t)r0 * kRow + rope_colb / 2;
-      const uint16_t* const g1 = kv_u + (int64_t)r1 * kRow + rope_colb1 / 2;
-      __builtin_amdgcn_global_load_lds(g0, dr0, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(g1, dr1, 16, 0, 0);
-    } else {
-      const uint32_t o0 = (uint32_t)(pr0 & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb;
-      const uint32_t o1 = (uint32_t)(pr1 & 0xFFFFFF) * (uint32_t)(kRow * 2) + rope_colb1;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dr0, 16, o0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, dr1, 16, o1, 0, 0, 0);
-    }
-    return pmask;
-  };
-
-  // Paired form: half hs of tile u of the split (rows 8hs .. 8hs+7, as in
-  // gather, and rope load hs); returns the mask of the tile's present rows.
+  // Returns the mask of the tile's present rows (bit r for row r).  (The
+  // entries are read in asm with its own wait: the compiler cannot tell s_idx
+  // from the gathers' LDS targets and would wait for every gather in flight
+  // before a plain read.)
   auto gather_half = [&](int u, uint16_t* dstt) __attribute__((always_inline)) -> uint32_t {
     int pv;
     {
@@ -809,56 +750,25 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  if constexpr (!kPair) {
-    uint16_t* const my0 = slot0[wave];
-    uint16_t* const my1 = slot1[wave];
-    // Step v computes tile v from slot v % 2 once this wave's loads of it are
-    // in (its loads of tile v + 1 may still be in flight), then gathers tile
-    // v + 2 into that slot once the wave's reads of it are complete.  The loop
-    // body has no branch (the compiler then keeps track of which slot a wait is
-    // for): a wave runs an even number of steps and gathers two tiles past its
-    // last; those tiles hold absent entries (position 0's row, masked), and an
-    // odd count's last step computes such a tile to no effect.
-    uint32_t pm0, pm1;  // present rows of the tiles in slot 0 and 1
-    auto step = [&](int v, auto BUFC) __attribute__((always_inline)) {
-      constexpr int buf = decltype(BUFC)::value;
-      uint32_t& pm = buf == 0 ? pm0 : pm1;
-      wait_vm_wide<kDecLoads>();
-      compute(buf == 0 ? my0 : my1, pm);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      pm = gather(v + 2, buf == 0 ? my0 : my1);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    const int nsteps = (ntw + 1) & ~1;
-    pm0 = gather(0, my0);
-    pm1 = gather(1, my1);
-    // the query operand loads (issued before the gathers) are complete here;
-    // marking them consumed keeps the compiler from waiting for every gather
-    // before the loop
-  #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
-    for (int v = 0; v < nsteps; v += 2) {
-      step(v, std::integral_constant<int, 0>{});
-      step(v + 1, std::integral_constant<int, 1>{});
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // (the two gathers past the last step)
-  } else {
-    // Paired form: half of each of this stream's NS tiles, all in flight at
-    // once (9 loads per half tile); before step v the wave waits for its
-    // halves of tiles up to v, and the barrier makes the other wave's halves
-    // visible too.
-    auto arr = [&](int v) __attribute__((always_inline)) -> uint16_t* {
-      return v == 0 ? slot0[st] : v == 1 ? slot1[st] : v == 2 ? slot2[st] : slot3[st];
-    };
-    uint32_t pmv[NS];
+  // Half of each of this stream's first (NS, at most 4) tiles goes out at
+  // once (9 loads per half tile); before step v the wave waits for its
+  // halves of tiles up to v, and the barrier makes the other wave's halves
+  // visible too.
+  auto arr = [&](int v) __attribute__((always_inline)) -> uint16_t* {
+    return v == 0 ? slot0[st] : v == 1 ? slot1[st] : v == 2 ? slot2[st] : slot3[st];
+  };
+  constexpr int kNS = kRing ? 4 : NS;  // tiles gathered before the first step
+  constexpr int kHalf = kDecKT / 2 + 1;     // loads per half tile
+  uint32_t pmv[kNS];
 #pragma unroll
-    for (int v = 0; v < NS; ++v) pmv[v] = gather_half(st + 2 * v, arr(v));
+  for (int v = 0; v < kNS; ++v) pmv[v] = gather_half(st + 2 * v, arr(v));
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
+  for (int ks = 0; ks < 18; ++ks) asm volatile("" : "+v"(qb[ks]));
+  if constexpr (!kRing) {
     auto pstep = [&](auto VC) __attribute__((always_inline)) {
       constexpr int v = decltype(VC)::value;
       if constexpr (v < NS) {
-        wait_vm_wide<(NS - 1 - v) * (kDecKT / 2 + 1)>();
+        wait_vm_wide<(NS - 1 - v) * kHalf>();
         lds_barrier();
         compute(arr(v), pmv[v]);
       }
@@ -867,37 +777,68 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     pstep(std::integral_constant<int, 1>{});
     pstep(std::integral_constant<int, 2>{});
     pstep(std::integral_constant<int, 3>{});
+  } else {
+    // Step v of array b = v % 4: wait for this wave's halves of tile v (the
+    // halves of tiles v + 1, v + 2 stay in flight; step 0 also leaves tile
+    // 3's, the last two steps fewer), barrier, gather tile v + 3 into the
+    // array of tile v - 1 (both waves are past its step), compute tile v.
+    // Rounds of four steps: the first does not refill at step 0, the last
+    // refills only at its step 0; R = kps / 128 >= 2 rounds.
+    const int R = kps / (8 * kDecKT);
+    auto rstep = [&](int v, auto BC, auto WC, auto FC) __attribute__((always_inline)) {
+      constexpr int b = decltype(BC)::value;
+      wait_vm_wide<decltype(WC)::value>();
+      lds_barrier();
+      if constexpr (decltype(FC)::value) pmv[(b + 3) & 3] = gather_half(st + 2 * (v + 3), arr((b + 3) & 3));
+      compute(arr(b), pmv[b]);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using W3 = std::integral_constant<int, 3 * kHalf>;
+    using W2 = std::integral_constant<int, 2 * kHalf>;
+    using W1 = std::integral_constant<int, kHalf>;
+    using W0 = std::integral_constant<int, 0>;
+    using Y = std::true_type;
+    using N = std::false_type;
+    rstep(0, I0{}, W3{}, N{});
+    rstep(1, I1{}, W2{}, Y{});
+    rstep(2, I2{}, W2{}, Y{});
+    rstep(3, I3{}, W2{}, Y{});
+    for (int r = 1; r < R - 1; ++r) {
+      const int v = 4 * r;
+      rstep(v, I0{}, W2{}, Y{});
+      rstep(v + 1, I1{}, W2{}, Y{});
+      rstep(v + 2, I2{}, W2{}, Y{});
+      rstep(v + 3, I3{}, W2{}, Y{});
+    }
+    const int v = 4 * (R - 1);
+    rstep(v, I0{}, W2{}, Y{});
+    rstep(v + 1, I1{}, W2{}, N{});
+    rstep(v + 2, I2{}, W1{}, N{});
+    rstep(v + 3, I3{}, W0{}, N{});
   }
 
-  // ---- the waves' partial results of a head group (ring form: all four;
-  // paired form: the two streams of head group 2hh + hs): reference maxima and
-  // sums meet in LDS, then each wave adds up its share of the 32 latent
-  // blocks of 16 dims over those waves
-  constexpr int kComb = kPair ? 2 : kDecWaves;
-  auto cw = [&](int c) __attribute__((always_inline)) { return kPair ? hs + 2 * c : c; };
+  // ---- the two waves of head group 2hh + hs (the streams st = 0, 1):
+  // reference maxima and sums meet in LDS, then each wave adds up 16 of the
+  // 32 latent blocks of 16 dims over both
+  auto cw = [&](int c) __attribute__((always_inline)) { return hs + 2 * c; };  // c-th wave of the group
   const float l_sum = rows_sum(l_part);
   if (g == 0) {
     s_ml[wave][l16][0] = m_ref;
     s_ml[wave][l16][1] = l_sum;
   }
   __syncthreads();  // (also: every wave is done with its slots)
-  float mstar = -1e30f;
-#pragma unroll
-  for (int c = 0; c < kComb; ++c) mstar = fmaxf(mstar, s_ml[cw(c)][l16][0]);
-  float L = 0.f;
-#pragma unroll
-  for (int c = 0; c < kComb; ++c) L += __builtin_amdgcn_exp2f(s_ml[cw(c)][l16][0] - mstar) * s_ml[cw(c)][l16][1];
+  const float mstar = fmaxf(s_ml[cw(0)][l16][0], s_ml[cw(1)][l16][0]);
+  const float L = __builtin_amdgcn_exp2f(s_ml[cw(0)][l16][0] - mstar) * s_ml[cw(0)][l16][1] +
+                  __builtin_amdgcn_exp2f(s_ml[cw(1)][l16][0] - mstar) * s_ml[cw(1)][l16][1];
   const float wgt = __builtin_amdgcn_exp2f(m_ref - mstar);
-  // wave w's scaled o goes to [32 blocks][64 lanes] of f32x4 (32 KB): ring
-  // form, waves 0, 1 in slot0 and waves 2, 3 in slot1; paired form, wave w in
-  // slot w
-  static_assert(sizeof(slot0) >= (kPair ? 1 : 2) * 32 * 64 * sizeof(f32x4), "reduction area");
+  // wave w's scaled o goes to [32 blocks][64 lanes] of f32x4 (32 KB) in slot w
+  static_assert(sizeof(slot0) >= 32 * 64 * sizeof(f32x4), "reduction area");
   auto red = [&](int w) __attribute__((always_inline)) -> f32x4* {
-    if constexpr (kPair)
-      return reinterpret_cast<f32x4*>(w == 0 ? &slot0[0][0] : w == 1 ? &slot1[0][0] : w == 2 ? &slot2[0][0]
-                                                                                            : &slot3[0][0]);
-    else
-      return reinterpret_cast<f32x4*>(w < 2 ? &slot0[0][0] : &slot1[0][0]) + (w & 1) * 32 * 64;
+    return reinterpret_cast<f32x4*>(w == 0 ? &slot0[0][0] : w == 1 ? &slot1[0][0] : w == 2 ? &slot2[0][0]
+                                                                                          : &slot3[0][0]);
   };
   {
     f32x4* const mine = red(wave);
@@ -906,13 +847,10 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
   }
   __syncthreads();
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  constexpr int kBlocks = 32 / kComb;  // blocks per wave: ring 8, paired 16
 #pragma unroll
-  for (int bb = 0; bb < kBlocks; ++bb) {
-    const int b = kBlocks * (kPair ? st : wave) + bb;
-    f32x4 sum = red(cw(0))[b * 64 + lane];
-#pragma unroll
-    for (int c = 1; c < kComb; ++c) sum += red(cw(c))[b * 64 + lane];
+  for (int bb = 0; bb < 16; ++bb) {
+    const int b = 16 * st + bb;
+    f32x4 sum = red(cw(0))[b * 64 + lane] + red(cw(1))[b * 64 + lane];
     sum *= inv;
     if (S == 1) {
       *reinterpret_cast<u32x2*>(o_lat + ((int64_t)t * kHeads + hq) * kLat + 16 * b + 4 * g) =
@@ -923,7 +861,7 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
           u32x2{cvt_pk_bf16(sum[0], sum[1]), cvt_pk_bf16(sum[2], sum[3])};
     }
   }
-  if (S > 1 && (kPair ? st : wave) == 0 && g == 0) {
+  if (S > 1 && st == 0 && g == 0) {
     const int64_t base = ((int64_t)t * S + sp) * kHeads + hq;
     ml_part[base * 2] = mstar;
     ml_part[base * 2 + 1] = L;
@@ -1794,14 +1732,22 @@ __global__ __launch_bounds__(512) void head_gemm_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------- plan + launch
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Steps per stream of the paired decode core (32 heads per workgroup, about
-// 256 workgroups) for a decode batch of T queries at top-k k, when its splits
-// need at most 4 steps of two 16-key tiles; 0: the per-wave rings.
-static int dec_pair_steps(int T, int k) {
+// Steps per stream of the decode core for a batch of T <= 16 queries at top-k
+// k >= 1 (about 256 workgroups: ceil(128 / T) key splits per query), and its
+// keys per split: 1-4 steps; splits of more than 4 steps take the ring form
+// (NS = 8), keys per split a multiple of 128 (whole rounds of 4 steps).
+static_assert(kMaxTopk / ((128 + kDecTMax - 1) / kDecTMax) <= kDecMaxKps, "ring splits fit s_idx");
+static int dec_pair_steps(int T, int k, int* kps) {
   const int sp = (128 + T - 1) / T;
   const int pk = (k + sp - 1) / sp;
   const int ns = (pk + 2 * kDecKT - 1) / (2 * kDecKT);
-  return ns <= 4 ? ns : 0;
+  if (ns <= 4) {
+    if (kps) *kps = 2 * kDecKT * ns;
+    return ns;
+  }
+  const int rk = (pk + 8 * kDecKT - 1) / (8 * kDecKT) * (8 * kDecKT);
+  if (kps) *kps = rk;
+  return 8;
 }
 
 MlaPlan plan_mla(int T, int k) {
@@ -1821,23 +1767,11 @@ MlaPlan plan_mla(int T, int k) {
   kps = (kps + kKT - 1) / kKT * kKT;
   p.keys_per_split = kps;
   p.splits = (k + kps - 1) / kps;
-  // Decode core: the paired form where it applies, else about 256 workgroups
-  // of (query, 16 heads, split), splits of whole 64-key rounds (16 keys per
-  // wave) and at most kDecMaxKps keys.
-  p.dec = T > 0 && T <= kDecTMax;
+  // Decode core (batches of up to 16 queries)
+  p.dec = T > 0 && T <= kDecTMax && k >= 1;
   if (p.dec) {
-    const int ns = dec_pair_steps(T, k);
-    if (ns > 0) {
-      p.dec_keys_per_split = 2 * kDecKT * ns;
-      p.dec_splits = (k + p.dec_keys_per_split - 1) / p.dec_keys_per_split;
-    } else {
-      const int s0 = (64 + T - 1) / T;
-      int dk = (k + s0 - 1) / s0;
-      dk = (dk + kDecKT * kDecWaves - 1) / (kDecKT * kDecWaves) * (kDecKT * kDecWaves);
-      dk = dk < kDecMaxKps ? dk : kDecMaxKps;
-      p.dec_keys_per_split = dk;
-      p.dec_splits = (k + dk - 1) / dk;
-    }
+    dec_pair_steps(T, k, &p.dec_keys_per_split);
+    p.dec_splits = (k + p.dec_keys_per_split - 1) / p.dec_keys_per_split;
   }
   const int max_splits = p.dec && p.dec_splits > p.splits ? p.dec_splits : p.splits;
   const size_t lat = (size_t)T * kHeads * kLat * sizeof(uint16_t);
@@ -1886,10 +1820,10 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
   const dim3 grid(T, p.splits);
   const int kps = p.keys_per_split;
   if (dec) {
-    const int ns = dec_pair_steps(T, p.k);
-    const int dgrid = (ns ? 16 : 32) * ((T * S + 7) / 8);
+    int dk;  // (the plan's dec_keys_per_split)
+    const int ns = dec_pair_steps(T, p.k, &dk);
+    const int dgrid = 16 * ((T * S + 7) / 8);
     const uint16_t* const kvb = static_cast<const uint16_t*>(kv);
-    const int dk = p.dec_keys_per_split;
 #define DSA_DEC_LAUNCH(PG, NS)                                                                       \
   mla_decode_kernel<PG, NS><<<dgrid, kDecWaves * 64, 0, st>>>(b.q_seq, b.rows, q_lat, q_rope, kvb, idx, T, \
                                                                p.k, scale_log2, dk, S, o_lat, o_part, ml_part)
@@ -1899,7 +1833,7 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
         case 2: DSA_DEC_LAUNCH(true, 2); break;
         case 3: DSA_DEC_LAUNCH(true, 3); break;
         case 4: DSA_DEC_LAUNCH(true, 4); break;
-        default: DSA_DEC_LAUNCH(true, 0); break;
+        default: DSA_DEC_LAUNCH(true, 8); break;
       }
     } else {
       switch (ns) {
@@ -1907,7 +1841,7 @@ hipError_t launch_sparse_mla(const LaunchBatch& b, const MlaPlan& p, const uint1
         case 2: DSA_DEC_LAUNCH(false, 2); break;
         case 3: DSA_DEC_LAUNCH(false, 3); break;
         case 4: DSA_DEC_LAUNCH(false, 4); break;
-        default: DSA_DEC_LAUNCH(false, 0); break;
+        default: DSA_DEC_LAUNCH(false, 8); break;
       }
     }
 #undef DSA_DEC_LAUNCH
