@@ -847,11 +847,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_slice_select_kernel(
   }
 }
 
-// Kernel 3 (grid T, plus 64 workgroups when an absorb job rides along): load
+// Kernel 3 (grid T, plus 128 workgroups when an absorb job rides along): load
 // list A and the candidates, resolve the lower digits, merge into the output.
-// Workgroup T + h, if launched, computes q_lat of head h for every query (each
-// wave two or more blocks of 32 latent columns) on CUs the T row workgroups
-// leave idle.
+// Workgroups T + 2h and T + 2h + 1, if launched, compute q_lat of head h for
+// every query (each wave one block of 32 latent columns) on CUs the T row
+// workgroups leave idle.
 template <int KMAX>
 __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* __restrict__ q_pos,
                                                                  const float* __restrict__ scores,
@@ -864,8 +864,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_finish_kernel(const int32_t* 
   if (t >= T) {  // the top-k LDS of this workgroup is free: per-wave staging for the absorption
     static_assert(kTkWaves * kAbsorbStage * sizeof(uint16_t) <= sizeof(sh.cand_key), "absorb staging");
     uint16_t* stage = reinterpret_cast<uint16_t*>(sh.cand_key) + (tid >> 6) * kAbsorbStage;
-    for (int c0 = (tid >> 6) * 32; c0 < kLat; c0 += kTkWaves * 32)
-      absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, t - T, c0, 0, (T + 31) / 32, stage);
+    // workgroup T + 2h + i: latent columns 256i .. 256i+255 of head h, one
+    // block of 32 per wave
+    const int j = t - T;
+    absorb_wave(ab.q_nope, ab.w_uk, ab.q_lat, T, j >> 1, (j & 1) * (kLat / 2) + (tid >> 6) * 32, 0, (T + 31) / 32,
+                stage);
     return;
   }
   const char* base = ws + (size_t)t * w.per_query;
@@ -947,7 +950,8 @@ hipError_t launch_topk(const LaunchBatch& b, const float* scores, int64_t ld, in
     topk_slice_hist_kernel<<<dim3(b.T, w.S), kSliceThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   topk_slice_select_kernel<<<dim3(b.T, w.S), kSelThreads, 0, st>>>(b.q_pos, scores, ld, k, wsb, w);
   const AbsorbJob ab = absorb ? *absorb : AbsorbJob{nullptr, nullptr, nullptr};
-  const int grid = b.T + (absorb ? kHeads : 0);
+  static_assert(kTkWaves * 32 * 2 == kLat, "two absorb workgroups per head, a 32-column block per wave");
+  const int grid = b.T + (absorb ? 2 * kHeads : 0);
   if (small)
     topk_finish_kernel<kTopkSmall><<<grid, kTkThreads, 0, st>>>(b.q_pos, scores, ld, k, idx, wsb, w, b.T, ab);
   else
