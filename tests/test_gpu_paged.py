@@ -96,6 +96,41 @@ def test_paged_absent_entries_read_finite_rows():
     assert torch.equal(oc, op)
 
 
+@pytest.mark.parametrize("T,k", [(12, 2048), (12, 8192), (8, 4096)])
+def test_paged_decode_core_ring_equals_contiguous(T, k):
+    """The decode core's ring of 4-step rounds (more than 8 queries at k 2048,
+    or k 4096 / 8192) on 16-token pages: index rows with -1 entries (one row
+    unsorted) give the same bytes as the contiguous layout, and sampled
+    queries match the oracle."""
+    _say(f"[paged decode ring] T={T} k={k}")
+    rng = np.random.default_rng(700 + T + k)
+    lens = [int(x) for x in rng.integers(k + 60, k + 3000, size=T)]
+    inp = synth.custom(lens, [(b, lens[b] - 1) for b in range(T)], seed=710 + T + k)
+    pc = synth.to_paged(inp, 16, seed=16)
+    dc = to_device(inp)
+    dp = to_device_paged(inp, pc, dc)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        m = int(rng.integers(k // 2, k + 1))
+        row = np.concatenate([np.sort(rng.choice(lens[t], m, replace=False)).astype(np.int32),
+                              np.full(k - m, -1, np.int32)])
+        idx[t] = rng.permutation(row) if t == 1 else row
+    it = torch.from_numpy(idx).cuda()
+    mla_c = dsa.dsa_sparse_mla_attn(dc.batch, dc.q_nope, dc.q_rope, dc.kv, dc.w_uk, dc.w_uv, it,
+                                    out_dtype=torch.float32)
+    mla_p = dsa.dsa_sparse_mla_attn(dp.batch, dp.q_nope, dp.q_rope, dp.kv, dp.w_uk, dp.w_uv, it,
+                                    out_dtype=torch.float32)
+    assert torch.equal(mla_c, mla_p)
+    out = mla_p.cpu().numpy()
+    for t in (0, 1, T - 1):
+        b = int(inp.q_seq[t])
+        r0 = int(inp.seq_row0[b])
+        kept = idx[t][idx[t] >= 0].astype(np.int64)
+        ref = O.mla_explicit(inp.q_nope[t], inp.q_rope[t], inp.kv[r0 + kept], inp.w_uk, inp.w_uv)
+        mx, rel = out_errors(out[t], ref)
+        assert mx <= OUT_MAX_ABS and rel <= OUT_REL_L2, (t, mx, rel)
+
+
 def test_paged_full_size_decode_sampled():
     """decode_b8_ctx204k with 64-token pages: identical to the contiguous layout,
     sampled queries against the oracle."""
