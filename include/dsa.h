@@ -178,6 +178,9 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  * Computed in weight-absorbed form: q_lat = W_UK[h] q_nope (rounded to bf16),
  * logits against the latent, online softmax in fp32, the latent-weighted sum
  * (rounded to bf16) up-projected by W_UV[h]; fp32 accumulation throughout.
+ * Batches of few queries split each query's kept positions over several
+ * workgroups: each split's normalised weighted sum is then also held in bf16
+ * (the latent's own type and range) before the splits are merged in fp32.
  *   q_nope [T,64,192], q_rope [T,64,64], w_uk [64,512,192], w_uv [64,512,256]:
  *   bf16.  kv: [rows,576] bf16, or [rows,400] bytes when batch->kv_format is
  *   DSA_KV_INT4 (the latent is then dequantised, code * scale, and rounded to
