@@ -528,14 +528,14 @@ __global__ __launch_bounds__(kCoreThreads) void mla_core_kernel(
 // gathered for both head halves is read from HBM about once.
 constexpr int kDecHeads = 16;
 constexpr int kDecWaves = 4;
-constexpr int kDecKT = 16;                          // keys per wave tile
+constexpr int kDecKT = 16;                          // keys per tile
 constexpr int kDecMaxKps = 1024;                    // keys per split
 constexpr int kDecTMax = 16;                        // batches up to this size
 constexpr int kDecLatStride = kLat / 8 + 2;          // 66 slots per latent row (2 of padding)
 constexpr int kDecRopeSlot0 = kDecKT * kDecLatStride;  // 1056: the rope area after 16 latent rows
 constexpr int kDecTileSlots = kDecRopeSlot0 + kDecKT * (kRope / 8);  // 1184 slots of 16 B
 
-// Wave tile layout (16 rows): the latent parts of the rows first, one 66-slot
+// Tile layout (16 rows): the latent parts of the rows first, one 66-slot
 // row each (logical chunk c of row r at r*66 + (c ^ (r / 8)): the XOR only
 // swaps neighbouring chunks, so a lane's successive chunks stay at constant
 // distances and its LDS reads share one address register), then the rope
