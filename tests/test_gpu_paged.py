@@ -96,10 +96,10 @@ def test_paged_absent_entries_read_finite_rows():
     assert torch.equal(oc, op)
 
 
-@pytest.mark.parametrize("T,k", [(12, 2048), (12, 8192), (8, 4096)])
+@pytest.mark.parametrize("T,k", [(12, 2048), (12, 8192), (8, 4096), (32, 2048)])
 def test_paged_decode_core_ring_equals_contiguous(T, k):
     """The decode core's ring of 4-step rounds (more than 8 queries at k 2048,
-    or k 4096 / 8192) on 16-token pages: index rows with -1 entries (one row
+    or k 4096 / 8192), and the key-split core above 16 queries, on 16-token pages: index rows with -1 entries (one row
     unsorted) give the same bytes as the contiguous layout, and sampled
     queries match the oracle."""
     _say(f"[paged decode ring] T={T} k={k}")

@@ -236,14 +236,16 @@ def test_sparse_mla_matches_oracle_given_oracle_indices(case):
 
 
 @pytest.mark.parametrize("T,k", [(1, 2048), (2, 2048), (3, 2048), (5, 2048), (7, 2048), (8, 2048), (12, 2048),
-                                 (16, 2048), (1, 8192), (8, 4096), (8, 8192), (16, 8192)])
+                                 (16, 2048), (24, 2048), (32, 2048), (1, 8192), (8, 4096), (8, 8192), (16, 8192),
+                                 (32, 8192)])
 def test_sparse_mla_decode_core_forms(T, k):
     """Decode batches of every size the decode core takes (1-16 queries): the
     paired form with 1-4 steps per stream (up to 8 queries at k 2048) and its
-    ring of 2-8 rounds (k 2048 above 8 queries, k 4096 and 8192), each query
+    ring of 2-8 rounds (k 2048 above 8 queries, k 4096 and 8192); above 16
+    queries the all-heads key-split core and separate merge; each query
     in its own sequence with ragged contexts, index rows with -1 entries (and
     one row unsorted): every query's output against the oracle, through the
-    split merge and up-projection launch."""
+    split merge and up-projection."""
     rng = np.random.default_rng(100 + T + k)
     lens = [int(x) for x in rng.integers(k + 60, 2 * k + 100, size=T)]
     inp = synth.custom(lens, [(b, lens[b] - 1) for b in range(T)], seed=300 + T + k)
