@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kDecWaves * 64) __attribute__((amdgpu_waves_per_eu(
     return v == 0 ? slot0[st] : v == 1 ? slot1[st] : v == 2 ? slot2[st] : slot3[st];
   };
   constexpr int kNS = kRing ? 4 : NS;  // tiles gathered before the first step
-  constexpr int kHalf = kDecKT / 2 + 1;     // loads per half tile
+  constexpr int kHalf = kDecKT / 2 + 1;  // loads per half tile
   uint32_t pmv[kNS];
 #pragma unroll
   for (int v = 0; v < kNS; ++v) pmv[v] = gather_half(st + 2 * v, arr(v));
