@@ -1486,6 +1486,29 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
     for (int i = 0; i < 4; ++i)
       rows[it][i] = ld16(w_uv + ((int64_t)h * kLat + 4 * q + i) * kV + eb * kUpEB + 8 * r);
   }
+  // W_UV slice transposed into wt[e][c] (B operand: 8 consecutive c per
+  // lane); done once the first merge loads are out, while they are in flight
+  auto transpose_w = [&]() __attribute__((always_inline)) {
+    // (the W_UV registers pass through an empty asm that also orders memory:
+    // the compiler otherwise hoists the transposition, and its wait for the
+    // W_UV loads, above the merge loads)
+#pragma unroll
+    for (int it = 0; it < kUnits; ++it)
+      asm volatile("" : "+v"(rows[it][0]), "+v"(rows[it][1]), "+v"(rows[it][2]), "+v"(rows[it][3]) : : "memory");
+#pragma unroll
+    for (int it = 0; it < kUnits; ++it) {
+      const int u = tid + kMuThreads * it;
+      const int q = u >> 3, r = u & 7;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
+        const int dw = e8 >> 1;
+        const u32x2 v = {__builtin_amdgcn_perm(rows[it][1][dw], rows[it][0][dw], sel),
+                         __builtin_amdgcn_perm(rows[it][3][dw], rows[it][2][dw], sel)};
+        *reinterpret_cast<u32x2*>(&wt[(8 * r + e8) * kWvLds + 4 * q]) = v;
+      }
+    }
+  };
   // merge: thread pairs (query t0 + tl, chunk of 8 dims), tid + 512 i, i < 2
   const int npairs = nq * (kLat / 8);
   for (int p0 = 0; p0 < npairs; p0 += kMuThreads) {
@@ -1506,6 +1529,7 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
         m_l[u] = *reinterpret_cast<const f32x2*>(ml + (int64_t)sp * kHeads * 2);
         v[u] = ld16(src + (int64_t)sp * kPartSlab);
       }
+      if (p0 == 0 && s0 == 0) transpose_w();  // (every workgroup has a first round)
       float cm = mstar;
 #pragma unroll
       for (int u = 0; u < kMuCh; ++u) cm = s0 + u < S ? fmaxf(cm, m_l[u][0]) : cm;
@@ -1532,20 +1556,6 @@ __global__ __launch_bounds__(kMuThreads) void merge_upproj_kernel(const uint16_t
       *reinterpret_cast<u32x4*>(&sa[tl * kMuARow + 8 * c8]) =
           u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-  }
-  // W_UV slice transposed into wt[e][c] (B operand: 8 consecutive c per lane)
-#pragma unroll
-  for (int it = 0; it < kUnits; ++it) {
-    const int u = tid + kMuThreads * it;
-    const int q = u >> 3, r = u & 7;
-#pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      const uint32_t sel = (e8 & 1) ? 0x07060302u : 0x05040100u;
-      const int dw = e8 >> 1;
-      const u32x2 v = {__builtin_amdgcn_perm(rows[it][1][dw], rows[it][0][dw], sel),
-                       __builtin_amdgcn_perm(rows[it][3][dw], rows[it][2][dw], sel)};
-      *reinterpret_cast<u32x2*>(&wt[(8 * r + e8) * kWvLds + 4 * q]) = v;
-    }
   }
   __syncthreads();
   // out rows 4g + i (queries), column l16 of dim block eblk
